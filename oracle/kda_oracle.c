@@ -1,0 +1,131 @@
+/*
+ * Float64 CPU oracle of the KDA forward recurrence (plain C + OpenMP).
+ *
+ * TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load or call this library; the KDA
+ * library never does, and the two share no source.
+ *
+ * It computes the recurrence token by token in double precision, one
+ * (sequence, head) pair per OpenMP task, with the five steps of
+ * "Module 03 - KDA I: The Delta-Rule Recurrence" (jared-hpc.com), section 2,
+ * and the beta-scaled error of "Kimi Delta Attention (KDA)" (brain.bigb.es):
+ *
+ *   (1) S~ = Diag(exp(g_t)) S      decay each key channel (row of S)
+ *   (2) v^ = S~^T k_t              prediction
+ *   (3) e  = beta_t (v_t - v^)     scaled error
+ *   (4) S  = S~ + k_t e^T          rank-one write
+ *   (5) o_t = S^T (scale q_t)      read of the updated state
+ *
+ * Inputs are float arrays holding exactly the values the GPU receives (a
+ * bfloat16 value is exact in float); every operation is done in double.
+ * Layouts: q, k, g [Ttot, H, Dk]; v [Ttot, H, Dv]; beta [Ttot, H];
+ * states [N, H, Dk, Dv] with row = key channel.
+ *
+ * Parity pins: the Python test-suite checks this file against the numpy
+ * oracle (same definition, written independently) on the small workloads.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int kda_oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* One (sequence, head) chain over tokens [t0, t1). S is Dk*Dv doubles,
+ * updated in place; o gets the outputs of the chain's tokens. */
+static void chain(const float* q, const float* k, const float* v, const float* g,
+                  const float* beta, double scale, int H, int Dk, int Dv, int h,
+                  int64_t t0, int64_t t1, double* S, double* o,
+                  double* vhat, double* err, double* dec) {
+    for (int64_t t = t0; t < t1; ++t) {
+        const float* qt = q + (t * H + h) * (int64_t)Dk;
+        const float* kt = k + (t * H + h) * (int64_t)Dk;
+        const float* vt = v + (t * H + h) * (int64_t)Dv;
+        const float* gt = g + (t * H + h) * (int64_t)Dk;
+        const double b = (double)beta[t * H + h];
+        for (int c = 0; c < Dk; ++c) dec[c] = exp((double)gt[c]);
+        /* (1) forget */
+        for (int c = 0; c < Dk; ++c)
+            for (int j = 0; j < Dv; ++j) S[c * Dv + j] *= dec[c];
+        /* (2) predict: v^ = S~^T k */
+        for (int j = 0; j < Dv; ++j) vhat[j] = 0.0;
+        for (int c = 0; c < Dk; ++c) {
+            const double kc = (double)kt[c];
+            for (int j = 0; j < Dv; ++j) vhat[j] += S[c * Dv + j] * kc;
+        }
+        /* (3) correct */
+        for (int j = 0; j < Dv; ++j) err[j] = b * ((double)vt[j] - vhat[j]);
+        /* (4) write */
+        for (int c = 0; c < Dk; ++c) {
+            const double kc = (double)kt[c];
+            for (int j = 0; j < Dv; ++j) S[c * Dv + j] += kc * err[j];
+        }
+        /* (5) read: o = S^T (scale q) */
+        double* ot = o + (t * H + h) * (int64_t)Dv;
+        for (int j = 0; j < Dv; ++j) ot[j] = 0.0;
+        for (int c = 0; c < Dk; ++c) {
+            const double qc = scale * (double)qt[c];
+            for (int j = 0; j < Dv; ++j) ot[j] += S[c * Dv + j] * qc;
+        }
+    }
+}
+
+/* Prefill over packed sequences. cu_seqlens is int32[num_seqs + 1] with
+ * cu[0] = 0 (fixed-length batches pass n*T). h0 may be NULL (zero state).
+ * o: double [Ttot, H, Dv]; ht: double [num_seqs, H, Dk, Dv] (may be NULL).
+ * Returns 0, or -1 on allocation failure. */
+int kda_oracle_prefill(const float* q, const float* k, const float* v, const float* g,
+                       const float* beta, double scale, const float* h0,
+                       const int32_t* cu_seqlens, int num_seqs, int H, int Dk, int Dv,
+                       double* o, double* ht) {
+    int failed = 0;
+    const int64_t pairs = (int64_t)num_seqs * H;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (int64_t p = 0; p < pairs; ++p) {
+        const int n = (int)(p / H), h = (int)(p % H);
+        double* S = (double*)malloc(sizeof(double) * ((size_t)Dk * Dv + 2 * (size_t)Dv + Dk));
+        if (!S) { failed = 1; continue; }
+        double* vhat = S + (size_t)Dk * Dv;
+        double* err = vhat + Dv;
+        double* dec = err + Dv;
+        const float* h0p = h0 ? h0 + ((int64_t)n * H + h) * (int64_t)Dk * Dv : NULL;
+        for (int64_t i = 0; i < (int64_t)Dk * Dv; ++i) S[i] = h0p ? (double)h0p[i] : 0.0;
+        chain(q, k, v, g, beta, scale, H, Dk, Dv, h, cu_seqlens[n], cu_seqlens[n + 1], S, o,
+              vhat, err, dec);
+        if (ht) memcpy(ht + ((int64_t)n * H + h) * (int64_t)Dk * Dv, S,
+                       sizeof(double) * (size_t)Dk * Dv);
+        free(S);
+    }
+    return failed ? -1 : 0;
+}
+
+/* One decode step: q, k, g [N, H, Dk]; v [N, H, Dv]; beta [N, H];
+ * state double [N, H, Dk, Dv] updated in place; o double [N, H, Dv]. */
+int kda_oracle_decode(const float* q, const float* k, const float* v, const float* g,
+                      const float* beta, double scale, double* state, double* o,
+                      int N, int H, int Dk, int Dv) {
+    int failed = 0;
+    const int64_t pairs = (int64_t)N * H;
+#pragma omp parallel for schedule(static) reduction(| : failed)
+    for (int64_t p = 0; p < pairs; ++p) {
+        double* tmp = (double*)malloc(sizeof(double) * (2 * (size_t)Dv + Dk));
+        if (!tmp) { failed = 1; continue; }
+        /* a decode step is one token of a chain whose "time" index is the pair */
+        const int n = (int)(p / H), h = (int)(p % H);
+        chain(q + (int64_t)n * H * Dk, k + (int64_t)n * H * Dk, v + (int64_t)n * H * Dv,
+              g + (int64_t)n * H * Dk, beta + (int64_t)n * H, scale, H, Dk, Dv, h, 0, 1,
+              state + p * (int64_t)Dk * Dv, o + (int64_t)n * H * Dv, tmp, tmp + Dv,
+              tmp + 2 * Dv);
+        free(tmp);
+    }
+    return failed ? -1 : 0;
+}
