@@ -1,1 +1,161 @@
-"""KDA (Kimi Delta Attention) forward recurrence for AMD MI355X (gfx950)."""
+"""KDA (Kimi Delta Attention) forward recurrence on AMD MI355X (gfx950).
+
+Thin ctypes binding over the C ABI of ``libkda.so`` (declared in
+``include/kda.h``). This module only marshals arguments: tensors must already
+live on the GPU, every step of the computation runs in the library's HIP
+kernels, and there is no CPU fallback -- if the library is missing the calls
+raise.
+
+    o, ht = fwd_chunked(q, k, v, g, beta, scale=1.0, initial_state=None,
+                        output_final_state=True, cu_seqlens=None)
+    o = decode_step(q, k, v, g, beta, state, scale=1.0)     # state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_SUCCESS = 0
+KDA_ERROR_INVALID_VALUE = 1
+KDA_ERROR_NOT_SUPPORTED = 2
+KDA_ERROR_WORKSPACE = 3
+KDA_ERROR_LAUNCH = 4
+KDA_DTYPE_F32 = 0
+KDA_DTYPE_BF16 = 1
+
+EXPORTED = ("kda_status_string", "kda_fwd_chunked_workspace_size", "kda_fwd_chunked",
+            "kda_decode_step")
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} failed: {status_string(status)} ({status})")
+
+
+_lib_handle = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libkda.so (built in-tree by gated_delta_rule_channel_amd.build)."""
+    global _lib_handle
+    if _lib_handle is not None and path is None:
+        return _lib_handle
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m gated_delta_rule_channel_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_fwd_chunked_workspace_size.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.kda_fwd_chunked_workspace_size.restype = i
+    lib.kda_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                    vp, sz, vp]
+    lib.kda_fwd_chunked.restype = i
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, i, i, i, i, i, i, vp]
+    lib.kda_decode_step.restype = i
+    if path is None:
+        _lib_handle = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return KDA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_size(B: int, T: int, H: int, Dk: int, Dv: int, num_seqs: int, varlen: bool,
+                   dtype_code: int) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().kda_fwd_chunked_workspace_size(B, T, H, Dk, Dv, num_seqs, int(varlen),
+                                                       dtype_code, ctypes.byref(out))
+    if st != KDA_SUCCESS:
+        raise KDAError(st, "kda_fwd_chunked_workspace_size")
+    return int(out.value)
+
+
+def _check_gpu(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous GPU tensors")
+
+
+def fwd_chunked(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
+                output_final_state: bool = True, cu_seqlens=None, workspace=None,
+                out=None, final_state=None, out_dtype=None) -> Tuple["object", Optional["object"]]:
+    """Chunked prefill. q, k, g: [B,T,H,Dk]; v: [B,T,H,Dv]; beta: [B,T,H];
+    initial_state: [N,H,Dk,Dv] float32 or None; cu_seqlens: int32 [N+1] (B == 1) or None.
+    out_dtype: torch.float32 (default) or torch.bfloat16.
+    Returns (o [B,T,H,Dv], ht [N,H,Dk,Dv] float32 or None)."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    _check_gpu(q, k, v, g, beta, initial_state, cu_seqlens, workspace, out, final_state)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    code = _dtype_code(q)
+    varlen = cu_seqlens is not None
+    N = (cu_seqlens.numel() - 1) if varlen else B
+    if g.dtype != torch.float32:
+        raise TypeError("g must be float32")
+    if initial_state is not None and initial_state.dtype != torch.float32:
+        raise TypeError("initial_state must be float32")
+    if varlen and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    nbytes = workspace_size(B, T, H, Dk, Dv, N, varlen, code)
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    o = out if out is not None else torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
+    ocode = _dtype_code(o)
+    ht = None
+    if output_final_state:
+        ht = final_state if final_state is not None else torch.empty(
+            (N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    st = load_library().kda_fwd_chunked(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(initial_state),
+        _ptr(ht), _ptr(o), _ptr(cu_seqlens), int(N), int(B), int(T), int(H), int(Dk), int(Dv),
+        code, ocode, _ptr(workspace), nbytes, _stream(q.device))
+    if st != KDA_SUCCESS:
+        raise KDAError(st, "kda_fwd_chunked")
+    return o, ht
+
+
+def decode_step(q, k, v, g, beta, state, scale: float = 1.0, out=None, out_dtype=None):
+    """One decode step. q, k, g: [N,H,Dk]; v: [N,H,Dv]; beta: [N,H];
+    state: [N,H,Dk,Dv] float32, updated in place. Returns o [N,H,Dv] (float32 by default)."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    _check_gpu(q, k, v, g, beta, state, out)
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    code = _dtype_code(q)
+    if g.dtype != torch.float32 or state.dtype != torch.float32:
+        raise TypeError("g and state must be float32")
+    o = out if out is not None else torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
+    st = load_library().kda_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(state), _ptr(o),
+        int(N), int(H), int(Dk), int(Dv), code, _dtype_code(o), _stream(q.device))
+    if st != KDA_SUCCESS:
+        raise KDAError(st, "kda_decode_step")
+    return o

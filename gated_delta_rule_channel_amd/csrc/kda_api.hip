@@ -1,0 +1,127 @@
+// Host side of the C ABI declared in include/kda.h: argument validation,
+// workspace carving and kernel launches. Every check happens before the first
+// launch, so an invalid call enqueues nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+
+namespace kda {
+hipError_t launch_decode(bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
+                         const void* k, const void* v, const float* g, const void* beta,
+                         float scale, float* state, void* o, int N, int H, hipStream_t s);
+hipError_t launch_chunk_map(const int32_t* cu, int N, int T, int max_slots, void* tab,
+                            int32_t* seq_off, hipStream_t s);
+hipError_t launch_prefill(bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
+                          const void* k, const void* v, const float* g, const void* beta,
+                          float scale, const float* h0, float* ht, void* o, const void* tab,
+                          const int32_t* seq_off, uint8_t* blocks, int N, int H, int max_slots,
+                          hipStream_t s);
+size_t prefill_block_bytes(int Dk, int Dv);
+}  // namespace kda
+
+namespace {
+
+bool head_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool dtype_ok(kda_dtype t) { return t == KDA_DTYPE_F32 || t == KDA_DTYPE_BF16; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t ru(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct PrefillPlan {
+    long long max_slots = 0;
+    int nseq = 0;
+    size_t tab_off = 0, seq_off = 0, blocks_off = 0, total = 0;
+};
+
+kda_status plan_prefill(int B, int T, int H, int Dk, int Dv, int num_seqs, bool varlen,
+                        kda_dtype dtype, PrefillPlan* p) {
+    if (B <= 0 || T <= 0 || H <= 0) return KDA_ERROR_INVALID_VALUE;
+    if (!head_ok(Dk) || !head_ok(Dv)) return KDA_ERROR_INVALID_VALUE;
+    if (!dtype_ok(dtype)) return KDA_ERROR_INVALID_VALUE;
+    if (varlen && (B != 1 || num_seqs < 1)) return KDA_ERROR_INVALID_VALUE;
+    const long long tokens = (long long)B * T;
+    if (tokens > (1LL << 30)) return KDA_ERROR_NOT_SUPPORTED;
+    p->nseq = varlen ? num_seqs : B;
+    p->max_slots = varlen ? (long long)T / 64 + num_seqs : (long long)B * ((T + 63) / 64);
+    if (p->max_slots > (1LL << 30) / H) return KDA_ERROR_NOT_SUPPORTED;
+    p->tab_off = 0;
+    p->seq_off = ru((size_t)p->max_slots * 16, 256);
+    p->blocks_off = p->seq_off + ru((size_t)(p->nseq + 1) * 4, 256);
+    p->total = p->blocks_off +
+               (size_t)p->max_slots * H * kda::prefill_block_bytes(Dk, Dv);
+    return KDA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_SUCCESS: return "KDA_SUCCESS";
+        case KDA_ERROR_INVALID_VALUE: return "KDA_ERROR_INVALID_VALUE";
+        case KDA_ERROR_NOT_SUPPORTED: return "KDA_ERROR_NOT_SUPPORTED";
+        case KDA_ERROR_WORKSPACE: return "KDA_ERROR_WORKSPACE";
+        case KDA_ERROR_LAUNCH: return "KDA_ERROR_LAUNCH";
+    }
+    return "KDA_ERROR_UNKNOWN";
+}
+
+kda_status kda_fwd_chunked_workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                          int cu_seqlens_given, kda_dtype dtype, size_t* bytes) {
+    if (!bytes) return KDA_ERROR_INVALID_VALUE;
+    PrefillPlan p;
+    const kda_status st = plan_prefill(B, T, H, Dk, Dv, num_seqs, cu_seqlens_given != 0, dtype, &p);
+    if (st != KDA_SUCCESS) return st;
+    *bytes = p.total;
+    return KDA_SUCCESS;
+}
+
+kda_status kda_fwd_chunked(const void* q, const void* k, const void* v, const float* g,
+                           const void* beta, float scale, const float* h0, float* ht, void* o,
+                           const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int Dk,
+                           int Dv, kda_dtype dtype, kda_dtype o_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !g || !beta || !o) return KDA_ERROR_INVALID_VALUE;
+    if (!dtype_ok(o_dtype)) return KDA_ERROR_INVALID_VALUE;
+    PrefillPlan p;
+    const kda_status st = plan_prefill(B, T, H, Dk, Dv, num_seqs, cu_seqlens != nullptr, dtype, &p);
+    if (st != KDA_SUCCESS) return st;
+    const void* ptrs[] = {q, k, v, g, beta, o, h0, ht};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned(ptr, 16)) return KDA_ERROR_INVALID_VALUE;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERROR_INVALID_VALUE;
+    if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256))
+        return KDA_ERROR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    void* tab = ws + p.tab_off;
+    int32_t* seq_off = reinterpret_cast<int32_t*>(ws + p.seq_off);
+    if (kda::launch_chunk_map(cu_seqlens, p.nseq, T, (int)p.max_slots, tab, seq_off, s) !=
+        hipSuccess)
+        return KDA_ERROR_LAUNCH;
+    if (kda::launch_prefill(dtype == KDA_DTYPE_BF16, o_dtype == KDA_DTYPE_BF16, Dk, Dv, q, k, v,
+                            g, beta, scale, h0, ht, o, tab, seq_off, ws + p.blocks_off, p.nseq,
+                            H, (int)p.max_slots, s) != hipSuccess)
+        return KDA_ERROR_LAUNCH;
+    return KDA_SUCCESS;
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const void* beta, float scale, float* state, void* o, int N, int H,
+                           int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype, void* stream) {
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERROR_INVALID_VALUE;
+    if (N <= 0 || H <= 0 || !head_ok(Dk) || !head_ok(Dv)) return KDA_ERROR_INVALID_VALUE;
+    if (!dtype_ok(dtype) || !dtype_ok(o_dtype)) return KDA_ERROR_INVALID_VALUE;
+    if ((long long)N * H > (1LL << 31) - 1) return KDA_ERROR_NOT_SUPPORTED;
+    const void* ptrs[] = {q, k, v, g, beta, state, o};
+    for (const void* ptr : ptrs)
+        if (!aligned(ptr, 16)) return KDA_ERROR_INVALID_VALUE;
+    if (kda::launch_decode(dtype == KDA_DTYPE_BF16, o_dtype == KDA_DTYPE_BF16, Dk, Dv, q, k, v, g,
+                           beta, scale, state, o, N, H,
+                           reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return KDA_ERROR_LAUNCH;
+    return KDA_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+// Shared device helpers for the KDA kernels (gfx950 / CDNA4, wave64).
+//
+// MFMA conventions used throughout (v_mfma_f32_16x16x32_bf16 and
+// v_mfma_f32_16x16x4_f32), for a lane l of a wave, with m = l % 16 and
+// grp = l / 16:
+//   A fragment: row m of the 16 x K tile, K elements 8*grp .. 8*grp+7 of the
+//               current 32-wide K slice;
+//   B fragment: column m of the K x 16 tile, the same 8 K elements;
+//   C/D:        four fp32 values, rows 4*grp + r (r = 0..3), column m.
+// Only the pairing of K elements between A and B matters, so any layout that
+// gives both operands the same 8 K indices per lane is valid.
+//
+// Operand precision policies (the MFMA operand type of a kernel):
+//   PolF32   -- fp32 operands, eight v_mfma_f32_16x16x4_f32 per 32-wide slice
+//               (element e of each lane's fragment is the e-th 4-wide K step).
+//   PolSplit -- each fp32 operand x is held as two bfloat16 values,
+//               hi = bf16(x) and lo = bf16(x - hi) (about 16 significant bits),
+//               and a product is hi*hi + hi*lo + lo*hi: three
+//               v_mfma_f32_16x16x32_bf16 with fp32 accumulation. Stored
+//               matrices keep the hi and lo parts in two planes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 64;       // tokens per chunk
+constexpr int kBlock = 16;       // tokens per sub-block (MFMA tile edge)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- input / output element access (q, k, v, beta, o) -----------------------------------
+// Load 8 consecutive input elements as floats.
+__device__ __forceinline__ void load8f(float* d, const bf16* p) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = (float)x[e];
+}
+__device__ __forceinline__ void load8f(float* d, const float* p) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
+    d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
+}
+// Store 4 consecutive values converted to T.
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+    bf16x4 x;
+    x[0] = (bf16)a; x[1] = (bf16)b; x[2] = (bf16)c; x[3] = (bf16)d;
+    *reinterpret_cast<bf16x4*>(p) = x;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ float4 load4f(const bf16* p) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+    return make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+}
+__device__ __forceinline__ float4 load4f(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+}
+
+// ---- operand policies ----------------------------------------------------------------------
+struct PolF32 {
+    using Store = float;                    // element type of stored operand matrices
+    static constexpr int kPlanes = 1;
+    struct Frag {
+        float v[8];
+        __device__ __forceinline__ void zero() {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        }
+        __device__ __forceinline__ void set(int e, float x) { v[e] = x; }
+        __device__ __forceinline__ float get(int e) const { return v[e]; }
+    };
+    __device__ static __forceinline__ void mma(floatx4& acc, const Frag& a, const Frag& b) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+    }
+    // element x at index i of a stored matrix whose planes are ps elements apart
+    __device__ static __forceinline__ void put(Store* base, size_t i, size_t /*ps*/, float x) {
+        base[i] = x;
+    }
+    __device__ static __forceinline__ float get(const Store* base, size_t i, size_t /*ps*/) {
+        return base[i];
+    }
+    // 8 consecutive stored elements (32-byte aligned) into a fragment
+    __device__ static __forceinline__ void load(Frag& f, const Store* base, size_t i,
+                                                size_t /*ps*/) {
+        load8f(f.v, base + i);
+    }
+    __device__ static __forceinline__ void store(Store* base, size_t i, size_t /*ps*/,
+                                                 const Frag& f) {
+        reinterpret_cast<float4*>(base + i)[0] = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
+        reinterpret_cast<float4*>(base + i)[1] = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
+    }
+    // 4 consecutive elements (16-byte aligned)
+    __device__ static __forceinline__ void store4(Store* base, size_t i, size_t /*ps*/, float a,
+                                                  float b, float c, float d) {
+        *reinterpret_cast<float4*>(base + i) = make_float4(a, b, c, d);
+    }
+    __device__ static __forceinline__ float4 load4f(const Store* base, size_t i, size_t /*ps*/) {
+        return *reinterpret_cast<const float4*>(base + i);
+    }
+};
+
+struct PolSplit {
+    using Store = bf16;
+    static constexpr int kPlanes = 2;
+    struct Frag {
+        bf16x8 hi, lo;
+        __device__ __forceinline__ void zero() {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { hi[e] = (bf16)0.f; lo[e] = (bf16)0.f; }
+        }
+        __device__ __forceinline__ void set(int e, float x) {
+            const bf16 h = (bf16)x;
+            hi[e] = h;
+            lo[e] = (bf16)(x - (float)h);
+        }
+        __device__ __forceinline__ float get(int e) const { return (float)hi[e] + (float)lo[e]; }
+    };
+    __device__ static __forceinline__ void mma(floatx4& acc, const Frag& a, const Frag& b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+    }
+    __device__ static __forceinline__ void put(Store* base, size_t i, size_t ps, float x) {
+        const bf16 h = (bf16)x;
+        base[i] = h;
+        base[ps + i] = (bf16)(x - (float)h);
+    }
+    __device__ static __forceinline__ float get(const Store* base, size_t i, size_t ps) {
+        return (float)base[i] + (float)base[ps + i];
+    }
+    __device__ static __forceinline__ void load(Frag& f, const Store* base, size_t i, size_t ps) {
+        f.hi = *reinterpret_cast<const bf16x8*>(base + i);
+        f.lo = *reinterpret_cast<const bf16x8*>(base + ps + i);
+    }
+    __device__ static __forceinline__ void store(Store* base, size_t i, size_t ps,
+                                                 const Frag& f) {
+        *reinterpret_cast<bf16x8*>(base + i) = f.hi;
+        *reinterpret_cast<bf16x8*>(base + ps + i) = f.lo;
+    }
+    // 4 consecutive elements (8-byte aligned in each plane)
+    __device__ static __forceinline__ void store4(Store* base, size_t i, size_t ps, float a,
+                                                  float b, float c, float d) {
+        bf16x4 h, l;
+        h[0] = (bf16)a; h[1] = (bf16)b; h[2] = (bf16)c; h[3] = (bf16)d;
+        l[0] = (bf16)(a - (float)h[0]); l[1] = (bf16)(b - (float)h[1]);
+        l[2] = (bf16)(c - (float)h[2]); l[3] = (bf16)(d - (float)h[3]);
+        *reinterpret_cast<bf16x4*>(base + i) = h;
+        *reinterpret_cast<bf16x4*>(base + ps + i) = l;
+    }
+    __device__ static __forceinline__ float4 load4f(const Store* base, size_t i, size_t ps) {
+        const bf16x4 h = *reinterpret_cast<const bf16x4*>(base + i);
+        const bf16x4 l = *reinterpret_cast<const bf16x4*>(base + ps + i);
+        return make_float4((float)h[0] + (float)l[0], (float)h[1] + (float)l[1],
+                           (float)h[2] + (float)l[2], (float)h[3] + (float)l[3]);
+    }
+};
+
+// The operand policy of an input type: fp32 inputs keep fp32 MFMA, bf16 inputs use
+// split-bf16 operands.
+template <typename TI> struct PolOf;
+template <> struct PolOf<float> { using type = PolF32; };
+template <> struct PolOf<bf16> { using type = PolSplit; };
+
+}  // namespace kda

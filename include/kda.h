@@ -1,0 +1,131 @@
+/*
+ * kda.h -- C ABI of the KDA (Kimi Delta Attention) forward recurrence on
+ * AMD MI355X (gfx950). Link with libkda.so.
+ *
+ * The operation. For every sequence, head and token t, with the head's state
+ * S (d_k x d_v, one row per key channel, float32):
+ *
+ *   S~  = Diag(exp(g_t)) S          decay each key channel
+ *   v^  = S~^T k_t                  predict the value stored at k_t
+ *   e   = beta_t (v_t - v^)         beta-scaled error
+ *   S   = S~ + k_t e^T              rank-one write
+ *   o_t = S^T (scale * q_t)         read of the updated state
+ *
+ * These are the five steps of "Module 03 - KDA I: The Delta-Rule Recurrence"
+ * (jared-hpc.com), section 2, with beta folded into the error as on "Kimi
+ * Delta Attention (KDA)" (brain.bigb.es), where the log-decay g = log(alpha)
+ * and the [.., d_k, d_v] state layout are also given (section "KDA: one gate
+ * per key channel"). kda_fwd_chunked evaluates whole sequences with the
+ * chunkwise schedule of that page's section "Two schedules for the same
+ * recurrence" (chunks of 64 tokens); kda_decode_step applies one step.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous, owned
+ *    by the caller. The library allocates no memory and keeps no global
+ *    mutable state; calls on different streams are independent.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    default stream). Arguments are validated on the host before anything is
+ *    enqueued: on any error nothing runs and no output is touched. Faults that
+ *    happen while kernels execute surface at the caller's next
+ *    synchronisation, not in the returned status.
+ *  - Supported head sizes: Dk, Dv in {16, 32, 64, 128}.
+ *  - dtype selects the element type of q, k, v and beta, o_dtype that of o:
+ *    KDA_DTYPE_F32 (float) or KDA_DTYPE_BF16 (bfloat16). g and all states are
+ *    always float32. Pointers must be 16-byte aligned.
+ *  - Precision. With float32 inputs every product runs on fp32 MFMA. With
+ *    bfloat16 inputs every operand is carried as a pair of bfloat16 values
+ *    (high part and rounding residue, about 16 significant bits) and each
+ *    product takes three bf16 MFMAs with fp32 accumulation; states and
+ *    accumulators are float32 throughout. A float32 o keeps the full result;
+ *    a bfloat16 o is the float32 result rounded to nearest even.
+ *  - Preconditions that are documented, not checked: g is finite; states and
+ *    inputs are finite; o does not overlap any input; cu_seqlens is
+ *    non-decreasing with cu[0] = 0 and cu[num_seqs] = T.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_SUCCESS = 0,
+    KDA_ERROR_INVALID_VALUE = 1,  /* bad pointer, size, alignment or combination */
+    KDA_ERROR_NOT_SUPPORTED = 2,  /* valid request the library does not implement */
+    KDA_ERROR_WORKSPACE = 3,      /* workspace missing or smaller than required */
+    KDA_ERROR_LAUNCH = 4          /* the HIP runtime refused a kernel launch */
+} kda_status;
+
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kda_status_string(kda_status s);
+
+/* Bytes of device workspace kda_fwd_chunked needs for these sizes.
+ * Host only: touches no device memory. cu_seqlens_given says whether the
+ * call will pass cu_seqlens (then B must be 1 and num_seqs is the number of
+ * packed sequences); the bound used is floor(T/64) + num_seqs chunks per head
+ * for packed input and B * ceil(T/64) otherwise, so cu_seqlens is never read
+ * on the host. The size does not depend on dtype (operands take 4 bytes per
+ * element in both precisions). Errors: KDA_ERROR_INVALID_VALUE for a NULL
+ * `bytes`, a non-positive size, or an unsupported head size. */
+kda_status kda_fwd_chunked_workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                          int cu_seqlens_given, kda_dtype dtype, size_t* bytes);
+
+/* Chunked prefill over B x T tokens (or num_seqs packed sequences).
+ *
+ *  q, k   [B, T, H, Dk]  dtype         (q normally carries d_k^-1/2 already)
+ *  v      [B, T, H, Dv]  dtype
+ *  g      [B, T, H, Dk]  float32       log-decay per key channel, g <= 0
+ *  beta   [B, T, H]      dtype         write strength
+ *  scale                               multiplies q in the read
+ *  h0     [N, H, Dk, Dv] float32 or NULL (zero initial state)
+ *  ht     [N, H, Dk, Dv] float32 or NULL (final state not stored); may equal h0
+ *  o      [B, T, H, Dv]  o_dtype       output, every element written
+ *  cu_seqlens  device int32[num_seqs + 1] or NULL. When given, B must be 1
+ *              and the sequences are the packed segments of T; otherwise the
+ *              N = B rows are the sequences and num_seqs is ignored.
+ *  workspace   device buffer of at least kda_fwd_chunked_workspace_size()
+ *              bytes (256-byte aligned); its contents are scratch.
+ *
+ * Sequences never share a chunk; a zero-length sequence leaves ht = h0 (or
+ * zeros). Any finite g is handled exactly up to float32 rounding: every
+ * in-chunk decay factor the kernels form is bounded by 2^120 in magnitude,
+ * and 16-token blocks whose decay is too steep for that bound take a slower
+ * pairwise path.
+ * Errors (nothing is enqueued): KDA_ERROR_INVALID_VALUE for NULL q, k, v, g,
+ * beta or o, non-positive sizes, B != 1 with cu_seqlens, num_seqs < 1 with
+ * cu_seqlens, misaligned pointers or an unsupported head size;
+ * KDA_ERROR_WORKSPACE if workspace is NULL or too small; KDA_ERROR_LAUNCH if
+ * a launch fails. */
+kda_status kda_fwd_chunked(const void* q, const void* k, const void* v, const float* g,
+                           const void* beta, float scale, const float* h0, float* ht, void* o,
+                           const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int Dk,
+                           int Dv, kda_dtype dtype, kda_dtype o_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* One decode step for N independent requests against persistent states.
+ *
+ *  q, k   [N, H, Dk]  dtype
+ *  v      [N, H, Dv]  dtype
+ *  g      [N, H, Dk]  float32
+ *  beta   [N, H]      dtype
+ *  state  [N, H, Dk, Dv] float32, read and updated in place (each element is
+ *         read once and written once)
+ *  o      [N, H, Dv]  o_dtype
+ *
+ * Errors (nothing is enqueued): KDA_ERROR_INVALID_VALUE for NULL pointers,
+ * non-positive sizes, misalignment or an unsupported head size;
+ * KDA_ERROR_LAUNCH if the launch fails. */
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const void* beta, float scale, float* state, void* o, int N, int H,
+                           int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

@@ -1,0 +1,116 @@
+"""The C ABI library on a host without a GPU: it loads, exports every symbol the
+header declares, sizes workspaces, and rejects invalid arguments before any
+device work (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_channel_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_channel_amd import build
+        build.build()
+    return kda.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(kda.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError):
+        kda.load_library(str(tmp_path / "nope.so"))
+
+
+def test_status_strings(lib):
+    assert kda.status_string(0) == "KDA_SUCCESS"
+    assert kda.status_string(1) == "KDA_ERROR_INVALID_VALUE"
+    assert kda.status_string(3) == "KDA_ERROR_WORKSPACE"
+    assert kda.status_string(99).startswith("KDA_ERROR")
+
+
+def test_workspace_size(lib):
+    # chunk slots: B * ceil(T/64) fixed-length, floor(T/64) + N packed
+    # per (chunk, head): W, Qd, KdT, U, A_qk at 4 bytes per element, exp(G_end) in fp32
+    per_block = 4 * (3 * 64 * 128 + 64 * 128 + 64 * 64) + 128 * 4
+    n = kda.workspace_size(1, 8192, 64, 128, 128, 1, False, kda.KDA_DTYPE_BF16)
+    assert n == kda.workspace_size(1, 8192, 64, 128, 128, 1, False, kda.KDA_DTYPE_F32)
+    slots = 128
+    header = ((slots * 16 + 255) // 256) * 256 + 256
+    assert n == header + slots * 64 * ((per_block + 255) // 256 * 256)
+    n2 = kda.workspace_size(1, 105872, 64, 128, 128, 8, True, kda.KDA_DTYPE_BF16)
+    assert n2 > kda.workspace_size(1, 105872 - 64 * 8, 64, 128, 128, 8, True, kda.KDA_DTYPE_BF16)
+    with pytest.raises(kda.KDAError):
+        kda.workspace_size(1, 64, 1, 48, 64, 1, False, kda.KDA_DTYPE_F32)
+    with pytest.raises(kda.KDAError):
+        kda.workspace_size(2, 64, 1, 64, 64, 2, True, kda.KDA_DTYPE_F32)   # packed needs B == 1
+    with pytest.raises(kda.KDAError):
+        kda.workspace_size(1, 0, 1, 64, 64, 1, False, kda.KDA_DTYPE_F32)
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails host validation first
+
+
+def _fwd(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=1.0, h0=None, ht=None, o=FAKE,
+             cu=None, N=1, B=1, T=64, H=1, Dk=64, Dv=64, dtype=0, odtype=0, ws=None, wsb=0,
+             stream=None)
+    a.update(over)
+    return lib.kda_fwd_chunked(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["h0"],
+                               a["ht"], a["o"], a["cu"], a["N"], a["B"], a["T"], a["H"],
+                               a["Dk"], a["Dv"], a["dtype"], a["odtype"], a["ws"], a["wsb"],
+                               a["stream"])
+
+
+def test_prefill_validation(lib):
+    E = kda.KDA_ERROR_INVALID_VALUE
+    assert _fwd(lib, q=None) == E
+    assert _fwd(lib, o=None) == E
+    assert _fwd(lib, Dk=48) == E
+    assert _fwd(lib, Dv=256) == E
+    assert _fwd(lib, T=0) == E
+    assert _fwd(lib, H=-1) == E
+    assert _fwd(lib, dtype=7) == E
+    assert _fwd(lib, odtype=5) == E
+    assert _fwd(lib, cu=FAKE, B=2, N=2) == E             # packed input requires B == 1
+    assert _fwd(lib, cu=FAKE, N=0) == E
+    assert _fwd(lib, k=FAKE + 4) == E                    # misaligned
+    assert _fwd(lib, ht=FAKE + 8) == E
+    assert _fwd(lib) == kda.KDA_ERROR_WORKSPACE          # no workspace
+    assert _fwd(lib, ws=FAKE, wsb=10) == kda.KDA_ERROR_WORKSPACE
+    assert _fwd(lib, ws=FAKE + 16, wsb=1 << 40) == kda.KDA_ERROR_WORKSPACE   # not 256-aligned
+
+
+def test_decode_validation(lib):
+    E = kda.KDA_ERROR_INVALID_VALUE
+    f = lambda **o: lib.kda_decode_step(o.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, 1.0,
+                                        o.get("state", FAKE), FAKE, o.get("N", 4), 2,
+                                        o.get("Dk", 64), o.get("Dv", 64), o.get("dtype", 1),
+                                        o.get("odtype", 0), None)
+    assert f(q=None) == E
+    assert f(state=None) == E
+    assert f(N=0) == E
+    assert f(Dk=24) == E
+    assert f(Dv=512) == E
+    assert f(dtype=2) == E
+    assert f(odtype=3) == E
+    assert f(state=FAKE + 4) == E

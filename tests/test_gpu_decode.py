@@ -1,0 +1,76 @@
+"""Decode-step parity on the GPU (through the C ABI) against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_channel_amd as kda
+from gated_delta_rule_channel_amd import inputs as I
+from oracle import native
+from tests.parity_util import check
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x: I.DecodeInputs, dtype: str):
+    dev = torch.device("cuda:0")
+    q, k, v, g, b = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta))
+    st = x.state.to(dev)
+    o = kda.decode_step(q, k, v, g, b, st, scale=x.scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), st.cpu().numpy()
+
+
+def test_decode_full_workload():
+    """The decode workload at full size: 256 requests x 64 heads x 128 x 128 fp32 states."""
+    w = I.WORKLOADS[3]
+    print(f"[decode] {w.name}", flush=True)
+    x = I.decode_inputs(w)
+    o_ref, S_ref = native.decode(x.q, x.k, x.v, x.g, x.beta, x.state)
+    o, S = _run(x, w.dtype)
+    check("o", o, o_ref, w.dtype)
+    check("state", S, S_ref, w.dtype)
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 16), (16, 128), (64, 64)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_shapes(dk, dv, dtype):
+    import dataclasses
+    w = dataclasses.replace(I.WORKLOADS[3], Dk=dk, Dv=dv, dtype=dtype, H=3, N=5)
+    print(f"[decode] dk={dk} dv={dv} {dtype}", flush=True)
+    x = I.decode_inputs(w)
+    o_ref, S_ref = native.decode(x.q, x.k, x.v, x.g, x.beta, x.state, scale=0.75)
+    x.scale = 0.75
+    o, S = _run(x, dtype)
+    check("o", o, o_ref, dtype)
+    check("state", S, S_ref, dtype)
+
+
+def test_decode_steps_equal_prefill():
+    """T decode steps against a carried state equal one prefill over the same tokens."""
+    w = I.WORKLOADS[1]
+    x = I.prefill_inputs(w, heads=[0, 1], T=70)
+    dev = torch.device("cuda:0")
+    o_pf, ht_pf = kda.fwd_chunked(*(t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta)),
+                                  initial_state=x.h0.to(dev))
+    st = x.h0.to(dev).clone()
+    outs = []
+    for t in range(x.q.shape[1]):
+        sl = lambda a: a[:, t].contiguous().to(dev)
+        outs.append(kda.decode_step(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), st))
+    torch.cuda.synchronize()
+    o_dec = torch.stack(outs, dim=1).cpu().numpy()
+    check("o(decode) vs o(prefill)", o_dec, o_pf.cpu().numpy(), "f32")
+    check("state(decode) vs ht(prefill)", st.cpu().numpy(), ht_pf.cpu().numpy(), "f32")
+
+
+def test_decode_bf16_output_is_rounded_fp32_output():
+    w = I.WORKLOADS[3]
+    x = I.decode_inputs(w, heads=[0, 1, 2], N=7)
+    dev = torch.device("cuda:0")
+    q, k, v, g, b = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta))
+    s1, s2 = x.state.to(dev), x.state.to(dev)
+    o32 = kda.decode_step(q, k, v, g, b, s1)
+    o16 = kda.decode_step(q, k, v, g, b, s2, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(s1, s2)
