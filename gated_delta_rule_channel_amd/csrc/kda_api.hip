@@ -14,9 +14,9 @@ hipError_t launch_chunk_map(const int32_t* cu, int N, int T, int max_slots, void
                             int32_t* seq_off, hipStream_t s);
 hipError_t launch_prefill(bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
                           const void* k, const void* v, const float* g, const void* beta,
-                          float scale, const float* h0, float* ht, void* o, const void* tab,
-                          const int32_t* seq_off, uint8_t* blocks, int N, int H, int max_slots,
-                          hipStream_t s);
+                          float scale, const float* h0, float* ht, void* o, const int32_t* cu,
+                          int T, const void* tab, const int32_t* seq_off, uint8_t* blocks, int N,
+                          int H, int max_slots, hipStream_t s);
 size_t prefill_block_bytes(int Dk, int Dv);
 }  // namespace kda
 
@@ -101,8 +101,8 @@ kda_status kda_fwd_chunked(const void* q, const void* k, const void* v, const fl
         hipSuccess)
         return KDA_ERROR_LAUNCH;
     if (kda::launch_prefill(dtype == KDA_DTYPE_BF16, o_dtype == KDA_DTYPE_BF16, Dk, Dv, q, k, v,
-                            g, beta, scale, h0, ht, o, tab, seq_off, ws + p.blocks_off, p.nseq,
-                            H, (int)p.max_slots, s) != hipSuccess)
+                            g, beta, scale, h0, ht, o, cu_seqlens, T, tab, seq_off,
+                            ws + p.blocks_off, p.nseq, H, (int)p.max_slots, s) != hipSuccess)
         return KDA_ERROR_LAUNCH;
     return KDA_SUCCESS;
 }

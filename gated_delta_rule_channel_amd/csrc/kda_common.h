@@ -72,6 +72,31 @@ __device__ __forceinline__ float4 load4f(const float* p) {
     return *reinterpret_cast<const float4*>(p);
 }
 
+// Eight consecutive input elements kept in their input type (packed for bf16).
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+    bf16x8 v;
+    __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (bf16)0.f;
+    }
+    __device__ __forceinline__ float get(int e) const { return (float)v[e]; }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = reinterpret_cast<const float4*>(p)[0];
+        b = reinterpret_cast<const float4*>(p)[1];
+    }
+    __device__ __forceinline__ void zero() { a = make_float4(0.f, 0.f, 0.f, 0.f); b = a; }
+    __device__ __forceinline__ float get(int e) const {
+        const float4& x = e < 4 ? a : b;
+        const int i = e & 3;
+        return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
+    }
+};
+
 // ---- operand policies ----------------------------------------------------------------------
 struct PolF32 {
     using Store = float;                    // element type of stored operand matrices
@@ -89,6 +114,20 @@ struct PolF32 {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+    }
+    // product with an operand b that is exact in the policy's leading part
+    __device__ static __forceinline__ void mma_exact(floatx4& acc, const Frag& a, const Frag& b) {
+        mma(acc, a, b);
+    }
+    // 16-wide K fragments (16x16x16 shapes): lane (m, grp) holds K = 4 grp + r, r = 0..3
+    struct Frag4 {
+        float v[4];
+        __device__ __forceinline__ void set(int r, float x) { v[r] = x; }
+    };
+    __device__ static __forceinline__ void mma16(floatx4& acc, const Frag4& a, const Frag4& b) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[r], b.v[r], acc, 0, 0, 0);
     }
     // element x at index i of a stored matrix whose planes are ps elements apart
     __device__ static __forceinline__ void put(Store* base, size_t i, size_t /*ps*/, float x) {
@@ -115,6 +154,13 @@ struct PolF32 {
     __device__ static __forceinline__ float4 load4f(const Store* base, size_t i, size_t /*ps*/) {
         return *reinterpret_cast<const float4*>(base + i);
     }
+    // 4 stored elements kept raw until use (prefetch buffers)
+    struct Raw4 { float4 v; };
+    __device__ static __forceinline__ void load4raw(Raw4& r, const Store* base, size_t i,
+                                                    size_t /*ps*/) {
+        r.v = *reinterpret_cast<const float4*>(base + i);
+    }
+    __device__ static __forceinline__ float4 raw4f(const Raw4& r) { return r.v; }
 };
 
 struct PolSplit {
@@ -137,6 +183,28 @@ struct PolSplit {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+    }
+    // product with an operand b that is exact in bfloat16 (b.lo == 0): two MFMAs
+    __device__ static __forceinline__ void mma_exact(floatx4& acc, const Frag& a, const Frag& b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+    }
+    // 16-wide K fragments (16x16x16 shapes): lane (m, grp) holds K = 4 grp + r, r = 0..3
+    struct Frag4 {
+        bf16x4 hi, lo;
+        __device__ __forceinline__ void set(int r, float x) {
+            const bf16 h = (bf16)x;
+            hi[r] = h;
+            lo[r] = (bf16)(x - (float)h);
+        }
+    };
+    __device__ static __forceinline__ void mma16(floatx4& acc, const Frag4& a, const Frag4& b) {
+        typedef short short4v __attribute__((ext_vector_type(4)));
+        const short4v ah = __builtin_bit_cast(short4v, a.hi), al = __builtin_bit_cast(short4v, a.lo);
+        const short4v bh = __builtin_bit_cast(short4v, b.hi), bl = __builtin_bit_cast(short4v, b.lo);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
     }
     __device__ static __forceinline__ void put(Store* base, size_t i, size_t ps, float x) {
         const bf16 h = (bf16)x;
@@ -171,7 +239,35 @@ struct PolSplit {
         return make_float4((float)h[0] + (float)l[0], (float)h[1] + (float)l[1],
                            (float)h[2] + (float)l[2], (float)h[3] + (float)l[3]);
     }
+    struct Raw4 { bf16x4 h, l; };
+    __device__ static __forceinline__ void load4raw(Raw4& r, const Store* base, size_t i,
+                                                    size_t ps) {
+        r.h = *reinterpret_cast<const bf16x4*>(base + i);
+        r.l = *reinterpret_cast<const bf16x4*>(base + ps + i);
+    }
+    __device__ static __forceinline__ float4 raw4f(const Raw4& r) {
+        return make_float4((float)r.h[0] + (float)r.l[0], (float)r.h[1] + (float)r.l[1],
+                           (float)r.h[2] + (float)r.l[2], (float)r.h[3] + (float)r.l[3]);
+    }
 };
+
+// ---- cross-lane helpers (a DPP row = 16 consecutive lanes = one value of grp) ------------
+// inclusive prefix sum over the 16 lanes of each row
+__device__ __forceinline__ float row_scan16(float x) {
+    int v = __builtin_bit_cast(int, x);
+    float s = x;
+    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x111, 0xf, 0xf, true));
+    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x112, 0xf, 0xf, true));
+    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x114, 0xf, 0xf, true));
+    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x118, 0xf, 0xf, true));
+    (void)v;
+    return s;
+}
+// value of lane n (compile-time) of each row, broadcast to the row
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
+}
 
 // The operand policy of an input type: fp32 inputs keep fp32 MFMA, bf16 inputs use
 // split-bf16 operands.

@@ -24,7 +24,7 @@
 //  * prep_kernel: one workgroup per (chunk, head), fully parallel. Computes
 //    everything that does not depend on S and writes it to the workspace:
 //    W [64][Dk], Qd = scale q exp(G) [64][Dk], KdT = (k exp(G_end-G))^T
-//    [Dk][64], U [64][Dv], A_qk [64][64] (operand precision) and exp(G_end)
+//    [Dk][64], U^T [Dv][64], A_qk [64][64] (operand precision) and exp(G_end)
 //    [Dk] (fp32).
 //  * state_kernel: one workgroup per (sequence, head, 32-column value tile),
 //    the only serial pass; S stays in fp32 MFMA accumulators for the whole
@@ -57,7 +57,7 @@ struct WsLayout {
     static constexpr size_t W = 0;                        // [64][DK]   W
     static constexpr size_t QD = W + 64 * DK * 4;         // [64][DK]   scale q exp(G)
     static constexpr size_t KDT = QD + 64 * DK * 4;       // [DK][64]   (k exp(G_end - G))^T
-    static constexpr size_t U = KDT + DK * 64 * 4;        // [64][DV]   U
+    static constexpr size_t U = KDT + DK * 64 * 4;        // [DV][64]   U^T
     static constexpr size_t AQ = U + 64 * DV * 4;         // [64][64]   A_qk
     static constexpr size_t GEND = AQ + 64 * 64 * 4;      // float [DK] exp(G_end)
     static constexpr size_t BYTES = round_up(GEND + DK * sizeof(float), 256);
@@ -122,41 +122,22 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
 // ------------------------------------------------------------------------------------------
 // prep kernel
 // ------------------------------------------------------------------------------------------
-template <int DK, int DV>
-struct PrepShape {
-    static constexpr int KS = DK >= 32 ? DK / 32 : 1;   // 32-wide channel slices (padded)
-    static constexpr int DKP = KS * 32;
-    static constexpr int GST = DKP + 4;                 // fp32 row stride of the prefix sums
-    static constexpr int AST = 64 + 4;                  // fp32 row stride of A_kk and T
-    static constexpr int KBST = DKP + 8;                // row stride of k exp(G_end(J) - G)
-    static constexpr int TST = 64 + 8;                  // row stride of transposed operands
-};
+// One workgroup (4 waves) per (chunk, head). Wave w owns the 32-channel slice
+// [32 w, 32 w + 32) of the keys for all 64 tokens, held in MFMA fragment layout: lane
+// (m, grp) holds token 16 I + m of every 16-token block I and the 8 channels
+// 32 w + 8 grp + e. In-chunk prefix sums are DPP scans across the 16 lanes of a row.
+// Each wave forms its slice's partial A_kk / A_qk blocks with MFMAs; the four partials of
+// a block are summed in LDS in a fixed order (the waves visit the row blocks in rotated
+// order, one writer per block per step), so results are bitwise reproducible. Wave w
+// also owns the 32 value columns [32 w, 32 w + 32) for U. Register-level transposes
+// (token-major fragments to channel-major ones) are products with an identity slice.
+__host__ __device__ constexpr int tri_tile(int I, int J) { return I * (I + 1) / 2 + J; }
 
-template <typename Pol, int DK, int DV>
-struct PrepSmem {
-    using Sh = PrepShape<DK, DV>;
-    using St = typename Pol::Store;
-    static constexpr int P = Pol::kPlanes;
-    union {
-        float G[64][Sh::GST];        // block-local prefix sums (log2 units); later T
-        float T[64][Sh::AST];
-    } g;
-    float A[64][Sh::AST];            // A_kk (strictly lower, fp32)
-    union {
-        St KB[P][64][Sh::KBST];      // k exp(G_end(J) - G), per row block J
-        St VbT[P][DV][Sh::TST];      // (beta v)^T
-    } kv;
-    St WopT[P][Sh::DKP][Sh::TST];    // (beta k exp(G))^T
-    float lam[4][Sh::DKP];           // block totals
-    float mid[4][Sh::DKP];           // prefix sum at the 8th row of each block
-    float Pf[4][Sh::DKP];            // exp(G at the end of block I-1), chunk-start reference
-    float Z[4][Sh::DKP];             // exp(G_end - G at the end of block I)
-    float X[3][Sh::DKP];             // exp(G_r(I) - G_end(J)) for (I,J) = (2,0), (3,0), (3,1)
-    float Y[4][16][17];              // per-wave scratch of the block inverse
-    int bad[4];                      // diagonal block needs the pairwise path
-};
+// Keeps the compiler from sinking prefetch loads to their first use: loads issued before
+// this point stay before it, so they are in flight while the following code runs.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
 
-// 16 x 16 x 16 fp32 product on LDS blocks, one wave: lane (r = l/4, cq = l%4) computes
+// 16 x 16 x 16 fp32 product on LDS tiles, one wave: lane (r = l/4, cq = l%4) computes
 // out[r][4cq .. 4cq+3] (+)= sign * sum_m X[r][m] Y[m][4cq ..].
 __device__ __forceinline__ void blk16_mm(float* out, int ost, const float* X, int xst,
                                          const float* Y, int yst, float sign, bool accumulate) {
@@ -177,6 +158,28 @@ __device__ __forceinline__ void blk16_mm(float* out, int ost, const float* X, in
     }
 }
 
+// Channel-major tile of a token-major fragment: with x holding rows (tokens) m and 8 K
+// columns 8 grp + e of a 32-wide slice, returns the C-layout tile D[t][n] = x[t][16 h + n]
+// (lane (n, grp) gets D[4 grp + r][n]), i.e. x times an identity slice (exact).
+template <typename Pol>
+__device__ __forceinline__ floatx4 transpose_half(const typename Pol::Frag& x, int h, int m,
+                                                  int grp) {
+    typename Pol::Frag E;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) E.set(e, (8 * grp + e == 16 * h + m) ? 1.f : 0.f);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    Pol::mma_exact(acc, x, E);
+    return acc;
+}
+
+template <typename Pol>
+__device__ __forceinline__ typename Pol::Frag4 frag4_of(const floatx4& d) {
+    typename Pol::Frag4 f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f.set(r, d[r]);
+    return f;
+}
+
 template <typename TI, int DK, int DV>
 __global__ __launch_bounds__(256) void prep_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
@@ -184,17 +187,19 @@ __global__ __launch_bounds__(256) void prep_kernel(
     const int4* __restrict__ tab, uint8_t* __restrict__ ws, int H) {
     using Pol = typename PolOf<TI>::type;
     using Frag = typename Pol::Frag;
+    using Frag4 = typename Pol::Frag4;
     using St = typename Pol::Store;
-    using Sh = PrepShape<DK, DV>;
     using Ly = WsLayout<DK, DV>;
-    constexpr int KS = Sh::KS, DKP = Sh::DKP;
-    __shared__ PrepSmem<Pol, DK, DV> sm;
-    St* const sKB = &sm.kv.KB[0][0][0];
-    St* const sVbT = &sm.kv.VbT[0][0][0];
-    St* const sWopT = &sm.WopT[0][0][0];
-    constexpr size_t psKB = (size_t)64 * Sh::KBST;
-    constexpr size_t psVbT = (size_t)DV * Sh::TST;
-    constexpr size_t psWopT = (size_t)DKP * Sh::TST;
+    constexpr int NSL = DK >= 32 ? DK / 32 : 1;          // channel slices (32 wide, padded)
+    constexpr int DVP = DV >= 32 ? DV : 32;
+    constexpr int NVS = DVP / 32;                         // value slices
+    // lower 16x16 blocks, rows padded to 20 floats so that 16 lanes reading 4 floats of
+    // 16 different rows hit distinct LDS banks
+    __shared__ float sKK[10][16][20];                     // A_kk lower blocks
+    __shared__ float sQK[10][16][20];                     // A_qk lower blocks
+    __shared__ float sT[10][16][20];                      // T = (I + A_kk)^-1 lower blocks
+    __shared__ float sY[4][16][17];                       // per-wave scratch of the inverse
+    __shared__ float4 sDW[4][4][2][64];                   // per wave: (beta k exp G)^T tiles
 
     const int slot = blockIdx.x, h = blockIdx.y;
     const int4 ci = tab[slot];
@@ -213,193 +218,230 @@ __global__ __launch_bounds__(256) void prep_kernel(
     float* gGend = reinterpret_cast<float*>(blk + Ly::GEND);
     constexpr size_t psW = (size_t)64 * DK, psU = (size_t)64 * DV, psAq = 64 * 64;
 
-    // ---- phase 1: block-local prefix sums of g (log2 units); wave = row block ----
-    {
-        const int I = wave;
-        for (int c = lane; c < DKP; c += 64) {
-            float run = 0.f;
-#pragma unroll 4
-            for (int r = 0; r < 16; ++r) {
-                const int i = 16 * I + r;
-                float x = 0.f;
-                if (c < DK && i < L) x = g[(size_t)(t0 + i) * rowq + (size_t)h * DK + c] * kLog2e;
-                run += x;
-                sm.g.G[i][c] = run;
-                if (r == 7) sm.mid[I][c] = run;
-            }
-            sm.lam[I][c] = run;
-        }
-        if (lane == 0) sm.bad[I] = 0;
-    }
-    // v rows for U, loaded early into registers: thread -> (token row, 8 columns)
-    constexpr int VCG = DV / 8;                                  // 8-column groups per row
-    constexpr int VRPP = (256 / VCG) < 64 ? (256 / VCG) : 64;   // rows per pass
-    constexpr int VPASS = 64 / VRPP;
-    const bool vact = tid / VCG < VRPP;
-    float vreg[VPASS][8];
-    float vbeta[VPASS];
-    {
-        const int vc = (tid % VCG) * 8;
-#pragma unroll
-        for (int p = 0; p < VPASS; ++p) {
-            const int i = tid / VCG + p * VRPP;
-            if (vact && i < L) {
-                load8f(vreg[p], v + (size_t)(t0 + i) * rowv + (size_t)h * DV + vc);
-                vbeta[p] = to_f(beta[(size_t)(t0 + i) * H + h]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vreg[p][e] = 0.f;
-                vbeta[p] = 0.f;
-            }
-        }
-    }
-    __syncthreads();
-    // ---- phase 1b: cross-block factors per channel ----
-    for (int c = tid; c < DKP; c += 256) {
-        const float l0 = sm.lam[0][c], l1 = sm.lam[1][c], l2 = sm.lam[2][c], l3 = sm.lam[3][c];
-        sm.Pf[0][c] = 1.f;
-        sm.Pf[1][c] = fast_exp2(l0);
-        sm.Pf[2][c] = fast_exp2(l0 + l1);
-        sm.Pf[3][c] = fast_exp2(l0 + l1 + l2);
-        sm.Z[0][c] = fast_exp2(l1 + l2 + l3);
-        sm.Z[1][c] = fast_exp2(l2 + l3);
-        sm.Z[2][c] = fast_exp2(l3);
-        sm.Z[3][c] = 1.f;
-        sm.X[0][c] = fast_exp2(l1);          // (2,0)
-        sm.X[1][c] = fast_exp2(l1 + l2);     // (3,0)
-        sm.X[2][c] = fast_exp2(l2);          // (3,1)
-        if (c < DK) gGend[c] = fast_exp2(l0 + l1 + l2 + l3);
-    }
-    __syncthreads();
+    const bool cs = wave < NSL;                  // this wave owns a channel slice
+    const int c0 = 32 * wave + 8 * grp;          // first of this lane's 8 channels
+    const bool cvalid = cs && c0 < DK;
 
-    // ---- phase 2: decay factors and operands, MFMA fragment layout ----
-    // wave = row block I, lane -> row i = 16 I + m, channels 32 kappa + 8 grp + e.
-    // The diagonal block products are accumulated here, slice by slice.
-    const int I = wave;
-    const int i = 16 * I + m;
-    const bool valid = i < L;
-    const float bi = valid ? to_f(beta[(size_t)(t0 + i) * H + h]) : 0.f;
-    Frag KA[KS], QA[KS];
-    floatx4 dkk = {0.f, 0.f, 0.f, 0.f}, dqk = {0.f, 0.f, 0.f, 0.f};
-    bool bad = false;
+    // ---- loads: g, k, q of the slice for all 64 tokens; beta of the lane's tokens ----
+    float G[4][8];
+    Raw8<TI> kr[4], qr[4];
+    float bt[4];
 #pragma unroll
-    for (int kap = 0; kap < KS; ++kap) {
-        const int c0 = 32 * kap + 8 * grp;
-        float kf[8], qf[8];
-        if (valid && c0 < DK) {
-            load8f(kf, k + (size_t)(t0 + i) * rowq + (size_t)h * DK + c0);
-            load8f(qf, q + (size_t)(t0 + i) * rowq + (size_t)h * DK + c0);
+    for (int I = 0; I < 4; ++I) {
+        const int row = 16 * I + m;
+        const bool ok = cvalid && row < L;
+        if (ok) {
+            const size_t off = (size_t)(t0 + row) * rowq + (size_t)h * DK + c0;
+            load8f(G[I], g + off);
+            kr[I].load(k + off);
+            qr[I].load(q + off);
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { kf[e] = 0.f; qf[e] = 0.f; }
+            for (int e = 0; e < 8; ++e) G[I][e] = 0.f;
+            kr[I].zero();
+            qr[I].zero();
         }
-        Frag KE, QE, KR, qd;
+        bt[I] = row < L ? to_f(beta[(size_t)(t0 + row) * H + h]) : 0.f;
+    }
+    // zero the A accumulators while the loads are in flight
+    for (int idx = tid; idx < 10 * 16 * 20; idx += 256) {
+        (&sKK[0][0][0])[idx] = 0.f;
+        (&sQK[0][0][0])[idx] = 0.f;
+    }
+
+    // ---- block-local prefix sums (log2 units) and the chunk total per channel ----
+    float gtot[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gtot[e] = 0.f;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int c = c0 + e;
-            const float G = sm.g.G[i][c];
-            const float x = G - sm.mid[I][c];
-            bad |= fabsf(x) > 120.f;
-            const float e1 = fast_exp2(x), e2 = fast_exp2(-x);
-            const float ea = fast_exp2(G), eb = fast_exp2(sm.lam[I][c] - G);
-            const float kk = kf[e], qq = scale * qf[e];
-            KE.set(e, bi * kk * e1);
-            QE.set(e, qq * e1);
-            KR.set(e, kk * e2);
-            const float ka = bi * kk * ea, qa = qq * ea, kb = kk * eb;
-            KA[kap].set(e, ka);
-            QA[kap].set(e, qa);
-            const float p = sm.Pf[I][c];
-            qd.set(e, qa * p);
-            Pol::put(sKB, (size_t)i * Sh::KBST + c, psKB, kb);
-            Pol::put(sWopT, (size_t)c * Sh::TST + i, psWopT, ka * p);
-            if (c < DK) Pol::put(gKdT, (size_t)c * 64 + i, psW, kb * sm.Z[I][c]);
+            G[I][e] = row_scan16(G[I][e] * kLog2e);
+            gtot[e] += row_bcast<15>(G[I][e]);
         }
-        if (c0 < DK) Pol::store(gQd, (size_t)i * DK + c0, psW, qd);
-        // diagonal block: entry (row i, column j = 16 I + 4 grp + r) of the transposed product
-        Pol::mma(dkk, KR, KE);
-        Pol::mma(dqk, KR, QE);
     }
-    if (__any(bad) && lane == 0) sm.bad[I] = 1;
-    __syncthreads();
-
-    // ---- phase 3: A_kk and A_qk blocks of row block I (transposed MFMA products) ----
-    // acc[r] of the product (A = column-block operand, B = row-block operand) holds
-    // the entry (row i = 16 I + m, column j = 16 J + 4 grp + r).
-    {
-        const bool pairwise = sm.bad[I] != 0;
-        for (int J = 0; J <= I; ++J) {
-            floatx4 akk = dkk, aqk = dqk;
-            if (J < I) {
-                akk = floatx4{0.f, 0.f, 0.f, 0.f};
-                aqk = floatx4{0.f, 0.f, 0.f, 0.f};
-                const int xi = (I == 2 && J == 0) ? 0 : (I == 3 && J == 0) ? 1 : 2;
-                const bool scaled = J < I - 1;
-                const int j = 16 * J + m;
+    if (cvalid && m == 0) {
 #pragma unroll
-                for (int kap = 0; kap < KS; ++kap) {
-                    const int c0 = 32 * kap + 8 * grp;
+        for (int e = 0; e < 8; ++e) gGend[c0 + e] = fast_exp2(gtot[e]);
+    }
+    __syncthreads();                                    // A accumulators zeroed
+
+    // ---- rotated pass over the row blocks: operands, Qd, Kd^T, partial A blocks ----
+#pragma unroll 1
+    for (int st = 0; st < 4; ++st) {
+        if (cs) {
+            const int I = (wave + st) & 3;
+            const int row = 16 * I + m;
+            float bi = 0.f;
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+                if (J == I) bi = bt[J];
+            // selects block I's registers (I is wave-dependent) without dynamic indexing
+            auto pick = [&](int e, float& Gv, float& kk, float& qq) {
+#pragma unroll
+                for (int J = 0; J < 4; ++J)
+                    if (J == I) { Gv = G[J][e]; kk = kr[J].get(e); qq = qr[J].get(e); }
+            };
+            // (a) chunk-start / chunk-end references: Qd (to the workspace), Kd^T (to the
+            //     workspace, transposed), Wop^T (to LDS for W)
+            {
+                Frag Wop, Qd, Kd;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float Gv = 0.f, kk = 0.f, qq = 0.f, pf = 0.f;
+                    pick(e, Gv, kk, qq);
+#pragma unroll
+                    for (int J = 0; J < 3; ++J) {
+                        const float lamJ = row_bcast<15>(G[J][e]);
+                        if (J < I) pf += lamJ;
+                    }
+                    const float Gc = pf + Gv;
+                    const float ec = fast_exp2(Gc), ed = fast_exp2(gtot[e] - Gc);
+                    Wop.set(e, bi * kk * ec);
+                    Qd.set(e, scale * qq * ec);
+                    Kd.set(e, kk * ed);
+                }
+                if (cvalid) Pol::store(gQd, (size_t)row * DK + c0, psW, Qd);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const floatx4 dk = transpose_half<Pol>(Kd, hh, m, grp);
+                    const int ch = 32 * wave + 16 * hh + m;
+                    if (32 * wave + 16 * hh < DK)
+                        Pol::store4(gKdT, (size_t)ch * 64 + 16 * I + 4 * grp, psW, dk[0], dk[1],
+                                    dk[2], dk[3]);
+                    const floatx4 dw = transpose_half<Pol>(Wop, hh, m, grp);
+                    sDW[wave][I][hh][lane] = make_float4(dw[0], dw[1], dw[2], dw[3]);
+                }
+            }
+            // (b) diagonal block (midpoint reference, or pairwise when out of range)
+            {
+                floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+                Frag KE, QE, KR;
+                bool bad = false;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float Gv = 0.f, kk = 0.f, qq = 0.f;
+                    pick(e, Gv, kk, qq);
+                    const float x = Gv - row_bcast<7>(Gv);
+                    bad |= fabsf(x) > 120.f;
+                    const float e1 = fast_exp2(x), e2 = fast_exp2(-x);
+                    KE.set(e, bi * kk * e1);
+                    QE.set(e, scale * qq * e1);
+                    KR.set(e, kk * e2);
+                }
+                if (!__any(bad)) {
+                    Pol::mma(akk, KR, KE);
+                    Pol::mma(aqk, KR, QE);
+                } else {
+                    // exact pairwise sums over this slice: entry (i = m, j = jj)
+#pragma unroll 1
+                    for (int jj = 0; jj < 16; ++jj) {
+                        float skk = 0.f, sqk = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            float Gv = 0.f, kk = 0.f, qq = 0.f;
+                            pick(e, Gv, kk, qq);
+                            const int src = (lane & 48) | jj;
+                            const float Gj = __shfl(Gv, src);
+                            const float kj = __shfl(kk, src);
+                            const float d = jj <= m ? fast_exp2(Gv - Gj) : 0.f;
+                            skk += kk * kj * d;
+                            sqk += scale * qq * kj * d;
+                        }
+                        skk += __shfl_xor(skk, 16);
+                        skk += __shfl_xor(skk, 32);
+                        sqk += __shfl_xor(sqk, 16);
+                        sqk += __shfl_xor(sqk, 32);
+                        if ((jj >> 2) == grp) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (r == (jj & 3)) { akk[r] = bi * skk; aqk[r] = sqk; }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 4 * grp + r;
+                    if (!(j < m)) akk[r] = 0.f;
+                    if (!(j <= m)) aqk[r] = 0.f;
+                }
+                float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(I, I)][m][4 * grp]);
+                float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(I, I)][m][4 * grp]);
+                float4 a = *pk, c = *pq;
+                a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
+                c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
+                *pk = a;
+                *pq = c;
+            }
+            // (c) off-diagonal blocks J < I: reference at the end of block I - 1
+            if (I > 0) {
+                Frag KA, QA;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float Gv = 0.f, kk = 0.f, qq = 0.f;
+                    pick(e, Gv, kk, qq);
+                    const float ea = fast_exp2(Gv);
+                    KA.set(e, bi * kk * ea);
+                    QA.set(e, scale * qq * ea);
+                }
+#pragma unroll 1
+                for (int J = 0; J < I; ++J) {
+                    // k of block J decayed to the start of block I
                     Frag b;
-                    if (scaled) {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            b.set(e, Pol::get(sKB, (size_t)j * Sh::KBST + c0 + e, psKB) *
-                                         sm.X[xi][c0 + e]);
-                    } else {
-                        Pol::load(b, sKB, (size_t)j * Sh::KBST + c0, psKB);
+                    for (int e = 0; e < 8; ++e) {
+                        float GJ = 0.f, kJ = 0.f, xs = 0.f;
+#pragma unroll
+                        for (int J2 = 0; J2 < 3; ++J2) {
+                            const float lamJ2 = row_bcast<15>(G[J2][e]);
+                            if (J2 == J) { GJ = G[J2][e]; kJ = kr[J2].get(e); xs += lamJ2; }
+                            if (J2 > J && J2 < I) xs += lamJ2;
+                        }
+                        b.set(e, kJ * fast_exp2(xs - GJ));
                     }
-                    Pol::mma(akk, b, KA[kap]);
-                    Pol::mma(aqk, b, QA[kap]);
+                    floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+                    Pol::mma(akk, b, KA);
+                    Pol::mma(aqk, b, QA);
+                    float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(I, J)][m][4 * grp]);
+                    float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(I, J)][m][4 * grp]);
+                    float4 a = *pk, c = *pq;
+                    a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
+                    c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
+                    *pk = a;
+                    *pq = c;
                 }
             }
-            const int j0 = 16 * J + 4 * grp;
-            float kv4[4], qv4[4];
+        }
+        __syncthreads();
+    }
+
+    // ---- value slice of this wave (for U), loaded now so it lands during the inverse ----
+    const int vc0 = 32 * wave + 8 * grp;
+    const bool vvalid = wave < NVS && vc0 < DV;
+    float vf[4][8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = j0 + r;
-                kv4[r] = (j < i) ? akk[r] : 0.f;
-                qv4[r] = (j <= i) ? aqk[r] : 0.f;
-            }
-            if (!(J == I && pairwise)) {
-                *reinterpret_cast<float4*>(&sm.A[i][j0]) = make_float4(kv4[0], kv4[1], kv4[2], kv4[3]);
-                Pol::store4(gAq, (size_t)i * 64 + j0, psAq, qv4[0], qv4[1], qv4[2], qv4[3]);
-            }
-        }
-        // upper blocks are zero
-        for (int J = I + 1; J < 4; ++J) {
-            const int j0 = 16 * J + 4 * grp;
-            Pol::store4(gAq, (size_t)i * 64 + j0, psAq, 0.f, 0.f, 0.f, 0.f);
-            *reinterpret_cast<float4*>(&sm.A[i][j0]) = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        if (pairwise) {
-            // exact path for a diagonal block whose midpoint factors leave 2^+-120
-            for (int idx = lane; idx < 256; idx += 64) {
-                const int ii = idx >> 4, jj = idx & 15;
-                const int ri = 16 * I + ii, rj = 16 * I + jj;
-                float skk = 0.f, sqk = 0.f;
-                if (jj <= ii && ri < L) {
-                    const TI* ki = k + (size_t)(t0 + ri) * rowq + (size_t)h * DK;
-                    const TI* qi = q + (size_t)(t0 + ri) * rowq + (size_t)h * DK;
-                    const TI* kj = k + (size_t)(t0 + rj) * rowq + (size_t)h * DK;
-                    for (int c = 0; c < DK; ++c) {
-                        const float d = fast_exp2(sm.g.G[ri][c] - sm.g.G[rj][c]);
-                        const float kjc = to_f(kj[c]) * d;
-                        skk += to_f(ki[c]) * kjc;
-                        sqk += to_f(qi[c]) * kjc;
-                    }
-                }
-                const float bri = ri < L ? to_f(beta[(size_t)(t0 + ri) * H + h]) : 0.f;
-                sm.A[ri][rj] = jj < ii ? bri * skk : 0.f;
-                Pol::put(gAq, (size_t)ri * 64 + rj, psAq, jj <= ii ? scale * sqk : 0.f);
-            }
+    for (int I = 0; I < 4; ++I) {
+        const int row = 16 * I + m;
+        if (vvalid && row < L) {
+            load8f(vf[I], v + (size_t)(t0 + row) * rowv + (size_t)h * DV + vc0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vf[I][e] = 0.f;
         }
     }
-    __syncthreads();
+    // A_qk to the workspace (upper blocks zero)
+    for (int idx = tid; idx < 64 * 16; idx += 256) {
+        const int row = idx >> 4, cg = idx & 15;
+        const int I = row >> 4, il = row & 15, J = cg >> 2, jl = (cg & 3) * 4;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (J <= I) x = *reinterpret_cast<const float4*>(&sQK[tri_tile(I, J)][il][jl]);
+        Pol::store4(gAq, (size_t)row * 64 + cg * 4, psAq, x.x, x.y, x.z, x.w);
+    }
 
-    // ---- phase 4: T = (I + A_kk)^-1, blocked; G is dead, its space holds T ----
-    float (*Tm)[Sh::AST] = sm.g.T;
+    // ---- T = (I + A_kk)^-1: diagonal blocks by forward substitution, then by levels ----
     {
-        // diagonal 16x16 inverses by forward substitution, one column per lane
+        const int I = wave;
         if (lane < 16) {
             const int n = lane;
             float x[16];
@@ -407,79 +449,84 @@ __global__ __launch_bounds__(256) void prep_kernel(
             for (int ii = 0; ii < 16; ++ii) {
                 float s = 0.f;
 #pragma unroll
-                for (int mm = 0; mm < ii; ++mm) s += sm.A[16 * I + ii][16 * I + mm] * x[mm];
+                for (int mm = 0; mm < ii; ++mm) s += sKK[tri_tile(I, I)][ii][mm] * x[mm];
                 x[ii] = (ii == n) ? 1.f : (ii > n ? -s : 0.f);
             }
 #pragma unroll
-            for (int ii = 0; ii < 16; ++ii) Tm[16 * I + ii][16 * I + n] = x[ii];
-        }
-        // zero the strictly-upper blocks of row block I
-        for (int idx = lane; idx < 16 * 64; idx += 64) {
-            const int ii = idx >> 6, jj = idx & 63;
-            if (jj >= 16 * (I + 1)) Tm[16 * I + ii][jj] = 0.f;
+            for (int ii = 0; ii < 16; ++ii) sT[tri_tile(I, I)][ii][n] = x[ii];
         }
     }
     __syncthreads();
-    // level d: T[I][I-d] = -T[I][I] * sum_{M=I-d}^{I-1} A[I][M] T[M][I-d]
     for (int d = 1; d <= 3; ++d) {
+        const int I = wave;
         const bool act = I >= d;
         const int J = I - d;
         if (act) {
             for (int M = J; M < I; ++M)
-                blk16_mm(&sm.Y[I][0][0], 17, &sm.A[16 * I][16 * M], Sh::AST, &Tm[16 * M][16 * J],
-                         Sh::AST, 1.f, M != J);
+                blk16_mm(&sY[I][0][0], 17, &sKK[tri_tile(I, M)][0][0], 20,
+                         &sT[tri_tile(M, J)][0][0], 20, 1.f, M != J);
         }
         __syncthreads();
         if (act)
-            blk16_mm(&Tm[16 * I][16 * J], Sh::AST, &Tm[16 * I][16 * I], Sh::AST, &sm.Y[I][0][0], 17,
-                     -1.f, false);
+            blk16_mm(&sT[tri_tile(I, J)][0][0], 20, &sT[tri_tile(I, I)][0][0], 20,
+                     &sY[I][0][0], 17, -1.f, false);
         __syncthreads();
     }
 
-    // ---- phase 5: (beta v)^T into LDS (KB is dead), then W = T Wop and U = T (beta v) ----
-    if (vact) {
-        const int vc = (tid % VCG) * 8;
+    // ---- W = T (beta k exp G) and U = T (beta v), transposed products over 16-token blocks ----
+    // W^T(ct, I) = sum_{J <= I} Wop_J^T (channels x tokens j) T_IJ^T (tokens j x tokens i);
+    // lane (n = token i, grp) of the result holds W[16 I + n][channel 4 grp + r].
+    if (cs) {
 #pragma unroll
-        for (int p = 0; p < VPASS; ++p) {
-            const int ii = tid / VCG + p * VRPP;
+        for (int hh = 0; hh < 2; ++hh) {
+            if (32 * wave + 16 * hh < DK) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                Pol::put(sVbT, (size_t)(vc + e) * Sh::TST + ii, psVbT, vbeta[p] * vreg[p][e]);
+                for (int I = 0; I < 4; ++I) {
+                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int J = 0; J <= I; ++J) {
+                        const float4 w4 = sDW[wave][J][hh][lane];
+                        Frag4 aw;
+                        aw.set(0, w4.x); aw.set(1, w4.y); aw.set(2, w4.z); aw.set(3, w4.w);
+                        Frag4 tb;
+                        const float4 t4 = *reinterpret_cast<const float4*>(&sT[tri_tile(I, J)][m][4 * grp]);
+                        tb.set(0, t4.x); tb.set(1, t4.y); tb.set(2, t4.z); tb.set(3, t4.w);
+                        Pol::mma16(acc, aw, tb);
+                    }
+                    Pol::store4(gW, (size_t)(16 * I + m) * DK + 32 * wave + 16 * hh + 4 * grp, psW,
+                                acc[0], acc[1], acc[2], acc[3]);
+                }
+            }
         }
     }
-    __syncthreads();
-    {
-        // wave -> 16 output rows (tokens 16 wave ..); B operand = rows of T (K = tokens j)
-        const int it = wave;
-        const int nks = it < 2 ? 1 : 2;               // 32-token slices with nonzero T[i][j]
-        const int row = 16 * it + m;
-        Frag tb[2];
+    if (wave < NVS) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            if (s < nks) {
+        for (int hh = 0; hh < 2; ++hh) {
+            if (32 * wave + 16 * hh < DV) {
+                Frag4 av[4];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) tb[s].set(e, Tm[row][32 * s + 8 * grp + e]);
+                for (int J = 0; J < 4; ++J) {
+                    Frag vb;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vb.set(e, bt[J] * vf[J][e]);
+                    av[J] = frag4_of<Pol>(transpose_half<Pol>(vb, hh, m, grp));
+                }
+                // U(I, ct) = sum_{J <= I} T_IJ (tokens i x tokens j) (beta v)_J (tokens j x
+                // values); lane (n = value, grp) of the result holds U[16 I + 4 grp + r][n]
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int J = 0; J <= I; ++J) {
+                        Frag4 ta;
+                        const float4 t4 = *reinterpret_cast<const float4*>(&sT[tri_tile(I, J)][m][4 * grp]);
+                        ta.set(0, t4.x); ta.set(1, t4.y); ta.set(2, t4.z); ta.set(3, t4.w);
+                        Pol::mma16(acc, ta, av[J]);
+                    }
+                    Pol::store4(gU, (size_t)(32 * wave + 16 * hh + m) * 64 + 16 * I + 4 * grp, psU,
+                                acc[0], acc[1], acc[2], acc[3]);
+                }
             }
-        }
-        for (int ct = 0; ct < DK / 16; ++ct) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < nks; ++s) {
-                Frag a;
-                Pol::load(a, sWopT, (size_t)(16 * ct + m) * Sh::TST + 32 * s + 8 * grp, psWopT);
-                Pol::mma(acc, a, tb[s]);
-            }
-            Pol::store4(gW, (size_t)row * DK + 16 * ct + 4 * grp, psW, acc[0], acc[1], acc[2],
-                        acc[3]);
-        }
-        for (int ct = 0; ct < DV / 16; ++ct) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < nks; ++s) {
-                Frag a;
-                Pol::load(a, sVbT, (size_t)(16 * ct + m) * Sh::TST + 32 * s + 8 * grp, psVbT);
-                Pol::mma(acc, a, tb[s]);
-            }
-            Pol::store4(gU, (size_t)row * DV + 16 * ct + 4 * grp, psU, acc[0], acc[1], acc[2],
-                        acc[3]);
         }
     }
 }
@@ -487,37 +534,115 @@ __global__ __launch_bounds__(256) void prep_kernel(
 // ------------------------------------------------------------------------------------------
 // state kernel
 // ------------------------------------------------------------------------------------------
+// One workgroup of 8 waves per (sequence, head, 32-column value tile). Waves 0-3 (the E
+// role) own token tile w of every chunk: E = U - W S, O = Qd S + A_qk E and the output
+// store. Waves 4-7 (the S role) own channel tiles w-4, w, ... of the state, kept in fp32
+// MFMA accumulators for the whole sequence: S' = Diag(exp G_end) S + Kd^T E. The two roles
+// meet twice per chunk through LDS: E [value][token] and the operand copy of S
+// [value][channel]. Every product is oriented so that the MFMA result tile has tokens or
+// channels along its rows: a lane then holds 4 consecutive rows of one value column, which
+// is 4 consecutive elements of those LDS layouts (8-byte LDS stores, no 2-byte scatter).
+// Each role loads only its own workspace operands, one chunk ahead, into two alternating
+// register sets.
 template <int DK, int DV, int BV>
 struct StateShape {
     static constexpr int KS = DK >= 32 ? DK / 32 : 1;
     static constexpr int DKP = KS * 32;
     static constexpr int NVT = BV / 16;                 // value tiles of the workgroup
     static constexpr int NCT = DK / 16;                 // channel tiles of the state
-    static constexpr int NST = NVT * NCT;               // state tiles
-    static constexpr int MAXT = (NST + 3) / 4;          // state tiles per wave
-    static constexpr int SST = DKP + 8;                 // row stride of the S^T copy
-    static constexpr int EST = 64 + 8;                  // row stride of E^T
+    static constexpr int CTW = NCT >= 4 ? NCT / 4 : 1;  // channel tiles per S-role wave
+    static constexpr int SST = DKP + 8;                 // row stride of the S copy
+    static constexpr int EST = 64 + 8;                  // row stride of E
     static constexpr int VT = DV / BV;                  // value tiles per head
 };
 
+template <typename Pol, int DK, int DV, int BV>
+struct EOps {                          // E-role operands of one chunk (token tile = wave)
+    using Sh = StateShape<DK, DV, BV>;
+    using Frag = typename Pol::Frag;
+    Frag w[Sh::KS], qd[Sh::KS];        // rows of W and Qd
+    typename Pol::Raw4 u[Sh::NVT];     // U^T at (value column, 4 tokens)
+    Frag aq[2];                        // row of A_qk in 32-token slices
+};
+
+template <typename Pol, int DK, int DV, int BV>
+struct SOps {                          // S-role operands of one chunk
+    using Sh = StateShape<DK, DV, BV>;
+    using Frag = typename Pol::Frag;
+    Frag kd[Sh::CTW][2];               // rows of Kd^T of the owned channel tiles
+    float4 gd[Sh::CTW];                // exp(G_end) of the lane's 4 channels per tile
+};
+
+template <typename Pol, int DK, int DV, int BV>
+__device__ __forceinline__ void load_e_ops(EOps<Pol, DK, DV, BV>& c,
+                                           const uint8_t* __restrict__ ws, int cidx, int h, int H,
+                                           int v0, int tw, int m, int grp) {
+    using Sh = StateShape<DK, DV, BV>;
+    using Ly = WsLayout<DK, DV>;
+    using St = typename Pol::Store;
+    constexpr size_t psW = (size_t)64 * DK, psU = (size_t)64 * DV, psAq = 64 * 64;
+    const uint8_t* blk = ws + ((size_t)cidx * H + h) * Ly::BYTES;
+    const St* gW = reinterpret_cast<const St*>(blk + Ly::W);
+    const St* gQd = reinterpret_cast<const St*>(blk + Ly::QD);
+    const St* gU = reinterpret_cast<const St*>(blk + Ly::U);
+    const St* gAq = reinterpret_cast<const St*>(blk + Ly::AQ);
+    const int tok = 16 * tw + m;
+#pragma unroll
+    for (int kap = 0; kap < Sh::KS; ++kap) {
+        const int c0 = 32 * kap + 8 * grp;
+        if (c0 < DK) {
+            Pol::load(c.w[kap], gW, (size_t)tok * DK + c0, psW);
+            Pol::load(c.qd[kap], gQd, (size_t)tok * DK + c0, psW);
+        } else {
+            c.w[kap].zero();
+            c.qd[kap].zero();
+        }
+    }
+#pragma unroll
+    for (int vr = 0; vr < Sh::NVT; ++vr)
+        Pol::load4raw(c.u[vr], gU, (size_t)(v0 + 16 * vr + m) * 64 + 16 * tw + 4 * grp, psU);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        if (s == 0 || tw >= 2) Pol::load(c.aq[s], gAq, (size_t)tok * 64 + 32 * s + 8 * grp, psAq);
+    }
+}
+
+template <typename Pol, int DK, int DV, int BV>
+__device__ __forceinline__ void load_s_ops(SOps<Pol, DK, DV, BV>& c, const uint8_t* __restrict__ ws,
+                                           int cidx, int h, int H, int sw, int m, int grp) {
+    using Sh = StateShape<DK, DV, BV>;
+    using Ly = WsLayout<DK, DV>;
+    using St = typename Pol::Store;
+    constexpr size_t psW = (size_t)64 * DK;
+    const uint8_t* blk = ws + ((size_t)cidx * H + h) * Ly::BYTES;
+    const St* gKdT = reinterpret_cast<const St*>(blk + Ly::KDT);
+    const float* gGend = reinterpret_cast<const float*>(blk + Ly::GEND);
+#pragma unroll
+    for (int j = 0; j < Sh::CTW; ++j) {
+        const int ct = sw + 4 * j;
+        c.gd[j] = *reinterpret_cast<const float4*>(gGend + 16 * ct + 4 * grp);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            Pol::load(c.kd[j][ks], gKdT, (size_t)(16 * ct + m) * 64 + 32 * ks + 8 * grp, psW);
+    }
+}
+
 template <typename TI, typename TO, int DK, int DV, int BV>
-__global__ __launch_bounds__(256) void state_kernel(
-    const int4* __restrict__ tab, const int32_t* __restrict__ seq_off,
+__global__ __launch_bounds__(512) void state_kernel(
+    const int32_t* __restrict__ cu, int T, const int32_t* __restrict__ seq_off,
     const uint8_t* __restrict__ ws, const float* __restrict__ h0, float* __restrict__ ht,
     TO* __restrict__ o, int N, int H) {
     using Pol = typename PolOf<TI>::type;
     using Frag = typename Pol::Frag;
     using St = typename Pol::Store;
     using Sh = StateShape<DK, DV, BV>;
-    using Ly = WsLayout<DK, DV>;
-    constexpr int KS = Sh::KS, NVT = Sh::NVT, NCT = Sh::NCT, NST = Sh::NST, MAXT = Sh::MAXT;
+    constexpr int KS = Sh::KS, NVT = Sh::NVT, NCT = Sh::NCT, CTW = Sh::CTW;
     constexpr int P = Pol::kPlanes;
-    __shared__ St SLs[P][BV][Sh::SST];     // operand copy of S^T [value][channel]
-    __shared__ St ELs[P][BV][Sh::EST];     // E^T [value][token]
+    __shared__ St SLs[P][BV][Sh::SST];     // operand copy of S [value][channel]
+    __shared__ St ELs[P][BV][Sh::EST];     // E [value][token]
     St* const SL = &SLs[0][0][0];
     St* const EL = &ELs[0][0][0];
     constexpr size_t psS = (size_t)BV * Sh::SST, psE = (size_t)BV * Sh::EST;
-    constexpr size_t psW = (size_t)64 * DK, psU = (size_t)64 * DV, psAq = 64 * 64;
 
     // blocks b, b+8, b+16, ... share an XCD: keep all value tiles of a chain on one XCD
     const int b = blockIdx.x;
@@ -529,49 +654,47 @@ __global__ __launch_bounds__(256) void state_kernel(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int m = lane & 15, grp = lane >> 4;
+    const bool erole = wave < 4;
+    const int tw = wave & 3;                       // token tile (E role) / S-role index
+    const bool owns = !erole && (NCT >= 4 || tw < NCT);
 
-    // zero the pad channels of the S^T copy once (only read when DK < 32)
-    for (int idx = tid; idx < BV * (Sh::SST - DK); idx += 256) {
+    // zero the pad channels of the S copy once (only read when DK < 32)
+    for (int idx = tid; idx < BV * (Sh::SST - DK); idx += 512) {
         const int r = idx / (Sh::SST - DK), c = DK + idx % (Sh::SST - DK);
         Pol::put(SL, (size_t)r * Sh::SST + c, psS, 0.f);
     }
-    // state tiles owned by this wave: s = wave + 4 t -> (value tile s / NCT, channel tile s % NCT)
-    floatx4 S[MAXT];
+    // S-role state tiles: channel tile ct = tw + 4 j, value tile vr; lane (n = value, grp)
+    // holds S[16 ct + 4 grp + r][v0 + 16 vr + n]
+    floatx4 S[CTW][NVT];
     const size_t sbase = ((size_t)n * H + h) * DK * DV;
 #pragma unroll
-    for (int t = 0; t < MAXT; ++t) {
-        const int s = wave + 4 * t;
-        S[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (s < NST) {
-            const int vr = s / NCT, ct = s % NCT;
-            const int c = 16 * ct + m, vv = v0 + 16 * vr + 4 * grp;
-            if (h0) {
-                const float4 x = *reinterpret_cast<const float4*>(h0 + sbase + (size_t)c * DV + vv);
-                S[t] = floatx4{x.x, x.y, x.z, x.w};
-            }
+    for (int j = 0; j < CTW; ++j) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Pol::put(SL, (size_t)(16 * vr + 4 * grp + r) * Sh::SST + c, psS, S[t][r]);
+        for (int vr = 0; vr < NVT; ++vr) {
+            S[j][vr] = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (owns) {
+                const int c = 16 * (tw + 4 * j) + 4 * grp, vv = v0 + 16 * vr + m;
+                if (h0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[j][vr][r] = h0[sbase + (size_t)(c + r) * DV + vv];
+                }
+                Pol::store4(SL, (size_t)(16 * vr + m) * Sh::SST + c, psS, S[j][vr][0],
+                            S[j][vr][1], S[j][vr][2], S[j][vr][3]);
+            }
         }
     }
-    __syncthreads();
 
+    // The chunks of sequence n are the consecutive slots [c_beg, c_end); chunk c covers
+    // tokens [s_beg + 64 (c - c_beg), min(+64, s_end)). No per-chunk table reads happen in
+    // the loop (a scalar load there would share lgkmcnt with the LDS traffic and stall it).
     const int c_beg = seq_off[n], c_end = seq_off[n + 1];
+    const int s_beg = cu ? cu[n] : n * T, s_end = cu ? cu[n + 1] : (n + 1) * T;
     const size_t rowo = (size_t)H * DV;
-    for (int cidx = c_beg; cidx < c_end; ++cidx) {
-        const int4 ci = tab[cidx];
-        const int t0 = ci.x, L = ci.y;
-        const uint8_t* blk = ws + ((size_t)cidx * H + h) * Ly::BYTES;
-        const St* gW = reinterpret_cast<const St*>(blk + Ly::W);
-        const St* gQd = reinterpret_cast<const St*>(blk + Ly::QD);
-        const St* gKdT = reinterpret_cast<const St*>(blk + Ly::KDT);
-        const St* gU = reinterpret_cast<const St*>(blk + Ly::U);
-        const St* gAq = reinterpret_cast<const St*>(blk + Ly::AQ);
-        const float* gGend = reinterpret_cast<const float*>(blk + Ly::GEND);
 
-        // E^T = U^T - S^T W^T and O^T = S^T Qd^T for token tile w = wave
-        const int tok = 16 * wave + m;
-        floatx4 accE[NVT], accO[NVT];
+    // E role: E = U - W S into LDS; O = Qd S + A_qk E to memory. Tiles (token tile tw,
+    // value tile vr); lane (n = value, grp) holds rows (tokens) 16 tw + 4 grp + r.
+    auto e_phase1 = [&](const EOps<Pol, DK, DV, BV>& cur, floatx4 (&accO)[NVT]) {
+        floatx4 accE[NVT];
 #pragma unroll
         for (int vr = 0; vr < NVT; ++vr) {
             accE[vr] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -580,96 +703,129 @@ __global__ __launch_bounds__(256) void state_kernel(
 #pragma unroll
         for (int kap = 0; kap < KS; ++kap) {
             const int c0 = 32 * kap + 8 * grp;
-            Frag bw, bq;
-            if (c0 < DK) {
-                Pol::load(bw, gW, (size_t)tok * DK + c0, psW);
-                Pol::load(bq, gQd, (size_t)tok * DK + c0, psW);
-            } else {
-                bw.zero();
-                bq.zero();
-            }
 #pragma unroll
             for (int vr = 0; vr < NVT; ++vr) {
-                Frag a;
-                Pol::load(a, SL, (size_t)(16 * vr + m) * Sh::SST + c0, psS);
-                Pol::mma(accE[vr], a, bw);
-                Pol::mma(accO[vr], a, bq);
+                Frag b;
+                Pol::load(b, SL, (size_t)(16 * vr + m) * Sh::SST + c0, psS);
+                Pol::mma(accE[vr], cur.w[kap], b);
+                Pol::mma(accO[vr], cur.qd[kap], b);
             }
         }
 #pragma unroll
         for (int vr = 0; vr < NVT; ++vr) {
-            const float4 u = Pol::load4f(gU, (size_t)tok * DV + v0 + 16 * vr + 4 * grp, psU);
-            const float ur[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float e = ur[r] - accE[vr][r];
-                Pol::put(EL, (size_t)(16 * vr + 4 * grp + r) * Sh::EST + tok, psE, e);
-            }
+            const float4 u = Pol::raw4f(cur.u[vr]);
+            Pol::store4(EL, (size_t)(16 * vr + m) * Sh::EST + 16 * tw + 4 * grp, psE,
+                        u.x - accE[vr][0], u.y - accE[vr][1], u.z - accE[vr][2],
+                        u.w - accE[vr][3]);
         }
-        __syncthreads();
-        // O^T += E^T A_qk^T over the in-chunk tokens j <= tok
-        {
-            const int nks = wave < 2 ? 1 : 2;
-            for (int s = 0; s < nks; ++s) {
-                Frag bq;
-                Pol::load(bq, gAq, (size_t)tok * 64 + 32 * s + 8 * grp, psAq);
+    };
+    auto e_phase2 = [&](const EOps<Pol, DK, DV, BV>& cur, floatx4 (&accO)[NVT], int cidx) {
+        const int t0 = s_beg + kChunk * (cidx - c_beg);
+        const int len = s_end - t0 < kChunk ? s_end - t0 : kChunk;
+        const int nks = tw < 2 ? 1 : 2;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            if (s2 < nks) {
 #pragma unroll
                 for (int vr = 0; vr < NVT; ++vr) {
-                    Frag a;
-                    Pol::load(a, EL, (size_t)(16 * vr + m) * Sh::EST + 32 * s + 8 * grp, psE);
-                    Pol::mma(accO[vr], a, bq);
+                    Frag b;
+                    Pol::load(b, EL, (size_t)(16 * vr + m) * Sh::EST + 32 * s2 + 8 * grp, psE);
+                    Pol::mma(accO[vr], cur.aq[s2], b);
                 }
             }
-            if (tok < L) {
-                TO* orow = o + (size_t)(t0 + tok) * rowo + (size_t)h * DV + v0;
+        }
 #pragma unroll
-                for (int vr = 0; vr < NVT; ++vr)
-                    store4(orow + 16 * vr + 4 * grp, accO[vr][0], accO[vr][1], accO[vr][2],
-                           accO[vr][3]);
+        for (int r = 0; r < 4; ++r) {
+            const int tok = 16 * tw + 4 * grp + r;
+            if (tok < len) {
+                TO* orow = o + (size_t)(t0 + tok) * rowo + (size_t)h * DV + v0 + m;
+#pragma unroll
+                for (int vr = 0; vr < NVT; ++vr) orow[16 * vr] = from_f<TO>(accO[vr][r]);
             }
         }
-        // S^T = S^T Diag(exp G_end) + E^T Kd
+    };
+    // S role: S = Diag(exp G_end) S + Kd^T E, then the operand copy of S
+    auto s_phase2 = [&](const SOps<Pol, DK, DV, BV>& cur) {
+        if (!owns) return;
 #pragma unroll
-        for (int t = 0; t < MAXT; ++t) {
-            const int s = wave + 4 * t;
-            if (s < NST) {
-                const int vr = s / NCT, ct = s % NCT;
-                const int c = 16 * ct + m;
-                const float gd = gGend[c];
+        for (int j = 0; j < CTW; ++j) {
+            const int c = 16 * (tw + 4 * j) + 4 * grp;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[t][r] *= gd;
+            for (int vr = 0; vr < NVT; ++vr) {
+                S[j][vr][0] *= cur.gd[j].x;
+                S[j][vr][1] *= cur.gd[j].y;
+                S[j][vr][2] *= cur.gd[j].z;
+                S[j][vr][3] *= cur.gd[j].w;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    Frag a, bk;
-                    Pol::load(a, EL, (size_t)(16 * vr + m) * Sh::EST + 32 * ks + 8 * grp, psE);
-                    Pol::load(bk, gKdT, (size_t)c * 64 + 32 * ks + 8 * grp, psW);
-                    Pol::mma(S[t], a, bk);
+                    Frag b;
+                    Pol::load(b, EL, (size_t)(16 * vr + m) * Sh::EST + 32 * ks + 8 * grp, psE);
+                    Pol::mma(S[j][vr], cur.kd[j][ks], b);
                 }
+                Pol::store4(SL, (size_t)(16 * vr + m) * Sh::SST + c, psS, S[j][vr][0],
+                            S[j][vr][1], S[j][vr][2], S[j][vr][3]);
             }
         }
-        __syncthreads();   // every wave is done reading SL and EL of this chunk
-#pragma unroll
-        for (int t = 0; t < MAXT; ++t) {
-            const int s = wave + 4 * t;
-            if (s < NST) {
-                const int vr = s / NCT, ct = s % NCT;
-                const int c = 16 * ct + m;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Pol::put(SL, (size_t)(16 * vr + 4 * grp + r) * Sh::SST + c, psS, S[t][r]);
-            }
+    };
+
+    // Chunks go in pairs (operand sets A and B alternate); every prefetch is unconditional
+    // (index clamped to the last chunk) so that the loop has no branches around loads.
+    const int last = c_end - 1;
+    if (erole) {
+        EOps<Pol, DK, DV, BV> A, B;
+        floatx4 accO[NVT];
+        if (c_beg < c_end) { load_e_ops(A, ws, c_beg, h, H, v0, tw, m, grp); issue_fence(); }
+        __syncthreads();                                  // S copy initialised
+        int cidx = c_beg;
+        for (; cidx + 1 < c_end; cidx += 2) {
+            load_e_ops(B, ws, cidx + 1, h, H, v0, tw, m, grp);
+            issue_fence();
+            e_phase1(A, accO);
+            __syncthreads();                              // E complete
+            e_phase2(A, accO, cidx);
+            __syncthreads();                              // S updated, E consumed
+            load_e_ops(A, ws, min(cidx + 2, last), h, H, v0, tw, m, grp);
+            issue_fence();
+            e_phase1(B, accO);
+            __syncthreads();
+            e_phase2(B, accO, cidx + 1);
+            __syncthreads();
         }
+        if (cidx < c_end) {
+            e_phase1(A, accO);
+            __syncthreads();
+            e_phase2(A, accO, cidx);
+            __syncthreads();
+        }
+    } else {
+        SOps<Pol, DK, DV, BV> A, B;
+        if (c_beg < c_end && owns) { load_s_ops(A, ws, c_beg, h, H, tw, m, grp); issue_fence(); }
         __syncthreads();
-    }
-    if (ht) {
+        int cidx = c_beg;
+        for (; cidx + 1 < c_end; cidx += 2) {
+            if (owns) { load_s_ops(B, ws, cidx + 1, h, H, tw, m, grp); issue_fence(); }
+            __syncthreads();                              // E complete
+            s_phase2(A);
+            __syncthreads();
+            if (owns) { load_s_ops(A, ws, min(cidx + 2, last), h, H, tw, m, grp); issue_fence(); }
+            __syncthreads();
+            s_phase2(B);
+            __syncthreads();
+        }
+        if (cidx < c_end) {
+            __syncthreads();
+            s_phase2(A);
+            __syncthreads();
+        }
+        if (ht && owns) {
 #pragma unroll
-        for (int t = 0; t < MAXT; ++t) {
-            const int s = wave + 4 * t;
-            if (s < NST) {
-                const int vr = s / NCT, ct = s % NCT;
-                const int c = 16 * ct + m, vv = v0 + 16 * vr + 4 * grp;
-                *reinterpret_cast<float4*>(ht + sbase + (size_t)c * DV + vv) =
-                    make_float4(S[t][0], S[t][1], S[t][2], S[t][3]);
+            for (int j = 0; j < CTW; ++j) {
+#pragma unroll
+                for (int vr = 0; vr < NVT; ++vr) {
+                    const int c = 16 * (tw + 4 * j) + 4 * grp, vv = v0 + 16 * vr + m;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ht[sbase + (size_t)(c + r) * DV + vv] = S[j][vr][r];
+                }
             }
         }
     }
@@ -688,8 +844,9 @@ hipError_t launch_chunk_map(const int32_t* cu, int N, int T, int max_slots, void
 template <typename TI, typename TO, int DK, int DV>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const float* g,
                                    const void* beta, float scale, const float* h0, float* ht,
-                                   void* o, const void* tab, const int32_t* seq_off,
-                                   uint8_t* blocks, int N, int H, int max_slots, hipStream_t s) {
+                                   void* o, const int32_t* cu, int T, const void* tab,
+                                   const int32_t* seq_off, uint8_t* blocks, int N, int H,
+                                   int max_slots, hipStream_t s) {
     hipLaunchKernelGGL((prep_kernel<TI, DK, DV>), dim3(max_slots, H), dim3(256), 0, s,
                        (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
                        (const int4*)tab, blocks, H);
@@ -699,21 +856,21 @@ static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, 
     constexpr int VT = DV / BV;
     const long long chains = (long long)N * H;
     const long long nblk = ((chains + 7) / 8) * 8 * VT;
-    hipLaunchKernelGGL((state_kernel<TI, TO, DK, DV, BV>), dim3((unsigned)nblk), dim3(256), 0, s,
-                       (const int4*)tab, seq_off, (const uint8_t*)blocks, h0, ht, (TO*)o, N, H);
+    hipLaunchKernelGGL((state_kernel<TI, TO, DK, DV, BV>), dim3((unsigned)nblk), dim3(512), 0, s,
+                       cu, T, seq_off, (const uint8_t*)blocks, h0, ht, (TO*)o, N, H);
     return hipGetLastError();
 }
 
 template <typename TI, typename TO>
 static hipError_t dispatch_prefill(int Dk, int Dv, const void* q, const void* k, const void* v,
                                    const float* g, const void* beta, float scale,
-                                   const float* h0, float* ht, void* o, const void* tab,
-                                   const int32_t* seq_off, uint8_t* blocks, int N, int H,
-                                   int max_slots, hipStream_t s) {
+                                   const float* h0, float* ht, void* o, const int32_t* cu, int T,
+                                   const void* tab, const int32_t* seq_off, uint8_t* blocks,
+                                   int N, int H, int max_slots, hipStream_t s) {
 #define KDA_PF(DKV, DVV)                                                                    \
     if (Dk == DKV && Dv == DVV)                                                             \
-        return launch_prefill_t<TI, TO, DKV, DVV>(q, k, v, g, beta, scale, h0, ht, o, tab,  \
-                                                  seq_off, blocks, N, H, max_slots, s);
+        return launch_prefill_t<TI, TO, DKV, DVV>(q, k, v, g, beta, scale, h0, ht, o, cu, T,\
+                                                  tab, seq_off, blocks, N, H, max_slots, s);
     KDA_PF(16, 16) KDA_PF(16, 32) KDA_PF(16, 64) KDA_PF(16, 128)
     KDA_PF(32, 16) KDA_PF(32, 32) KDA_PF(32, 64) KDA_PF(32, 128)
     KDA_PF(64, 16) KDA_PF(64, 32) KDA_PF(64, 64) KDA_PF(64, 128)
@@ -724,20 +881,20 @@ static hipError_t dispatch_prefill(int Dk, int Dv, const void* q, const void* k,
 
 hipError_t launch_prefill(bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
                           const void* k, const void* v, const float* g, const void* beta,
-                          float scale, const float* h0, float* ht, void* o, const void* tab,
-                          const int32_t* seq_off, uint8_t* blocks, int N, int H, int max_slots,
-                          hipStream_t s) {
+                          float scale, const float* h0, float* ht, void* o, const int32_t* cu,
+                          int T, const void* tab, const int32_t* seq_off, uint8_t* blocks, int N,
+                          int H, int max_slots, hipStream_t s) {
     if (bf16_in) {
         if (bf16_out)
-            return dispatch_prefill<bf16, bf16>(Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, tab,
-                                                seq_off, blocks, N, H, max_slots, s);
-        return dispatch_prefill<bf16, float>(Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, tab,
-                                             seq_off, blocks, N, H, max_slots, s);
+            return dispatch_prefill<bf16, bf16>(Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T,
+                                                tab, seq_off, blocks, N, H, max_slots, s);
+        return dispatch_prefill<bf16, float>(Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T,
+                                             tab, seq_off, blocks, N, H, max_slots, s);
     }
     if (bf16_out)
-        return dispatch_prefill<float, bf16>(Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, tab,
-                                             seq_off, blocks, N, H, max_slots, s);
-    return dispatch_prefill<float, float>(Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, tab,
+        return dispatch_prefill<float, bf16>(Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T,
+                                             tab, seq_off, blocks, N, H, max_slots, s);
+    return dispatch_prefill<float, float>(Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T, tab,
                                           seq_off, blocks, N, H, max_slots, s);
 }
 
