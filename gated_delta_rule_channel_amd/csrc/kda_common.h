@@ -29,6 +29,8 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx32 __attribute__((ext_vector_type(32)));
+typedef unsigned u32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kChunk = 64;       // tokens per chunk
 constexpr int kBlock = 16;       // tokens per sub-block (MFMA tile edge)
@@ -154,6 +156,29 @@ struct PolF32 {
     __device__ static __forceinline__ float4 load4f(const Store* base, size_t i, size_t /*ps*/) {
         return *reinterpret_cast<const float4*>(base + i);
     }
+    // ---- fragment tiles in the workspace (two 1 KB parts, lane-contiguous 16 B each) ----
+    // part 0 holds elements 0..3 of every lane, part 1 elements 4..7
+    __device__ static __forceinline__ void tile_store(void* t, int lane, const Frag& f) {
+        float4* p = reinterpret_cast<float4*>(t);
+        p[lane] = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
+        p[64 + lane] = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
+    }
+    __device__ static __forceinline__ void tile_load(Frag& f, const void* t, int lane) {
+        const float4* p = reinterpret_cast<const float4*>(t);
+        const float4 a = p[lane], b = p[64 + lane];
+        f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+        f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    }
+    // elements 4 half .. 4 half + 3 of a lane's fragment
+    __device__ static __forceinline__ void tile_store_quad(void* t, int lane, int half, float a,
+                                                           float b, float c, float d) {
+        reinterpret_cast<float4*>(t)[64 * half + lane] = make_float4(a, b, c, d);
+    }
+    // quad tiles (1 KB): four elements per lane, 16 B
+    __device__ static __forceinline__ void quad_store(void* t, int lane, float a, float b, float c,
+                                                      float d) {
+        reinterpret_cast<float4*>(t)[lane] = make_float4(a, b, c, d);
+    }
     // 4 stored elements kept raw until use (prefetch buffers)
     struct Raw4 { float4 v; };
     __device__ static __forceinline__ void load4raw(Raw4& r, const Store* base, size_t i,
@@ -161,6 +186,17 @@ struct PolF32 {
         r.v = *reinterpret_cast<const float4*>(base + i);
     }
     __device__ static __forceinline__ float4 raw4f(const Raw4& r) { return r.v; }
+    __device__ static __forceinline__ void quad_load(Raw4& r, const void* t, int lane) {
+        r.v = reinterpret_cast<const float4*>(t)[lane];
+    }
+    // product with b exact in the leading part (same as mma16 in fp32)
+    __device__ static __forceinline__ void mma16_exact(floatx4& acc, const Frag4& a, const Frag4& b) {
+        mma16(acc, a, b);
+    }
+    // x times an exact 0/1 matrix e (an exact copy in fp32)
+    __device__ static __forceinline__ void mma_copy(floatx4& acc, const Frag& x, const Frag& e) {
+        mma(acc, x, e);
+    }
 };
 
 struct PolSplit {
@@ -239,6 +275,43 @@ struct PolSplit {
         return make_float4((float)h[0] + (float)l[0], (float)h[1] + (float)l[1],
                            (float)h[2] + (float)l[2], (float)h[3] + (float)l[3]);
     }
+    // ---- fragment tiles in the workspace (two 1 KB parts, lane-contiguous 16 B each) ----
+    // part 0 holds the hi parts of every lane, part 1 the lo parts
+    __device__ static __forceinline__ void tile_store(void* t, int lane, const Frag& f) {
+        bf16x8* p = reinterpret_cast<bf16x8*>(t);
+        p[lane] = f.hi;
+        p[64 + lane] = f.lo;
+    }
+    __device__ static __forceinline__ void tile_load(Frag& f, const void* t, int lane) {
+        const bf16x8* p = reinterpret_cast<const bf16x8*>(t);
+        f.hi = p[lane];
+        f.lo = p[64 + lane];
+    }
+    // elements 4 half .. 4 half + 3 of a lane's fragment
+    __device__ static __forceinline__ void tile_store_quad(void* t, int lane, int half, float a,
+                                                           float b, float c, float d) {
+        bf16x4 h, l;
+        split4(h, l, a, b, c, d);
+        bf16x4* p = reinterpret_cast<bf16x4*>(t);
+        p[2 * lane + half] = h;
+        p[128 + 2 * lane + half] = l;
+    }
+    // quad tiles (1 KB): four elements per lane as hi (8 B) then lo (8 B)
+    __device__ static __forceinline__ void quad_store(void* t, int lane, float a, float b, float c,
+                                                      float d) {
+        bf16x4 h, l;
+        split4(h, l, a, b, c, d);
+        bf16x8 x;
+        x[0] = h[0]; x[1] = h[1]; x[2] = h[2]; x[3] = h[3];
+        x[4] = l[0]; x[5] = l[1]; x[6] = l[2]; x[7] = l[3];
+        reinterpret_cast<bf16x8*>(t)[lane] = x;
+    }
+    __device__ static __forceinline__ void split4(bf16x4& h, bf16x4& l, float a, float b, float c,
+                                                  float d) {
+        h[0] = (bf16)a; h[1] = (bf16)b; h[2] = (bf16)c; h[3] = (bf16)d;
+        l[0] = (bf16)(a - (float)h[0]); l[1] = (bf16)(b - (float)h[1]);
+        l[2] = (bf16)(c - (float)h[2]); l[3] = (bf16)(d - (float)h[3]);
+    }
     struct Raw4 { bf16x4 h, l; };
     __device__ static __forceinline__ void load4raw(Raw4& r, const Store* base, size_t i,
                                                     size_t ps) {
@@ -249,7 +322,33 @@ struct PolSplit {
         return make_float4((float)r.h[0] + (float)r.l[0], (float)r.h[1] + (float)r.l[1],
                            (float)r.h[2] + (float)r.l[2], (float)r.h[3] + (float)r.l[3]);
     }
+    __device__ static __forceinline__ void quad_load(Raw4& r, const void* t, int lane) {
+        const bf16x8 x = reinterpret_cast<const bf16x8*>(t)[lane];
+        r.h = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+        r.l = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+    }
+    // product with b exact in bfloat16 (b.lo == 0): two MFMAs
+    __device__ static __forceinline__ void mma16_exact(floatx4& acc, const Frag4& a, const Frag4& b) {
+        typedef short short4v __attribute__((ext_vector_type(4)));
+        const short4v ah = __builtin_bit_cast(short4v, a.hi), al = __builtin_bit_cast(short4v, a.lo);
+        const short4v bh = __builtin_bit_cast(short4v, b.hi);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
+    }
+    // x (exact in bfloat16, x.lo == 0) times an exact 0/1 matrix e: one MFMA
+    __device__ static __forceinline__ void mma_copy(floatx4& acc, const Frag& x, const Frag& e) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.hi, e.hi, acc, 0, 0, 0);
+    }
 };
+
+// fp32 16 x 16 x 16 product: lane (m, grp) holds a[r] = A[m][4 grp + r] and
+// b[r] = B[4 grp + r][m]; acc gets the C layout (rows 4 grp + r, column m).
+__device__ __forceinline__ void mma16_f32(floatx4& acc, const float4& a, const float4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+}
 
 // ---- cross-lane helpers (a DPP row = 16 consecutive lanes = one value of grp) ------------
 // inclusive prefix sum over the 16 lanes of each row

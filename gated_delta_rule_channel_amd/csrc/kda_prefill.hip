@@ -47,25 +47,48 @@
 namespace kda {
 
 // ------------------------------------------------------------------------------------------
-// workspace layout (one block per (chunk slot, head); 4 bytes per operand element in both
-// operand policies: fp32, or bf16 hi and lo planes)
+// workspace layout
 // ------------------------------------------------------------------------------------------
+// One block per (chunk slot, head). Every operand of the state pass is stored in the
+// register layout of the MFMA fragment that consumes it, so that one load instruction of a
+// wave reads 1 KB of consecutive bytes (16 B per lane):
+//  * fragment tile (2 KB): 8 elements per lane in two 1 KB parts (PolSplit: the hi parts,
+//    then the lo parts; PolF32: elements 0..3, then 4..7);
+//  * quad tile (1 KB): 4 elements per lane, 16 B (PolSplit: hi then lo; PolF32: 4 floats).
+// With lane l = m + 16 grp:
+//  W, Qd  fragment tiles [token tile tw][channel step kap]: row 16 tw + m, channels
+//         32 kap + 8 grp + e (zero past Dk);
+//  Kd^T   fragment tiles [channel tile ct][token half ks]: channel 16 ct + m, tokens
+//         32 ks + 8 grp + e;
+//  U      quad tiles [value tile vt][token tile tw]: tokens 16 tw + 4 grp + r, value 16 vt + m;
+//  A_qk   fragment tiles [token tile tw][column half s]: row 16 tw + m, columns 32 s + 8 grp + e;
+//  exp(G_end) float [Dk].
 __host__ __device__ constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+__host__ __device__ constexpr size_t ws_block_bytes(int DK, int DV) {
+    return round_up((size_t)2 * 4 * (DK >= 32 ? DK / 32 : 1) * 2048 + (size_t)(DK / 16) * 2 * 2048 +
+                        (size_t)(DV / 16) * 4 * 1024 + 8 * 2048 + (size_t)DK * 4,
+                    256);
+}
 
 template <int DK, int DV>
 struct WsLayout {
-    static constexpr size_t W = 0;                        // [64][DK]   W
-    static constexpr size_t QD = W + 64 * DK * 4;         // [64][DK]   scale q exp(G)
-    static constexpr size_t KDT = QD + 64 * DK * 4;       // [DK][64]   (k exp(G_end - G))^T
-    static constexpr size_t U = KDT + DK * 64 * 4;        // [DV][64]   U^T
-    static constexpr size_t AQ = U + 64 * DV * 4;         // [64][64]   A_qk
-    static constexpr size_t GEND = AQ + 64 * 64 * 4;      // float [DK] exp(G_end)
+    static constexpr int KS = DK >= 32 ? DK / 32 : 1;   // 32-channel steps (padded)
+    static constexpr int NCT = DK / 16;                  // 16-channel tiles
+    static constexpr int NVT = DV / 16;                  // 16-value tiles
+    static constexpr size_t FT = 2048;                   // fragment tile
+    static constexpr size_t QT = 1024;                   // quad tile
+    static constexpr size_t W = 0;
+    static constexpr size_t QD = W + 4 * KS * FT;
+    static constexpr size_t KDT = QD + 4 * KS * FT;
+    static constexpr size_t U = KDT + NCT * 2 * FT;
+    static constexpr size_t AQ = U + NVT * 4 * QT;
+    static constexpr size_t GEND = AQ + 8 * FT;
     static constexpr size_t BYTES = round_up(GEND + DK * sizeof(float), 256);
+    static_assert(BYTES == ws_block_bytes(DK, DV), "workspace block size");
 };
 
-size_t prefill_block_bytes(int Dk, int Dv) {
-    return round_up((size_t)4 * (64 * Dk * 3 + 64 * Dv + 64 * 64) + Dk * 4, 256);
-}
+size_t prefill_block_bytes(int Dk, int Dv) { return ws_block_bytes(Dk, Dv); }
 
 // ------------------------------------------------------------------------------------------
 // chunk map
@@ -128,49 +151,69 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
 // 32 w + 8 grp + e. In-chunk prefix sums are DPP scans across the 16 lanes of a row.
 // Each wave forms its slice's partial A_kk / A_qk blocks with MFMAs; the four partials of
 // a block are summed in LDS in a fixed order (the waves visit the row blocks in rotated
-// order, one writer per block per step), so results are bitwise reproducible. Wave w
-// also owns the 32 value columns [32 w, 32 w + 32) for U. Register-level transposes
-// (token-major fragments to channel-major ones) are products with an identity slice.
+// order, one writer per block per step), so results are bitwise reproducible. The row
+// block of a step is wave-uniform, so per-block registers are read with register-indexed
+// moves. T = (I + A_kk)^-1 is formed in fp32: diagonal blocks by forward substitution, the
+// rest column block by column block with fp32 MFMAs. W and U use T' = T diag(beta):
+// W = T' (k exp G), U = T' v. Register-level transposes (token-major fragments to
+// channel-major ones) are products with an identity slice.
 __host__ __device__ constexpr int tri_tile(int I, int J) { return I * (I + 1) / 2 + J; }
 
 // Keeps the compiler from sinking prefetch loads to their first use: loads issued before
 // this point stay before it, so they are in flight while the following code runs.
 __device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
 
-// 16 x 16 x 16 fp32 product on LDS tiles, one wave: lane (r = l/4, cq = l%4) computes
-// out[r][4cq .. 4cq+3] (+)= sign * sum_m X[r][m] Y[m][4cq ..].
-__device__ __forceinline__ void blk16_mm(float* out, int ost, const float* X, int xst,
-                                         const float* Y, int yst, float sign, bool accumulate) {
-    const int lane = threadIdx.x & 63;
-    const int r = lane >> 2, c0 = (lane & 3) * 4;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const float x = X[r * xst + m];
-        const float* y = Y + m * yst + c0;
-        a0 += x * y[0]; a1 += x * y[1]; a2 += x * y[2]; a3 += x * y[3];
+// 32 input elements of a lane (4 token blocks x 8 channels), readable with a wave-uniform
+// block index.
+template <typename T> struct In32;
+template <> struct In32<bf16> {
+    u32x16 w;                                            // two bfloat16 per word
+    __device__ __forceinline__ void load(int I, const bf16* p) {
+        const uint4 x = *reinterpret_cast<const uint4*>(p);
+        w[4 * I] = x.x; w[4 * I + 1] = x.y; w[4 * I + 2] = x.z; w[4 * I + 3] = x.w;
     }
-    float* o = out + r * ost + c0;
-    if (accumulate) {
-        o[0] += sign * a0; o[1] += sign * a1; o[2] += sign * a2; o[3] += sign * a3;
-    } else {
-        o[0] = sign * a0; o[1] = sign * a1; o[2] = sign * a2; o[3] = sign * a3;
+    __device__ __forceinline__ void zero(int I) {
+        w[4 * I] = 0u; w[4 * I + 1] = 0u; w[4 * I + 2] = 0u; w[4 * I + 3] = 0u;
     }
-}
-
-// Channel-major tile of a token-major fragment: with x holding rows (tokens) m and 8 K
-// columns 8 grp + e of a 32-wide slice, returns the C-layout tile D[t][n] = x[t][16 h + n]
-// (lane (n, grp) gets D[4 grp + r][n]), i.e. x times an identity slice (exact).
-template <typename Pol>
-__device__ __forceinline__ floatx4 transpose_half(const typename Pol::Frag& x, int h, int m,
-                                                  int grp) {
-    typename Pol::Frag E;
+    __device__ __forceinline__ void get8(int I, float* o) const {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) E.set(e, (8 * grp + e == 16 * h + m) ? 1.f : 0.f);
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    Pol::mma_exact(acc, x, E);
-    return acc;
-}
+        for (int p = 0; p < 4; ++p) {
+            const unsigned x = w[4 * I + p];
+            o[2 * p] = __uint_as_float(x << 16);
+            o[2 * p + 1] = __uint_as_float(x & 0xffff0000u);
+        }
+    }
+    // the 8 elements of block I as an exact operand fragment
+    __device__ __forceinline__ void frag(int I, PolSplit::Frag& f) const {
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 x;
+        x[0] = w[4 * I]; x[1] = w[4 * I + 1]; x[2] = w[4 * I + 2]; x[3] = w[4 * I + 3];
+        f.hi = __builtin_bit_cast(bf16x8, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f.lo[e] = (bf16)0.f;
+    }
+};
+template <> struct In32<float> {
+    floatx32 v;
+    __device__ __forceinline__ void load(int I, const float* p) {
+        const float4 a = reinterpret_cast<const float4*>(p)[0];
+        const float4 b = reinterpret_cast<const float4*>(p)[1];
+        v[8 * I] = a.x; v[8 * I + 1] = a.y; v[8 * I + 2] = a.z; v[8 * I + 3] = a.w;
+        v[8 * I + 4] = b.x; v[8 * I + 5] = b.y; v[8 * I + 6] = b.z; v[8 * I + 7] = b.w;
+    }
+    __device__ __forceinline__ void zero(int I) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[8 * I + e] = 0.f;
+    }
+    __device__ __forceinline__ void get8(int I, float* o) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = v[8 * I + e];
+    }
+    __device__ __forceinline__ void frag(int I, PolF32::Frag& f) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f.v[e] = v[8 * I + e];
+    }
+};
 
 template <typename Pol>
 __device__ __forceinline__ typename Pol::Frag4 frag4_of(const floatx4& d) {
@@ -188,130 +231,121 @@ __global__ __launch_bounds__(256) void prep_kernel(
     using Pol = typename PolOf<TI>::type;
     using Frag = typename Pol::Frag;
     using Frag4 = typename Pol::Frag4;
-    using St = typename Pol::Store;
     using Ly = WsLayout<DK, DV>;
     constexpr int NSL = DK >= 32 ? DK / 32 : 1;          // channel slices (32 wide, padded)
-    constexpr int DVP = DV >= 32 ? DV : 32;
-    constexpr int NVS = DVP / 32;                         // value slices
+    constexpr int NVS = DV >= 32 ? DV / 32 : 1;          // value slices
     // lower 16x16 blocks, rows padded to 20 floats so that 16 lanes reading 4 floats of
     // 16 different rows hit distinct LDS banks
     __shared__ float sKK[10][16][20];                     // A_kk lower blocks
     __shared__ float sQK[10][16][20];                     // A_qk lower blocks
     __shared__ float sT[10][16][20];                      // T = (I + A_kk)^-1 lower blocks
-    __shared__ float sY[4][16][17];                       // per-wave scratch of the inverse
-    __shared__ float4 sDW[4][4][2][64];                   // per wave: (beta k exp G)^T tiles
+    __shared__ float sBeta[64];
 
     const int slot = blockIdx.x, h = blockIdx.y;
     const int4 ci = tab[slot];
     const int t0 = ci.x, L = ci.y;
     if (L <= 0) return;                                   // uniform per workgroup
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = lane & 15, grp = lane >> 4;
     const size_t rowq = (size_t)H * DK, rowv = (size_t)H * DV;
     uint8_t* blk = ws + ((size_t)slot * H + h) * Ly::BYTES;
-    St* gW = reinterpret_cast<St*>(blk + Ly::W);
-    St* gQd = reinterpret_cast<St*>(blk + Ly::QD);
-    St* gKdT = reinterpret_cast<St*>(blk + Ly::KDT);
-    St* gU = reinterpret_cast<St*>(blk + Ly::U);
-    St* gAq = reinterpret_cast<St*>(blk + Ly::AQ);
     float* gGend = reinterpret_cast<float*>(blk + Ly::GEND);
-    constexpr size_t psW = (size_t)64 * DK, psU = (size_t)64 * DV, psAq = 64 * 64;
 
     const bool cs = wave < NSL;                  // this wave owns a channel slice
     const int c0 = 32 * wave + 8 * grp;          // first of this lane's 8 channels
     const bool cvalid = cs && c0 < DK;
 
-    // ---- loads: g, k, q of the slice for all 64 tokens; beta of the lane's tokens ----
-    float G[4][8];
-    Raw8<TI> kr[4], qr[4];
-    float bt[4];
+    // ---- loads: g, k, q of the slice for all 64 tokens; beta of the chunk to LDS ----
+    floatx32 G;
+    In32<TI> K, Q;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         const int row = 16 * I + m;
-        const bool ok = cvalid && row < L;
-        if (ok) {
+        if (cvalid && row < L) {
             const size_t off = (size_t)(t0 + row) * rowq + (size_t)h * DK + c0;
-            load8f(G[I], g + off);
-            kr[I].load(k + off);
-            qr[I].load(q + off);
+            const float4 g0 = reinterpret_cast<const float4*>(g + off)[0];
+            const float4 g1 = reinterpret_cast<const float4*>(g + off)[1];
+            G[8 * I] = g0.x; G[8 * I + 1] = g0.y; G[8 * I + 2] = g0.z; G[8 * I + 3] = g0.w;
+            G[8 * I + 4] = g1.x; G[8 * I + 5] = g1.y; G[8 * I + 6] = g1.z; G[8 * I + 7] = g1.w;
+            K.load(I, k + off);
+            Q.load(I, q + off);
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) G[I][e] = 0.f;
-            kr[I].zero();
-            qr[I].zero();
+            for (int e = 0; e < 8; ++e) G[8 * I + e] = 0.f;
+            K.zero(I);
+            Q.zero(I);
         }
-        bt[I] = row < L ? to_f(beta[(size_t)(t0 + row) * H + h]) : 0.f;
     }
+    if (tid < 64) sBeta[tid] = tid < L ? to_f(beta[(size_t)(t0 + tid) * H + h]) : 0.f;
     // zero the A accumulators while the loads are in flight
     for (int idx = tid; idx < 10 * 16 * 20; idx += 256) {
         (&sKK[0][0][0])[idx] = 0.f;
         (&sQK[0][0][0])[idx] = 0.f;
     }
 
-    // ---- block-local prefix sums (log2 units) and the chunk total per channel ----
-    float gtot[8];
+    // ---- block-local prefix sums (log2 units); CE = cumulative value at each block end ----
+    floatx32 CE;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) gtot[e] = 0.f;
+    for (int e = 0; e < 8; ++e) {
+        float acc = 0.f;
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            G[I][e] = row_scan16(G[I][e] * kLog2e);
-            gtot[e] += row_bcast<15>(G[I][e]);
+        for (int I = 0; I < 4; ++I) {
+            G[8 * I + e] = row_scan16(G[8 * I + e] * kLog2e);
+            acc += row_bcast<15>(G[8 * I + e]);
+            CE[8 * I + e] = acc;
         }
     }
     if (cvalid && m == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) gGend[c0 + e] = fast_exp2(gtot[e]);
+        for (int e = 0; e < 8; ++e) gGend[c0 + e] = fast_exp2(CE[24 + e]);
     }
-    __syncthreads();                                    // A accumulators zeroed
+    // identity slices: Eid[hh] as a B operand maps K index 16 hh + n to column n
+    Frag Eid[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Eid[hh].set(e, (8 * grp + e == 16 * hh + m) ? 1.f : 0.f);
+    __syncthreads();                                    // A accumulators zeroed, beta in LDS
 
-    // ---- rotated pass over the row blocks: operands, Qd, Kd^T, partial A blocks ----
+    // ---- rotated pass over the row blocks: Qd, Kd^T, partial A blocks ----
 #pragma unroll 1
     for (int st = 0; st < 4; ++st) {
         if (cs) {
-            const int I = (wave + st) & 3;
+            const int I = (wave + st) & 3;                // wave-uniform
+            const int Ip = I > 0 ? I - 1 : 0;
             const int row = 16 * I + m;
-            float bi = 0.f;
+            const float bi = sBeta[row];
+            float Gl[8], kk[8], qq[8], pf[8];
+            K.get8(I, kk);
+            Q.get8(I, qq);
 #pragma unroll
-            for (int J = 0; J < 4; ++J)
-                if (J == I) bi = bt[J];
-            // selects block I's registers (I is wave-dependent) without dynamic indexing
-            auto pick = [&](int e, float& Gv, float& kk, float& qq) {
-#pragma unroll
-                for (int J = 0; J < 4; ++J)
-                    if (J == I) { Gv = G[J][e]; kk = kr[J].get(e); qq = qr[J].get(e); }
-            };
-            // (a) chunk-start / chunk-end references: Qd (to the workspace), Kd^T (to the
-            //     workspace, transposed), Wop^T (to LDS for W)
+            for (int e = 0; e < 8; ++e) {
+                Gl[e] = G[8 * I + e];
+                pf[e] = I > 0 ? CE[8 * Ip + e] : 0.f;     // cumulative value before block I
+            }
+            // (a) chunk-start / chunk-end references: Qd and Kd^T to the workspace
             {
-                Frag Wop, Qd, Kd;
+                Frag Qd, Kd;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    float Gv = 0.f, kk = 0.f, qq = 0.f, pf = 0.f;
-                    pick(e, Gv, kk, qq);
-#pragma unroll
-                    for (int J = 0; J < 3; ++J) {
-                        const float lamJ = row_bcast<15>(G[J][e]);
-                        if (J < I) pf += lamJ;
-                    }
-                    const float Gc = pf + Gv;
-                    const float ec = fast_exp2(Gc), ed = fast_exp2(gtot[e] - Gc);
-                    Wop.set(e, bi * kk * ec);
-                    Qd.set(e, scale * qq * ec);
-                    Kd.set(e, kk * ed);
+                    const float Gc = pf[e] + Gl[e];
+                    const float ec = fast_exp2(Gc), ed = fast_exp2(CE[24 + e] - Gc);
+                    Qd.set(e, scale * qq[e] * ec);
+                    Kd.set(e, kk[e] * ed);
                 }
-                if (cvalid) Pol::store(gQd, (size_t)row * DK + c0, psW, Qd);
+                Pol::tile_store(blk + Ly::QD + (I * Ly::KS + wave) * Ly::FT, lane, Qd);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const floatx4 dk = transpose_half<Pol>(Kd, hh, m, grp);
-                    const int ch = 32 * wave + 16 * hh + m;
-                    if (32 * wave + 16 * hh < DK)
-                        Pol::store4(gKdT, (size_t)ch * 64 + 16 * I + 4 * grp, psW, dk[0], dk[1],
-                                    dk[2], dk[3]);
-                    const floatx4 dw = transpose_half<Pol>(Wop, hh, m, grp);
-                    sDW[wave][I][hh][lane] = make_float4(dw[0], dw[1], dw[2], dw[3]);
+                    if (32 * wave + 16 * hh < DK) {
+                        floatx4 dk = {0.f, 0.f, 0.f, 0.f};
+                        Pol::mma_exact(dk, Kd, Eid[hh]);  // lane (channel n, grp): tokens 4 grp + r
+                        const int ct = 2 * wave + hh, ks = I >> 1;
+                        Pol::tile_store_quad(blk + Ly::KDT + (ct * 2 + ks) * Ly::FT,
+                                             m + 16 * (2 * (I & 1) + (grp >> 1)), grp & 1, dk[0],
+                                             dk[1], dk[2], dk[3]);
+                    }
                 }
             }
             // (b) diagonal block (midpoint reference, or pairwise when out of range)
@@ -321,14 +355,12 @@ __global__ __launch_bounds__(256) void prep_kernel(
                 bool bad = false;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    float Gv = 0.f, kk = 0.f, qq = 0.f;
-                    pick(e, Gv, kk, qq);
-                    const float x = Gv - row_bcast<7>(Gv);
+                    const float x = Gl[e] - row_bcast<7>(Gl[e]);
                     bad |= fabsf(x) > 120.f;
                     const float e1 = fast_exp2(x), e2 = fast_exp2(-x);
-                    KE.set(e, bi * kk * e1);
-                    QE.set(e, scale * qq * e1);
-                    KR.set(e, kk * e2);
+                    KE.set(e, bi * kk[e] * e1);
+                    QE.set(e, scale * qq[e] * e1);
+                    KR.set(e, kk[e] * e2);
                 }
                 if (!__any(bad)) {
                     Pol::mma(akk, KR, KE);
@@ -338,16 +370,14 @@ __global__ __launch_bounds__(256) void prep_kernel(
 #pragma unroll 1
                     for (int jj = 0; jj < 16; ++jj) {
                         float skk = 0.f, sqk = 0.f;
+                        const int src = (lane & 48) | jj;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            float Gv = 0.f, kk = 0.f, qq = 0.f;
-                            pick(e, Gv, kk, qq);
-                            const int src = (lane & 48) | jj;
-                            const float Gj = __shfl(Gv, src);
-                            const float kj = __shfl(kk, src);
-                            const float d = jj <= m ? fast_exp2(Gv - Gj) : 0.f;
-                            skk += kk * kj * d;
-                            sqk += scale * qq * kj * d;
+                            const float Gj = __shfl(Gl[e], src);
+                            const float kj = __shfl(kk[e], src);
+                            const float d = jj <= m ? fast_exp2(Gl[e] - Gj) : 0.f;
+                            skk += kk[e] * kj * d;
+                            sqk += scale * qq[e] * kj * d;
                         }
                         skk += __shfl_xor(skk, 16);
                         skk += __shfl_xor(skk, 32);
@@ -379,26 +409,21 @@ __global__ __launch_bounds__(256) void prep_kernel(
                 Frag KA, QA;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    float Gv = 0.f, kk = 0.f, qq = 0.f;
-                    pick(e, Gv, kk, qq);
-                    const float ea = fast_exp2(Gv);
-                    KA.set(e, bi * kk * ea);
-                    QA.set(e, scale * qq * ea);
+                    const float ea = fast_exp2(Gl[e]);
+                    KA.set(e, bi * kk[e] * ea);
+                    QA.set(e, scale * qq[e] * ea);
                 }
 #pragma unroll 1
                 for (int J = 0; J < I; ++J) {
                     // k of block J decayed to the start of block I
+                    const int Jp = J > 0 ? J - 1 : 0;
+                    float kJ[8];
+                    K.get8(J, kJ);
                     Frag b;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        float GJ = 0.f, kJ = 0.f, xs = 0.f;
-#pragma unroll
-                        for (int J2 = 0; J2 < 3; ++J2) {
-                            const float lamJ2 = row_bcast<15>(G[J2][e]);
-                            if (J2 == J) { GJ = G[J2][e]; kJ = kr[J2].get(e); xs += lamJ2; }
-                            if (J2 > J && J2 < I) xs += lamJ2;
-                        }
-                        b.set(e, kJ * fast_exp2(xs - GJ));
+                        const float ceJ = J > 0 ? CE[8 * Jp + e] : 0.f;
+                        b.set(e, kJ[e] * fast_exp2(pf[e] - ceJ - G[8 * J + e]));
                     }
                     floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
                     Pol::mma(akk, b, KA);
@@ -419,113 +444,136 @@ __global__ __launch_bounds__(256) void prep_kernel(
     // ---- value slice of this wave (for U), loaded now so it lands during the inverse ----
     const int vc0 = 32 * wave + 8 * grp;
     const bool vvalid = wave < NVS && vc0 < DV;
-    float vf[4][8];
+    In32<TI> V;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         const int row = 16 * I + m;
-        if (vvalid && row < L) {
-            load8f(vf[I], v + (size_t)(t0 + row) * rowv + (size_t)h * DV + vc0);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vf[I][e] = 0.f;
-        }
+        if (vvalid && row < L)
+            V.load(I, v + (size_t)(t0 + row) * rowv + (size_t)h * DV + vc0);
+        else
+            V.zero(I);
     }
-    // A_qk to the workspace (upper blocks zero)
-    for (int idx = tid; idx < 64 * 16; idx += 256) {
-        const int row = idx >> 4, cg = idx & 15;
-        const int I = row >> 4, il = row & 15, J = cg >> 2, jl = (cg & 3) * 4;
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (J <= I) x = *reinterpret_cast<const float4*>(&sQK[tri_tile(I, J)][il][jl]);
-        Pol::store4(gAq, (size_t)row * 64 + cg * 4, psAq, x.x, x.y, x.z, x.w);
+    // A_qk fragment tiles of token tile tw = wave (upper blocks zero)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int J = 2 * s + (grp >> 1), jl = 8 * (grp & 1);
+        Frag f;
+        if (J <= wave) {
+            const float4 x0 = *reinterpret_cast<const float4*>(&sQK[tri_tile(wave, J)][m][jl]);
+            const float4 x1 = *reinterpret_cast<const float4*>(&sQK[tri_tile(wave, J)][m][jl + 4]);
+            f.set(0, x0.x); f.set(1, x0.y); f.set(2, x0.z); f.set(3, x0.w);
+            f.set(4, x1.x); f.set(5, x1.y); f.set(6, x1.z); f.set(7, x1.w);
+        } else {
+            f.zero();
+        }
+        Pol::tile_store(blk + Ly::AQ + (wave * 2 + s) * Ly::FT, lane, f);
     }
 
-    // ---- T = (I + A_kk)^-1: diagonal blocks by forward substitution, then by levels ----
+    // ---- T = (I + A_kk)^-1: diagonal blocks by forward substitution (fp32) ----
+    if (lane < 16) {
+        const int I = wave, n = lane;
+        float x[16];
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+            float s = 0.f;
+#pragma unroll
+            for (int mm = 0; mm < ii; ++mm) s += sKK[tri_tile(I, I)][ii][mm] * x[mm];
+            x[ii] = (ii == n) ? 1.f : (ii > n ? -s : 0.f);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) sT[tri_tile(I, I)][ii][n] = x[ii];
+    }
+    __syncthreads();
+    // off-diagonal blocks, column block J = wave: T_IJ = -T_II sum_{M=J}^{I-1} A_IM T_MJ
     {
-        const int I = wave;
-        if (lane < 16) {
-            const int n = lane;
-            float x[16];
-#pragma unroll
-            for (int ii = 0; ii < 16; ++ii) {
-                float s = 0.f;
-#pragma unroll
-                for (int mm = 0; mm < ii; ++mm) s += sKK[tri_tile(I, I)][ii][mm] * x[mm];
-                x[ii] = (ii == n) ? 1.f : (ii > n ? -s : 0.f);
+        const int J = wave;
+#pragma unroll 1
+        for (int I = J + 1; I < 4; ++I) {
+            floatx4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int M = J; M < I; ++M) {
+                const float4 a = *reinterpret_cast<const float4*>(&sKK[tri_tile(I, M)][m][4 * grp]);
+                const float* tb = &sT[tri_tile(M, J)][4 * grp][m];
+                mma16_f32(Y, a, make_float4(tb[0], tb[20], tb[40], tb[60]));
             }
-#pragma unroll
-            for (int ii = 0; ii < 16; ++ii) sT[tri_tile(I, I)][ii][n] = x[ii];
+            // (T_II Y)^T = Y^T T_II^T: A = Y in its C layout, B = T_II read by rows
+            const float4 d = *reinterpret_cast<const float4*>(&sT[tri_tile(I, I)][m][4 * grp]);
+            floatx4 R = {0.f, 0.f, 0.f, 0.f};
+            mma16_f32(R, make_float4(Y[0], Y[1], Y[2], Y[3]), d);
+            *reinterpret_cast<float4*>(&sT[tri_tile(I, J)][m][4 * grp]) =
+                make_float4(-R[0], -R[1], -R[2], -R[3]);
         }
     }
     __syncthreads();
-    for (int d = 1; d <= 3; ++d) {
-        const int I = wave;
-        const bool act = I >= d;
-        const int J = I - d;
-        if (act) {
-            for (int M = J; M < I; ++M)
-                blk16_mm(&sY[I][0][0], 17, &sKK[tri_tile(I, M)][0][0], 20,
-                         &sT[tri_tile(M, J)][0][0], 20, 1.f, M != J);
+
+    // ---- T' = T diag(beta) as operand fragments: lane (m, grp) holds T'[16I + m][16J + 4grp + r]
+    Frag4 Tp[10];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+#pragma unroll
+        for (int J = 0; J <= I; ++J) {
+            const float4 t = *reinterpret_cast<const float4*>(&sT[tri_tile(I, J)][m][4 * grp]);
+            const float4 bb = *reinterpret_cast<const float4*>(&sBeta[16 * J + 4 * grp]);
+            Frag4& f = Tp[tri_tile(I, J)];
+            f.set(0, t.x * bb.x); f.set(1, t.y * bb.y); f.set(2, t.z * bb.z); f.set(3, t.w * bb.w);
         }
-        __syncthreads();
-        if (act)
-            blk16_mm(&sT[tri_tile(I, J)][0][0], 20, &sT[tri_tile(I, I)][0][0], 20,
-                     &sY[I][0][0], 17, -1.f, false);
-        __syncthreads();
     }
 
-    // ---- W = T (beta k exp G) and U = T (beta v), transposed products over 16-token blocks ----
-    // W^T(ct, I) = sum_{J <= I} Wop_J^T (channels x tokens j) T_IJ^T (tokens j x tokens i);
-    // lane (n = token i, grp) of the result holds W[16 I + n][channel 4 grp + r].
+    // ---- W = T' (k exp G): W^T(channel half, I) = sum_{J <= I} (k exp G)_J^T T'_IJ^T; the
+    //      result lane (m = token, grp) holds W[16 I + m][4 channels] ----
     if (cs) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
+            floatx4 accW[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) accW[I] = floatx4{0.f, 0.f, 0.f, 0.f};
             if (32 * wave + 16 * hh < DK) {
 #pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int J = 0; J < 4; ++J) {
+                    float kJ[8];
+                    K.get8(J, kJ);
+                    Frag kg;
 #pragma unroll
-                    for (int J = 0; J <= I; ++J) {
-                        const float4 w4 = sDW[wave][J][hh][lane];
-                        Frag4 aw;
-                        aw.set(0, w4.x); aw.set(1, w4.y); aw.set(2, w4.z); aw.set(3, w4.w);
-                        Frag4 tb;
-                        const float4 t4 = *reinterpret_cast<const float4*>(&sT[tri_tile(I, J)][m][4 * grp]);
-                        tb.set(0, t4.x); tb.set(1, t4.y); tb.set(2, t4.z); tb.set(3, t4.w);
-                        Pol::mma16(acc, aw, tb);
+                    for (int e = 0; e < 8; ++e) {
+                        const float ceJ = J > 0 ? CE[8 * (J - 1) + e] : 0.f;
+                        kg.set(e, kJ[e] * fast_exp2(ceJ + G[8 * J + e]));
                     }
-                    Pol::store4(gW, (size_t)(16 * I + m) * DK + 32 * wave + 16 * hh + 4 * grp, psW,
-                                acc[0], acc[1], acc[2], acc[3]);
+                    floatx4 t = {0.f, 0.f, 0.f, 0.f};
+                    Pol::mma_exact(t, kg, Eid[hh]);       // lane (channel n, grp): tokens 4 grp + r
+                    const Frag4 a = frag4_of<Pol>(t);
+#pragma unroll
+                    for (int I = J; I < 4; ++I) Pol::mma16(accW[I], a, Tp[tri_tile(I, J)]);
                 }
             }
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+                Pol::tile_store_quad(blk + Ly::W + (I * Ly::KS + wave) * Ly::FT,
+                                     m + 16 * (2 * hh + (grp >> 1)), grp & 1, accW[I][0],
+                                     accW[I][1], accW[I][2], accW[I][3]);
         }
     }
+    // ---- U = T' v: lane (m = value, grp) of tile (value tile, I) holds U[16 I + 4 grp + r][value] ----
     if (wave < NVS) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             if (32 * wave + 16 * hh < DV) {
-                Frag4 av[4];
+                floatx4 accU[4];
+#pragma unroll
+                for (int I = 0; I < 4; ++I) accU[I] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int J = 0; J < 4; ++J) {
                     Frag vb;
+                    V.frag(J, vb);
+                    floatx4 t = {0.f, 0.f, 0.f, 0.f};
+                    Pol::mma_copy(t, vb, Eid[hh]);        // lane (value n, grp): tokens 4 grp + r
+                    const Frag4 b = frag4_of<Pol>(t);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) vb.set(e, bt[J] * vf[J][e]);
-                    av[J] = frag4_of<Pol>(transpose_half<Pol>(vb, hh, m, grp));
+                    for (int I = J; I < 4; ++I) Pol::mma16_exact(accU[I], Tp[tri_tile(I, J)], b);
                 }
-                // U(I, ct) = sum_{J <= I} T_IJ (tokens i x tokens j) (beta v)_J (tokens j x
-                // values); lane (n = value, grp) of the result holds U[16 I + 4 grp + r][n]
 #pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int J = 0; J <= I; ++J) {
-                        Frag4 ta;
-                        const float4 t4 = *reinterpret_cast<const float4*>(&sT[tri_tile(I, J)][m][4 * grp]);
-                        ta.set(0, t4.x); ta.set(1, t4.y); ta.set(2, t4.z); ta.set(3, t4.w);
-                        Pol::mma16(acc, ta, av[J]);
-                    }
-                    Pol::store4(gU, (size_t)(32 * wave + 16 * hh + m) * 64 + 16 * I + 4 * grp, psU,
-                                acc[0], acc[1], acc[2], acc[3]);
-                }
+                for (int I = 0; I < 4; ++I)
+                    Pol::quad_store(blk + Ly::U + ((2 * wave + hh) * 4 + I) * Ly::QT, lane,
+                                    accU[I][0], accU[I][1], accU[I][2], accU[I][3]);
             }
         }
     }
@@ -576,54 +624,39 @@ struct SOps {                          // S-role operands of one chunk
 template <typename Pol, int DK, int DV, int BV>
 __device__ __forceinline__ void load_e_ops(EOps<Pol, DK, DV, BV>& c,
                                            const uint8_t* __restrict__ ws, int cidx, int h, int H,
-                                           int v0, int tw, int m, int grp) {
+                                           int v0, int tw, int lane) {
     using Sh = StateShape<DK, DV, BV>;
     using Ly = WsLayout<DK, DV>;
-    using St = typename Pol::Store;
-    constexpr size_t psW = (size_t)64 * DK, psU = (size_t)64 * DV, psAq = 64 * 64;
     const uint8_t* blk = ws + ((size_t)cidx * H + h) * Ly::BYTES;
-    const St* gW = reinterpret_cast<const St*>(blk + Ly::W);
-    const St* gQd = reinterpret_cast<const St*>(blk + Ly::QD);
-    const St* gU = reinterpret_cast<const St*>(blk + Ly::U);
-    const St* gAq = reinterpret_cast<const St*>(blk + Ly::AQ);
-    const int tok = 16 * tw + m;
 #pragma unroll
     for (int kap = 0; kap < Sh::KS; ++kap) {
-        const int c0 = 32 * kap + 8 * grp;
-        if (c0 < DK) {
-            Pol::load(c.w[kap], gW, (size_t)tok * DK + c0, psW);
-            Pol::load(c.qd[kap], gQd, (size_t)tok * DK + c0, psW);
-        } else {
-            c.w[kap].zero();
-            c.qd[kap].zero();
-        }
+        Pol::tile_load(c.w[kap], blk + Ly::W + (tw * Ly::KS + kap) * Ly::FT, lane);
+        Pol::tile_load(c.qd[kap], blk + Ly::QD + (tw * Ly::KS + kap) * Ly::FT, lane);
     }
 #pragma unroll
     for (int vr = 0; vr < Sh::NVT; ++vr)
-        Pol::load4raw(c.u[vr], gU, (size_t)(v0 + 16 * vr + m) * 64 + 16 * tw + 4 * grp, psU);
+        Pol::quad_load(c.u[vr], blk + Ly::U + ((v0 / 16 + vr) * 4 + tw) * Ly::QT, lane);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        if (s == 0 || tw >= 2) Pol::load(c.aq[s], gAq, (size_t)tok * 64 + 32 * s + 8 * grp, psAq);
+        if (s == 0 || tw >= 2) Pol::tile_load(c.aq[s], blk + Ly::AQ + (tw * 2 + s) * Ly::FT, lane);
     }
 }
 
 template <typename Pol, int DK, int DV, int BV>
 __device__ __forceinline__ void load_s_ops(SOps<Pol, DK, DV, BV>& c, const uint8_t* __restrict__ ws,
-                                           int cidx, int h, int H, int sw, int m, int grp) {
+                                           int cidx, int h, int H, int sw, int lane) {
     using Sh = StateShape<DK, DV, BV>;
     using Ly = WsLayout<DK, DV>;
-    using St = typename Pol::Store;
-    constexpr size_t psW = (size_t)64 * DK;
     const uint8_t* blk = ws + ((size_t)cidx * H + h) * Ly::BYTES;
-    const St* gKdT = reinterpret_cast<const St*>(blk + Ly::KDT);
     const float* gGend = reinterpret_cast<const float*>(blk + Ly::GEND);
+    const int grp = lane >> 4;
 #pragma unroll
     for (int j = 0; j < Sh::CTW; ++j) {
         const int ct = sw + 4 * j;
         c.gd[j] = *reinterpret_cast<const float4*>(gGend + 16 * ct + 4 * grp);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            Pol::load(c.kd[j][ks], gKdT, (size_t)(16 * ct + m) * 64 + 32 * ks + 8 * grp, psW);
+            Pol::tile_load(c.kd[j][ks], blk + Ly::KDT + (ct * 2 + ks) * Ly::FT, lane);
     }
 }
 
@@ -692,7 +725,9 @@ __global__ __launch_bounds__(512) void state_kernel(
     const size_t rowo = (size_t)H * DV;
 
     // E role: E = U - W S into LDS; O = Qd S + A_qk E to memory. Tiles (token tile tw,
-    // value tile vr); lane (n = value, grp) holds rows (tokens) 16 tw + 4 grp + r.
+    // value tile vr): for E, lane (n = value, grp) holds tokens 16 tw + 4 grp + r; O is
+    // formed transposed, so lane (n = token, grp) holds values 16 vr + 4 grp + r (16-byte
+    // output stores).
     auto e_phase1 = [&](const EOps<Pol, DK, DV, BV>& cur, floatx4 (&accO)[NVT]) {
         floatx4 accE[NVT];
 #pragma unroll
@@ -708,7 +743,7 @@ __global__ __launch_bounds__(512) void state_kernel(
                 Frag b;
                 Pol::load(b, SL, (size_t)(16 * vr + m) * Sh::SST + c0, psS);
                 Pol::mma(accE[vr], cur.w[kap], b);
-                Pol::mma(accO[vr], cur.qd[kap], b);
+                Pol::mma(accO[vr], b, cur.qd[kap]);       // O^T: rows = values
             }
         }
 #pragma unroll
@@ -730,18 +765,16 @@ __global__ __launch_bounds__(512) void state_kernel(
                 for (int vr = 0; vr < NVT; ++vr) {
                     Frag b;
                     Pol::load(b, EL, (size_t)(16 * vr + m) * Sh::EST + 32 * s2 + 8 * grp, psE);
-                    Pol::mma(accO[vr], cur.aq[s2], b);
+                    Pol::mma(accO[vr], b, cur.aq[s2]);
                 }
             }
         }
+        const int tok = 16 * tw + m;
+        if (tok < len) {
+            TO* orow = o + (size_t)(t0 + tok) * rowo + (size_t)h * DV + v0 + 4 * grp;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int tok = 16 * tw + 4 * grp + r;
-            if (tok < len) {
-                TO* orow = o + (size_t)(t0 + tok) * rowo + (size_t)h * DV + v0 + m;
-#pragma unroll
-                for (int vr = 0; vr < NVT; ++vr) orow[16 * vr] = from_f<TO>(accO[vr][r]);
-            }
+            for (int vr = 0; vr < NVT; ++vr)
+                store4(orow + 16 * vr, accO[vr][0], accO[vr][1], accO[vr][2], accO[vr][3]);
         }
     };
     // S role: S = Diag(exp G_end) S + Kd^T E, then the operand copy of S
@@ -774,17 +807,17 @@ __global__ __launch_bounds__(512) void state_kernel(
     if (erole) {
         EOps<Pol, DK, DV, BV> A, B;
         floatx4 accO[NVT];
-        if (c_beg < c_end) { load_e_ops(A, ws, c_beg, h, H, v0, tw, m, grp); issue_fence(); }
+        if (c_beg < c_end) { load_e_ops(A, ws, c_beg, h, H, v0, tw, lane); issue_fence(); }
         __syncthreads();                                  // S copy initialised
         int cidx = c_beg;
         for (; cidx + 1 < c_end; cidx += 2) {
-            load_e_ops(B, ws, cidx + 1, h, H, v0, tw, m, grp);
+            load_e_ops(B, ws, cidx + 1, h, H, v0, tw, lane);
             issue_fence();
             e_phase1(A, accO);
             __syncthreads();                              // E complete
             e_phase2(A, accO, cidx);
             __syncthreads();                              // S updated, E consumed
-            load_e_ops(A, ws, min(cidx + 2, last), h, H, v0, tw, m, grp);
+            load_e_ops(A, ws, min(cidx + 2, last), h, H, v0, tw, lane);
             issue_fence();
             e_phase1(B, accO);
             __syncthreads();
@@ -799,15 +832,15 @@ __global__ __launch_bounds__(512) void state_kernel(
         }
     } else {
         SOps<Pol, DK, DV, BV> A, B;
-        if (c_beg < c_end && owns) { load_s_ops(A, ws, c_beg, h, H, tw, m, grp); issue_fence(); }
+        if (c_beg < c_end && owns) { load_s_ops(A, ws, c_beg, h, H, tw, lane); issue_fence(); }
         __syncthreads();
         int cidx = c_beg;
         for (; cidx + 1 < c_end; cidx += 2) {
-            if (owns) { load_s_ops(B, ws, cidx + 1, h, H, tw, m, grp); issue_fence(); }
+            if (owns) { load_s_ops(B, ws, cidx + 1, h, H, tw, lane); issue_fence(); }
             __syncthreads();                              // E complete
             s_phase2(A);
             __syncthreads();
-            if (owns) { load_s_ops(A, ws, min(cidx + 2, last), h, H, tw, m, grp); issue_fence(); }
+            if (owns) { load_s_ops(A, ws, min(cidx + 2, last), h, H, tw, lane); issue_fence(); }
             __syncthreads();
             s_phase2(B);
             __syncthreads();
