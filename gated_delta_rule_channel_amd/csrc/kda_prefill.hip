@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
     for (int st = 0; st < 4; ++st) {
         if (cs) {
             const int I = (wave + st) & 3;                // wave-uniform
-            const int Ip = I > 0 ? I - 1 : 0;
+            const int Ip = __builtin_amdgcn_readfirstlane(I > 0 ? I - 1 : 0);
             const int row = 16 * I + m;
             const float bi = sBeta[row];
             float Gl[8], kk[8], qq[8], pf[8];
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
 #pragma unroll 1
                 for (int J = 0; J < I; ++J) {
                     // k of block J decayed to the start of block I
-                    const int Jp = J > 0 ? J - 1 : 0;
+                    const int Jp = __builtin_amdgcn_readfirstlane(J > 0 ? J - 1 : 0);
                     float kJ[8];
                     K.get8(J, kJ);
                     Frag b;
