@@ -2,19 +2,27 @@
 """Benchmark of the KDA forward hot path on one MI355X.
 
 One step = one chunked prefill over the main prefill workload (B1 T8192 H64
-d128, bf16 inputs, fp32 state, fp32 output) plus one decode step over the
-decode workload (256 requests x 64 heads, 128x128 fp32 states updated in
-place). Inputs are synthetic (seeded generators) and resident in HBM before
-timing starts. Prints one JSON line.
+d128, bf16 q/k/v/beta, fp32 g and state, fp32 output) plus one decode step
+over the decode workload (256 requests x 64 heads, 128x128 fp32 states
+updated in place). Inputs are synthetic (seeded generators) and resident in
+HBM before timing starts. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py --copy-calibration          # 1 GiB device copy (counter calibration)
+  python bench.py --traffic-summary F W CF CW # rocprofv3 --pmc CSVs -> profiles/ json
+
+The traffic summary takes four rocprofv3 counter-collection CSV files: FETCH_SIZE
+and WRITE_SIZE over a bench run, then over a --copy-calibration run; each counter
+is scaled by the factor that makes it read 1 GiB for the copy.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
-import platform
 import sys
 import time
 
@@ -24,6 +32,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 METRIC = "KDA prefill tokens/s (H=64,d=128,bf16) + decode-step state GB/s vs peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_main_prefill_and_decode.json")
+COPY_BYTES = 1 << 30
 
 
 def prefill_bytes(T, H, Dk, Dv, in_bytes, out_bytes, n_seq):
@@ -40,19 +50,145 @@ def decode_bytes(N, H, Dk, Dv, in_bytes, out_bytes):
 
 
 def prefill_flops(T, H, Dk, Dv, C=64):
-    """Algorithmic flops per chunk-head (1 FMA = 2 flops, triangles as triangles)."""
-    tri = C * (C - 1) // 2          # strictly lower pairs
-    trid = C * (C + 1) // 2         # lower incl. diagonal
-    akk = 2 * tri * Dk + tri        # + beta scaling
-    aqk = 2 * trid * Dk
-    ut = sum(2 * i * (i - 1) // 2 for i in range(C))   # forward substitution
-    w = 2 * trid * Dk + C * Dk
-    u = 2 * trid * Dv + C * Dv
-    state = 3 * 2 * C * Dk * Dv
-    aqe = 2 * trid * Dv
-    decay = Dk * Dv
-    per_chunk = akk + aqk + ut + w + u + state + aqe + decay
+    """Algorithmic flops of one prefill call, 1 FMA = 2 flops, triangles counted as
+    triangles: per chunk-head A_kk 2 C(C-1)/2 Dk, A_qk 2 C(C+1)/2 Dk, the forward
+    substitution sum_i i(i-1), W and U C^2 Dk and C^2 Dv, the three state contractions
+    6 C Dk Dv, A_qk E 2 C(C+1)/2 Dv and the state decay Dk Dv (9,020,800 at d = 128)."""
+    tri, trid = C * (C - 1) // 2, C * (C + 1) // 2
+    per_chunk = (2 * tri * Dk + 2 * trid * Dk + sum(i * (i - 1) for i in range(C))
+                 + C * C * Dk + C * C * Dv + 6 * C * Dk * Dv + 2 * trid * Dv + Dk * Dv)
     return per_chunk * H * (T // C)
+
+
+def kernels_source_hash():
+    """sha256 over the kernel sources and build script (counter figures are tied to it)."""
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "gated_delta_rule_channel_amd")
+    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ------------------------------------------------------------------------------------------
+# counter summary
+# ------------------------------------------------------------------------------------------
+def _pmc_per_kernel(path, counter):
+    """Average value per dispatch of one counter, per kernel name, from a rocprofv3 CSV."""
+    per_dispatch = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    sums, counts = {}, {}
+    for (_, name), v in per_dispatch.items():
+        sums[name] = sums.get(name, 0.0) + v
+        counts[name] = counts.get(name, 0) + 1
+    return {n: (sums[n] / counts[n], counts[n]) for n in sums}
+
+
+def _short(name):
+    for key in ("prep_kernel", "state_kernel", "chunk_map_kernel", "decode_kernel"):
+        if key in name:
+            return key
+    return None
+
+
+def traffic_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv):
+    cf = max(v for v, _ in _pmc_per_kernel(cfetch_csv, "FETCH_SIZE").values())
+    cw = max(v for v, _ in _pmc_per_kernel(cwrite_csv, "WRITE_SIZE").values())
+    f_fac = COPY_BYTES / (cf * 1024.0)
+    w_fac = COPY_BYTES / (cw * 1024.0)
+    fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
+    per = {}
+    for name, (v, n) in fetch.items():
+        s = _short(name)
+        if s:
+            per.setdefault(s, {})["fetch_bytes"] = v * 1024.0 * f_fac
+            per[s]["dispatches"] = n
+    for name, (v, n) in write.items():
+        s = _short(name)
+        if s:
+            per.setdefault(s, {})["write_bytes"] = v * 1024.0 * w_fac
+    out = {
+        "kernels_source_sha256": kernels_source_hash(),
+        "calibration": {"copy_bytes": COPY_BYTES, "copy_fetch_kib": cf, "copy_write_kib": cw,
+                        "fetch_factor": f_fac, "write_factor": w_fac},
+        "per_kernel": per,
+        "prefill_call_bytes": sum(per[k]["fetch_bytes"] + per[k]["write_bytes"]
+                                  for k in ("chunk_map_kernel", "prep_kernel", "state_kernel")
+                                  if k in per),
+        "decode_bytes": (per["decode_kernel"]["fetch_bytes"] + per["decode_kernel"]["write_bytes"]
+                         if "decode_kernel" in per else None),
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def load_traffic():
+    """Measured HBM bytes per prefill call and per decode step, or None when the counters
+    were taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, None
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None, None
+    if d.get("kernels_source_sha256") != kernels_source_hash():
+        return None, None
+    return d.get("prefill_call_bytes"), d.get("decode_bytes")
+
+
+# ------------------------------------------------------------------------------------------
+# modes
+# ------------------------------------------------------------------------------------------
+def copy_calibration():
+    import torch
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}), flush=True)
+
+
+def cpu_baseline(wp, min_seconds):
+    """The float64 C oracle over all heads of the main prefill workload, repeated until at
+    least min_seconds of CPU time have passed (input generation excluded)."""
+    from gated_delta_rule_channel_amd import inputs as I
+    from oracle import native
+    native.build()
+    x = I.prefill_inputs(wp)
+    tokens = x.q.shape[0] * x.q.shape[1]
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        native.prefill(x.q, x.k, x.v, x.g, x.beta)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": tokens * passes / dt, "unit": "tokens/s", "cores": native.num_threads(),
+            "kind": "oracle",
+            "sample": f"float64 C oracle (OpenMP over heads), all {wp.H} heads of {wp.name}, "
+                      f"{passes} passes in {dt:.1f} s (input cast to fp32 included)",
+            "cpu_model": _cpu_model()}
 
 
 def main():
@@ -61,13 +197,21 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"))
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the KDA hot path here runs on a single MI355X "
-              "(per-head and per-request work shards without exchange; see DESIGN.md). "
+              "(heads, requests and sequences shard across GPUs without exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
@@ -96,6 +240,7 @@ def main():
     def decode():
         kda.decode_step(dq, dk, dv, dg, db, state, scale=1.0, out=od)
 
+    # both calls launch on torch's current stream, which the events below record on
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
         prefill()
@@ -103,6 +248,7 @@ def main():
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     for e0, e1, e2 in ev:
         e0.record(stream)
@@ -123,29 +269,11 @@ def main():
     value = tokens / tp_mean
     pf_gbs = pf_bytes / tp_mean / 1e9
     dc_gbs = dc_bytes / td_mean / 1e9
+    # split-bf16 operands: every product runs as three bf16 MFMAs
+    mfma_busy = 3.0 * pf_flops / (BF16_PEAK_TFLOPS * 1e12) / tp_mean
+    traffic_pf, traffic_dc = load_traffic()
 
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "prefill_main_traffic.json")
-    if os.path.exists(tfile):
-        try:
-            traffic = json.load(open(tfile)).get("bytes_per_call")
-        except Exception:
-            traffic = None
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        from oracle import native
-        hs = list(range(min(args.cpu_heads, H)))
-        xs = I.prefill_inputs(wp, heads=hs)
-        native.build()
-        t0 = time.perf_counter()
-        native.prefill(xs.q, xs.k, xs.v, xs.g, xs.beta)
-        dt = time.perf_counter() - t0
-        cpu = {"value": tokens * len(hs) / H / dt, "unit": "tokens/s", "cores": native.num_threads(),
-               "kind": "oracle",
-               "sample": f"float64 C oracle (OpenMP over heads) on {len(hs)} of {H} heads of the "
-                         f"main prefill workload (T={T}), {dt:.2f} s; tokens/s scaled to all {H} heads",
-               "cpu_model": platform.processor() or _cpu_model()}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wp, args.cpu_seconds)
 
     out = {
         "metric": METRIC,
@@ -163,33 +291,27 @@ def main():
         "config": {"workload": f"{wp.name} (fp32 state, fp32 o) + {wd.name}",
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": Dk, "d_v": Dv,
                    "chunk": 64, "parallelism": "single GPU"},
-        "prefill": {"ms": tp_mean * 1e3, "ms_min": float(tp.min()) * 1e3, "tokens_per_s": value,
+        "prefill": {"ms": tp_mean * 1e3, "ms_median": float(np.median(tp)) * 1e3,
+                    "ms_min": float(tp.min()) * 1e3, "tokens_per_s": value,
                     "compulsory_bytes": pf_bytes, "hbm_gbs": pf_gbs,
-                    "algorithmic_flops": pf_flops, "tflops": pf_flops / tp_mean / 1e12},
-        "decode": {"ms": td_mean * 1e3, "ms_min": float(td.min()) * 1e3,
+                    "algorithmic_flops": pf_flops, "tflops": pf_flops / tp_mean / 1e12,
+                    "mfma_busy_frac_split_bf16": mfma_busy},
+        "decode": {"ms": td_mean * 1e3, "ms_median": float(np.median(td)) * 1e3,
+                   "ms_min": float(td.min()) * 1e3,
                    "state_updates_per_s": wd.N * wd.H / td_mean, "tokens_per_s": wd.N / td_mean,
                    "compulsory_bytes": dc_bytes, "hbm_gbs": dc_gbs,
                    "frac_of_peak": dc_gbs / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": pf_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": pf_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kda_fwd_chunked (chunk map + prep + state pass) per call"},
+                     "frac": pf_gbs / HBM_PEAK_GBS, "traffic": traffic_pf,
+                     "kernel": "kda_fwd_chunked call (chunk_map_kernel + prep_kernel + "
+                               "state_kernel), one launch sequence per step"},
         "roofline_decode": {"bound": "hbm", "achieved": dc_gbs, "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": dc_gbs / HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": dc_gbs / HBM_PEAK_GBS, "traffic": traffic_dc,
                             "kernel": "decode_kernel"},
         "cpu_baseline": cpu,
         "wall_s_timed": t_wall,
     }
     print(json.dumps(out), flush=True)
-
-
-def _cpu_model():
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return "unknown"
 
 
 if __name__ == "__main__":
