@@ -17,7 +17,7 @@ hipError_t launch_prefill(bool bf16_in, bool bf16_out, int Dk, int Dv, const voi
                           float scale, const float* h0, float* ht, void* o, const int32_t* cu,
                           int T, const void* tab, const int32_t* seq_off, uint8_t* blocks, int N,
                           int H, int max_slots, hipStream_t s);
-size_t prefill_block_bytes(int Dk, int Dv);
+size_t prefill_block_bytes(int Dk, int Dv, bool bf16_in);
 }  // namespace kda
 
 namespace {
@@ -48,7 +48,7 @@ kda_status plan_prefill(int B, int T, int H, int Dk, int Dv, int num_seqs, bool 
     p->seq_off = ru((size_t)p->max_slots * 16, 256);
     p->blocks_off = p->seq_off + ru((size_t)(p->nseq + 1) * 4, 256);
     p->total = p->blocks_off +
-               (size_t)p->max_slots * H * kda::prefill_block_bytes(Dk, Dv);
+               (size_t)p->max_slots * H * kda::prefill_block_bytes(Dk, Dv, dtype == KDA_DTYPE_BF16);
     return KDA_SUCCESS;
 }
 

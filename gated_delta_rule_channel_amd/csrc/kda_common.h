@@ -16,8 +16,12 @@
 //   PolSplit -- each fp32 operand x is held as two bfloat16 values,
 //               hi = bf16(x) and lo = bf16(x - hi) (about 16 significant bits),
 //               and a product is hi*hi + hi*lo + lo*hi: three
-//               v_mfma_f32_16x16x32_bf16 with fp32 accumulation. Stored
-//               matrices keep the hi and lo parts in two planes.
+//               v_mfma_f32_16x16x32_bf16 with fp32 accumulation. Matrices in
+//               LDS keep the hi and lo parts in two planes. Fragment tiles in
+//               the workspace hold x rounded to 24 bits (16 significant bits)
+//               as its upper 16 bits (a bfloat16, hi) and the next 8 bits
+//               (one extension byte); lo = x24 - hi is exact in bfloat16, so
+//               the pair is rebuilt without loss from 3 bytes per element.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,6 +35,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx32 __attribute__((ext_vector_type(32)));
 typedef unsigned u32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kChunk = 64;       // tokens per chunk
 constexpr int kBlock = 16;       // tokens per sub-block (MFMA tile edge)
@@ -111,6 +117,10 @@ struct PolF32 {
         }
         __device__ __forceinline__ void set(int e, float x) { v[e] = x; }
         __device__ __forceinline__ float get(int e) const { return v[e]; }
+        __device__ __forceinline__ void pin_regs() {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(v[e]));
+        }
     };
     __device__ static __forceinline__ void mma(floatx4& acc, const Frag& a, const Frag& b) {
 #pragma unroll
@@ -158,17 +168,38 @@ struct PolF32 {
     }
     // ---- fragment tiles in the workspace (two 1 KB parts, lane-contiguous 16 B each) ----
     // part 0 holds elements 0..3 of every lane, part 1 elements 4..7
-    __device__ static __forceinline__ void tile_store(void* t, int lane, const Frag& f) {
+    static constexpr int kTileBytes = 2048;
+    using Tile = Frag;                      // fp32 tiles are used as loaded
+    __device__ static __forceinline__ void tile_store_vals(void* t, int lane, const float* x) {
         float4* p = reinterpret_cast<float4*>(t);
-        p[lane] = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
-        p[64 + lane] = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
+        p[lane] = make_float4(x[0], x[1], x[2], x[3]);
+        p[64 + lane] = make_float4(x[4], x[5], x[6], x[7]);
     }
-    __device__ static __forceinline__ void tile_load(Frag& f, const void* t, int lane) {
+    __device__ static __forceinline__ void tile_load_raw(Tile& f, const void* t, int lane) {
         const float4* p = reinterpret_cast<const float4*>(t);
         const float4 a = p[lane], b = p[64 + lane];
         f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
         f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
     }
+    __device__ static __forceinline__ void tile_decode(Frag& f, const Tile& r) { f = r; }
+    // pair tiles: two fragment tiles a, b back to back
+    static constexpr int kPairBytes = 4096;
+    struct Pair { Frag f[2]; };
+    __device__ static __forceinline__ void pair_store_vals(void* t, int lane, int which,
+                                                           const float* x) {
+        tile_store_vals(reinterpret_cast<uint8_t*>(t) + 2048 * which, lane, x);
+    }
+    __device__ static __forceinline__ void pair_store_quad(void* t, int lane, int which, int half,
+                                                           float a, float b, float c, float d) {
+        reinterpret_cast<float4*>(reinterpret_cast<uint8_t*>(t) + 2048 * which)[64 * half + lane] =
+            make_float4(a, b, c, d);
+    }
+    __device__ static __forceinline__ void pair_load(Pair& r, const void* t, int lane) {
+        tile_load_raw(r.f[0], t, lane);
+        tile_load_raw(r.f[1], reinterpret_cast<const uint8_t*>(t) + 2048, lane);
+    }
+    template <int W>
+    __device__ static __forceinline__ void pair_decode(Frag& f, const Pair& r) { f = r.f[W]; }
     // elements 4 half .. 4 half + 3 of a lane's fragment
     __device__ static __forceinline__ void tile_store_quad(void* t, int lane, int half, float a,
                                                            float b, float c, float d) {
@@ -214,6 +245,10 @@ struct PolSplit {
             lo[e] = (bf16)(x - (float)h);
         }
         __device__ __forceinline__ float get(int e) const { return (float)hi[e] + (float)lo[e]; }
+        __device__ __forceinline__ void pin_regs() {
+            asm volatile("" : "+v"(hi));
+            asm volatile("" : "+v"(lo));
+        }
     };
     __device__ static __forceinline__ void mma(floatx4& acc, const Frag& a, const Frag& b) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
@@ -275,26 +310,104 @@ struct PolSplit {
         return make_float4((float)h[0] + (float)l[0], (float)h[1] + (float)l[1],
                            (float)h[2] + (float)l[2], (float)h[3] + (float)l[3]);
     }
-    // ---- fragment tiles in the workspace (two 1 KB parts, lane-contiguous 16 B each) ----
-    // part 0 holds the hi parts of every lane, part 1 the lo parts
-    __device__ static __forceinline__ void tile_store(void* t, int lane, const Frag& f) {
-        bf16x8* p = reinterpret_cast<bf16x8*>(t);
-        p[lane] = f.hi;
-        p[64 + lane] = f.lo;
+    // ---- fragment tiles in the workspace (1.5 KB): part 0 (1 KB) holds the eight hi
+    // values of every lane (16 B), part 1 (512 B) their extension bytes (8 B) ----
+    static constexpr int kTileBytes = 1536;
+    struct Tile { bf16x8 hi; u32x2 ext; };
+    // x rounded to nearest even at bit 8: 24 bits of float32, 16 significant bits
+    __device__ static __forceinline__ unsigned round24(float x) {
+        unsigned u = __float_as_uint(x);
+        u += 0x7fu + ((u >> 8) & 1u);
+        return u & 0xffffff00u;
     }
-    __device__ static __forceinline__ void tile_load(Frag& f, const void* t, int lane) {
-        const bf16x8* p = reinterpret_cast<const bf16x8*>(t);
-        f.hi = p[lane];
-        f.lo = p[64 + lane];
+    __device__ static __forceinline__ unsigned ext4(unsigned a, unsigned b, unsigned c,
+                                                    unsigned d) {
+        return ((a >> 8) & 0xffu) | (b & 0xff00u) | ((c << 8) & 0xff0000u) |
+               ((d << 16) & 0xff000000u);
+    }
+    __device__ static __forceinline__ void tile_store_vals(void* t, int lane, const float* x) {
+        unsigned r[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = round24(x[e]);
+        u32x4 hw;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) hw[p] = (r[2 * p] >> 16) | (r[2 * p + 1] & 0xffff0000u);
+        u32x2 ew;
+        ew[0] = ext4(r[0], r[1], r[2], r[3]);
+        ew[1] = ext4(r[4], r[5], r[6], r[7]);
+        reinterpret_cast<u32x4*>(t)[lane] = hw;
+        reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(t) + 1024)[lane] = ew;
     }
     // elements 4 half .. 4 half + 3 of a lane's fragment
     __device__ static __forceinline__ void tile_store_quad(void* t, int lane, int half, float a,
                                                            float b, float c, float d) {
-        bf16x4 h, l;
-        split4(h, l, a, b, c, d);
-        bf16x4* p = reinterpret_cast<bf16x4*>(t);
-        p[2 * lane + half] = h;
-        p[128 + 2 * lane + half] = l;
+        const unsigned r0 = round24(a), r1 = round24(b), r2 = round24(c), r3 = round24(d);
+        u32x2 hw;
+        hw[0] = (r0 >> 16) | (r1 & 0xffff0000u);
+        hw[1] = (r2 >> 16) | (r3 & 0xffff0000u);
+        reinterpret_cast<u32x2*>(t)[2 * lane + half] = hw;
+        reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(t) + 1024)[2 * lane + half] =
+            ext4(r0, r1, r2, r3);
+    }
+    __device__ static __forceinline__ void tile_load_raw(Tile& r, const void* t, int lane) {
+        r.hi = reinterpret_cast<const bf16x8*>(t)[lane];
+        r.ext = reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(t) + 1024)[lane];
+    }
+    // hi as stored; lo = (hi with its extension byte) - hi, exact in bfloat16
+    __device__ static __forceinline__ void tile_decode(Frag& f, const Tile& r) {
+        f.hi = r.hi;
+        const u32x4 w = __builtin_bit_cast(u32x4, r.hi);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const unsigned e = r.ext[p >> 1] >> (16 * (p & 1));
+            const unsigned h0 = w[p] << 16, h1 = w[p] & 0xffff0000u;
+            const unsigned x0 = h0 | ((e & 0xffu) << 8), x1 = h1 | (e & 0xff00u);
+            f.lo[2 * p] = (bf16)(__uint_as_float(x0) - __uint_as_float(h0));
+            f.lo[2 * p + 1] = (bf16)(__uint_as_float(x1) - __uint_as_float(h1));
+        }
+    }
+    // pair tiles (3 KB): the hi values of fragment a (1 KB), of fragment b (1 KB), then the
+    // extension bytes of both (1 KB: 8 B of a, 8 B of b per lane), so two fragments take
+    // three 16-byte loads per lane
+    static constexpr int kPairBytes = 3072;
+    struct Pair { bf16x8 hi[2]; u32x4 ext; };
+    __device__ static __forceinline__ void pair_store_vals(void* t, int lane, int which,
+                                                           const float* x) {
+        unsigned r[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = round24(x[e]);
+        u32x4 hw;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) hw[p] = (r[2 * p] >> 16) | (r[2 * p + 1] & 0xffff0000u);
+        u32x2 ew;
+        ew[0] = ext4(r[0], r[1], r[2], r[3]);
+        ew[1] = ext4(r[4], r[5], r[6], r[7]);
+        reinterpret_cast<u32x4*>(t)[64 * which + lane] = hw;
+        reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(t) + 2048)[2 * lane + which] = ew;
+    }
+    __device__ static __forceinline__ void pair_store_quad(void* t, int lane, int which, int half,
+                                                           float a, float b, float c, float d) {
+        const unsigned r0 = round24(a), r1 = round24(b), r2 = round24(c), r3 = round24(d);
+        u32x2 hw;
+        hw[0] = (r0 >> 16) | (r1 & 0xffff0000u);
+        hw[1] = (r2 >> 16) | (r3 & 0xffff0000u);
+        reinterpret_cast<u32x2*>(t)[128 * which + 2 * lane + half] = hw;
+        reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(t) + 2048)[4 * lane + 2 * which + half] =
+            ext4(r0, r1, r2, r3);
+    }
+    __device__ static __forceinline__ void pair_load(Pair& r, const void* t, int lane) {
+        const bf16x8* p = reinterpret_cast<const bf16x8*>(t);
+        r.hi[0] = p[lane];
+        r.hi[1] = p[64 + lane];
+        r.ext = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(t) + 2048)[lane];
+    }
+    template <int W>
+    __device__ static __forceinline__ void pair_decode(Frag& f, const Pair& r) {
+        Tile t;
+        t.hi = r.hi[W];
+        t.ext[0] = r.ext[2 * W];
+        t.ext[1] = r.ext[2 * W + 1];
+        tile_decode(f, t);
     }
     // quad tiles (1 KB): four elements per lane as hi (8 B) then lo (8 B)
     __device__ static __forceinline__ void quad_store(void* t, int lane, float a, float b, float c,
@@ -348,6 +461,14 @@ __device__ __forceinline__ void mma16_f32(floatx4& acc, const float4& a, const f
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+}
+
+// Forces a register value to be computed here: the compiler may not sink its producers
+// (decodes, and the waits on the loads they read) past this point.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float4& x) {
+    asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
 }
 
 // ---- cross-lane helpers (a DPP row = 16 consecutive lanes = one value of grp) ------------

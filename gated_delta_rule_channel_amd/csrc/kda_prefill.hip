@@ -51,44 +51,48 @@ namespace kda {
 // ------------------------------------------------------------------------------------------
 // One block per (chunk slot, head). Every operand of the state pass is stored in the
 // register layout of the MFMA fragment that consumes it, so that one load instruction of a
-// wave reads 1 KB of consecutive bytes (16 B per lane):
-//  * fragment tile (2 KB): 8 elements per lane in two 1 KB parts (PolSplit: the hi parts,
-//    then the lo parts; PolF32: elements 0..3, then 4..7);
-//  * quad tile (1 KB): 4 elements per lane, 16 B (PolSplit: hi then lo; PolF32: 4 floats).
-// With lane l = m + 16 grp:
-//  W, Qd  fragment tiles [token tile tw][channel step kap]: row 16 tw + m, channels
+// wave reads 1 KB of consecutive bytes (16 B per lane). Fragments (8 elements per lane) are
+// stored in pairs (a, b): PolSplit, 3 KB: the hi values of a, of b, then the extension bytes
+// of both (x rounded to 24 bits = bfloat16 hi + 1 byte, 16 significant bits); PolF32, 4 KB:
+// two fp32 tiles. Quad tiles (1 KB) hold 4 elements per lane as bf16 hi then lo (PolSplit)
+// or 4 floats. With lane l = m + 16 grp:
+//  W, Qd  pairs [token tile tw][channel steps (2p, 2p+1)]: row 16 tw + m, channels
 //         32 kap + 8 grp + e (zero past Dk);
-//  Kd^T   fragment tiles [channel tile ct][token half ks]: channel 16 ct + m, tokens
+//  Kd^T   pairs [channel tile ct][token halves (0, 1)]: channel 16 ct + m, tokens
 //         32 ks + 8 grp + e;
 //  U      quad tiles [value tile vt][token tile tw]: tokens 16 tw + 4 grp + r, value 16 vt + m;
-//  A_qk   fragment tiles [token tile tw][column half s]: row 16 tw + m, columns 32 s + 8 grp + e;
+//  A_qk   pairs [token tile tw][column halves (0, 1)]: row 16 tw + m, columns 32 s + 8 grp + e;
 //  exp(G_end) float [Dk].
 __host__ __device__ constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-__host__ __device__ constexpr size_t ws_block_bytes(int DK, int DV) {
-    return round_up((size_t)2 * 4 * (DK >= 32 ? DK / 32 : 1) * 2048 + (size_t)(DK / 16) * 2 * 2048 +
-                        (size_t)(DV / 16) * 4 * 1024 + 8 * 2048 + (size_t)DK * 4,
+__host__ __device__ constexpr size_t ws_block_bytes(int DK, int DV, size_t PT) {
+    return round_up((size_t)2 * 4 * (((DK >= 32 ? DK / 32 : 1) + 1) / 2) * PT +
+                        (size_t)(DK / 16) * PT + (size_t)(DV / 16) * 4 * 1024 + 4 * PT +
+                        (size_t)DK * 4,
                     256);
 }
 
-template <int DK, int DV>
+template <int PTB, int DK, int DV>
 struct WsLayout {
     static constexpr int KS = DK >= 32 ? DK / 32 : 1;   // 32-channel steps (padded)
+    static constexpr int NP = (KS + 1) / 2;              // pairs of channel steps
     static constexpr int NCT = DK / 16;                  // 16-channel tiles
     static constexpr int NVT = DV / 16;                  // 16-value tiles
-    static constexpr size_t FT = 2048;                   // fragment tile
+    static constexpr size_t PT = PTB;                    // pair tile
     static constexpr size_t QT = 1024;                   // quad tile
     static constexpr size_t W = 0;
-    static constexpr size_t QD = W + 4 * KS * FT;
-    static constexpr size_t KDT = QD + 4 * KS * FT;
-    static constexpr size_t U = KDT + NCT * 2 * FT;
+    static constexpr size_t QD = W + 4 * NP * PT;
+    static constexpr size_t KDT = QD + 4 * NP * PT;
+    static constexpr size_t U = KDT + NCT * PT;
     static constexpr size_t AQ = U + NVT * 4 * QT;
-    static constexpr size_t GEND = AQ + 8 * FT;
+    static constexpr size_t GEND = AQ + 4 * PT;
     static constexpr size_t BYTES = round_up(GEND + DK * sizeof(float), 256);
-    static_assert(BYTES == ws_block_bytes(DK, DV), "workspace block size");
+    static_assert(BYTES == ws_block_bytes(DK, DV, PT), "workspace block size");
 };
 
-size_t prefill_block_bytes(int Dk, int Dv) { return ws_block_bytes(Dk, Dv); }
+size_t prefill_block_bytes(int Dk, int Dv, bool bf16_in) {
+    return ws_block_bytes(Dk, Dv, bf16_in ? PolSplit::kPairBytes : PolF32::kPairBytes);
+}
 
 // ------------------------------------------------------------------------------------------
 // chunk map
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
     using Pol = typename PolOf<TI>::type;
     using Frag = typename Pol::Frag;
     using Frag4 = typename Pol::Frag4;
-    using Ly = WsLayout<DK, DV>;
+    using Ly = WsLayout<Pol::kPairBytes, DK, DV>;
     constexpr int NSL = DK >= 32 ? DK / 32 : 1;          // channel slices (32 wide, padded)
     constexpr int NVS = DV >= 32 ? DV / 32 : 1;          // value slices
     // lower 16x16 blocks, rows padded to 20 floats so that 16 lanes reading 4 floats of
@@ -327,24 +331,26 @@ __global__ __launch_bounds__(256) void prep_kernel(
             }
             // (a) chunk-start / chunk-end references: Qd and Kd^T to the workspace
             {
-                Frag Qd, Kd;
+                Frag Kd;
+                float qdv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float Gc = pf[e] + Gl[e];
                     const float ec = fast_exp2(Gc), ed = fast_exp2(CE[24 + e] - Gc);
-                    Qd.set(e, scale * qq[e] * ec);
+                    qdv[e] = scale * qq[e] * ec;
                     Kd.set(e, kk[e] * ed);
                 }
-                Pol::tile_store(blk + Ly::QD + (I * Ly::KS + wave) * Ly::FT, lane, Qd);
+                Pol::pair_store_vals(blk + Ly::QD + (I * Ly::NP + (wave >> 1)) * Ly::PT, lane,
+                                     wave & 1, qdv);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     if (32 * wave + 16 * hh < DK) {
                         floatx4 dk = {0.f, 0.f, 0.f, 0.f};
                         Pol::mma_exact(dk, Kd, Eid[hh]);  // lane (channel n, grp): tokens 4 grp + r
                         const int ct = 2 * wave + hh, ks = I >> 1;
-                        Pol::tile_store_quad(blk + Ly::KDT + (ct * 2 + ks) * Ly::FT,
-                                             m + 16 * (2 * (I & 1) + (grp >> 1)), grp & 1, dk[0],
-                                             dk[1], dk[2], dk[3]);
+                        Pol::pair_store_quad(blk + Ly::KDT + ct * Ly::PT,
+                                             m + 16 * (2 * (I & 1) + (grp >> 1)), ks, grp & 1,
+                                             dk[0], dk[1], dk[2], dk[3]);
                     }
                 }
             }
@@ -457,16 +463,17 @@ __global__ __launch_bounds__(256) void prep_kernel(
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         const int J = 2 * s + (grp >> 1), jl = 8 * (grp & 1);
-        Frag f;
+        float a[8];
         if (J <= wave) {
             const float4 x0 = *reinterpret_cast<const float4*>(&sQK[tri_tile(wave, J)][m][jl]);
             const float4 x1 = *reinterpret_cast<const float4*>(&sQK[tri_tile(wave, J)][m][jl + 4]);
-            f.set(0, x0.x); f.set(1, x0.y); f.set(2, x0.z); f.set(3, x0.w);
-            f.set(4, x1.x); f.set(5, x1.y); f.set(6, x1.z); f.set(7, x1.w);
+            a[0] = x0.x; a[1] = x0.y; a[2] = x0.z; a[3] = x0.w;
+            a[4] = x1.x; a[5] = x1.y; a[6] = x1.z; a[7] = x1.w;
         } else {
-            f.zero();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[e] = 0.f;
         }
-        Pol::tile_store(blk + Ly::AQ + (wave * 2 + s) * Ly::FT, lane, f);
+        Pol::pair_store_vals(blk + Ly::AQ + wave * Ly::PT, lane, s, a);
     }
 
     // ---- T = (I + A_kk)^-1: diagonal blocks by forward substitution (fp32) ----
@@ -547,9 +554,9 @@ __global__ __launch_bounds__(256) void prep_kernel(
             }
 #pragma unroll
             for (int I = 0; I < 4; ++I)
-                Pol::tile_store_quad(blk + Ly::W + (I * Ly::KS + wave) * Ly::FT,
-                                     m + 16 * (2 * hh + (grp >> 1)), grp & 1, accW[I][0],
-                                     accW[I][1], accW[I][2], accW[I][3]);
+                Pol::pair_store_quad(blk + Ly::W + (I * Ly::NP + (wave >> 1)) * Ly::PT,
+                                     m + 16 * (2 * hh + (grp >> 1)), wave & 1, grp & 1,
+                                     accW[I][0], accW[I][1], accW[I][2], accW[I][3]);
         }
     }
     // ---- U = T' v: lane (m = value, grp) of tile (value tile, I) holds U[16 I + 4 grp + r][value] ----
@@ -582,19 +589,24 @@ __global__ __launch_bounds__(256) void prep_kernel(
 // ------------------------------------------------------------------------------------------
 // state kernel
 // ------------------------------------------------------------------------------------------
-// One workgroup of 8 waves per (sequence, head, 32-column value tile). Waves 0-3 (the E
-// role) own token tile w of every chunk: E = U - W S, O = Qd S + A_qk E and the output
-// store. Waves 4-7 (the S role) own channel tiles w-4, w, ... of the state, kept in fp32
-// MFMA accumulators for the whole sequence: S' = Diag(exp G_end) S + Kd^T E. The two roles
-// meet twice per chunk through LDS: E [value][token] and the operand copy of S
-// [value][channel]. Every product is oriented so that the MFMA result tile has tokens or
-// channels along its rows: a lane then holds 4 consecutive rows of one value column, which
-// is 4 consecutive elements of those LDS layouts (8-byte LDS stores, no 2-byte scatter).
-// Each role loads only its own workspace operands, one chunk ahead, into two alternating
-// register sets.
+// One workgroup of 12 waves per (sequence, head, 32-column value tile), in three roles of
+// four waves. Each chunk runs in two phases separated by workgroup barriers:
+//   phase A (S_c published): E role (token tile w)  E = U - W S_c      -> LDS
+//                            O role (token tile w)  O  = Qd S_c        (registers)
+//   phase B (E published):   S role (channel tiles) S_{c+1} = Diag(exp G_end) S_c + Kd^T E
+//                                                   -> LDS operand copy, fp32 in registers
+//                            O role                 O += A_qk E, write o
+// so the serial chain of a chunk is one product per phase, and every role decodes the next
+// chunk's operands and issues later chunks' loads while it is off the chain. The S role
+// keeps S in fp32 MFMA accumulators for the whole sequence. All reads of S_c and E happen
+// in the phase before they are overwritten, so one LDS copy of each suffices. Every product
+// is oriented so that the MFMA result tile has tokens or channels along its rows (4
+// consecutive elements per lane); O is formed transposed so that a lane writes 4
+// consecutive values of one token.
 template <int DK, int DV, int BV>
 struct StateShape {
     static constexpr int KS = DK >= 32 ? DK / 32 : 1;
+    static constexpr int NP = (KS + 1) / 2;
     static constexpr int DKP = KS * 32;
     static constexpr int NVT = BV / 16;                 // value tiles of the workgroup
     static constexpr int NCT = DK / 16;                 // channel tiles of the state
@@ -604,72 +616,28 @@ struct StateShape {
     static constexpr int VT = DV / BV;                  // value tiles per head
 };
 
-template <typename Pol, int DK, int DV, int BV>
-struct EOps {                          // E-role operands of one chunk (token tile = wave)
-    using Sh = StateShape<DK, DV, BV>;
-    using Frag = typename Pol::Frag;
-    Frag w[Sh::KS], qd[Sh::KS];        // rows of W and Qd
-    typename Pol::Raw4 u[Sh::NVT];     // U^T at (value column, 4 tokens)
-    Frag aq[2];                        // row of A_qk in 32-token slices
-};
-
-template <typename Pol, int DK, int DV, int BV>
-struct SOps {                          // S-role operands of one chunk
-    using Sh = StateShape<DK, DV, BV>;
-    using Frag = typename Pol::Frag;
-    Frag kd[Sh::CTW][2];               // rows of Kd^T of the owned channel tiles
-    float4 gd[Sh::CTW];                // exp(G_end) of the lane's 4 channels per tile
-};
-
-template <typename Pol, int DK, int DV, int BV>
-__device__ __forceinline__ void load_e_ops(EOps<Pol, DK, DV, BV>& c,
-                                           const uint8_t* __restrict__ ws, int cidx, int h, int H,
-                                           int v0, int tw, int lane) {
-    using Sh = StateShape<DK, DV, BV>;
-    using Ly = WsLayout<DK, DV>;
-    const uint8_t* blk = ws + ((size_t)cidx * H + h) * Ly::BYTES;
+template <typename Pol, int KS, int NP>
+__device__ __forceinline__ void decode_pairs(typename Pol::Frag (&d)[KS],
+                                             const typename Pol::Pair (&r)[NP]) {
 #pragma unroll
-    for (int kap = 0; kap < Sh::KS; ++kap) {
-        Pol::tile_load(c.w[kap], blk + Ly::W + (tw * Ly::KS + kap) * Ly::FT, lane);
-        Pol::tile_load(c.qd[kap], blk + Ly::QD + (tw * Ly::KS + kap) * Ly::FT, lane);
-    }
-#pragma unroll
-    for (int vr = 0; vr < Sh::NVT; ++vr)
-        Pol::quad_load(c.u[vr], blk + Ly::U + ((v0 / 16 + vr) * 4 + tw) * Ly::QT, lane);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        if (s == 0 || tw >= 2) Pol::tile_load(c.aq[s], blk + Ly::AQ + (tw * 2 + s) * Ly::FT, lane);
-    }
-}
-
-template <typename Pol, int DK, int DV, int BV>
-__device__ __forceinline__ void load_s_ops(SOps<Pol, DK, DV, BV>& c, const uint8_t* __restrict__ ws,
-                                           int cidx, int h, int H, int sw, int lane) {
-    using Sh = StateShape<DK, DV, BV>;
-    using Ly = WsLayout<DK, DV>;
-    const uint8_t* blk = ws + ((size_t)cidx * H + h) * Ly::BYTES;
-    const float* gGend = reinterpret_cast<const float*>(blk + Ly::GEND);
-    const int grp = lane >> 4;
-#pragma unroll
-    for (int j = 0; j < Sh::CTW; ++j) {
-        const int ct = sw + 4 * j;
-        c.gd[j] = *reinterpret_cast<const float4*>(gGend + 16 * ct + 4 * grp);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            Pol::tile_load(c.kd[j][ks], blk + Ly::KDT + (ct * 2 + ks) * Ly::FT, lane);
+    for (int kap = 0; kap < KS; ++kap) {
+        if (kap & 1) Pol::template pair_decode<1>(d[kap], r[kap >> 1]);
+        else Pol::template pair_decode<0>(d[kap], r[kap >> 1]);
     }
 }
 
 template <typename TI, typename TO, int DK, int DV, int BV>
-__global__ __launch_bounds__(512) void state_kernel(
+__global__ __launch_bounds__(768) void state_kernel(
     const int32_t* __restrict__ cu, int T, const int32_t* __restrict__ seq_off,
     const uint8_t* __restrict__ ws, const float* __restrict__ h0, float* __restrict__ ht,
     TO* __restrict__ o, int N, int H) {
     using Pol = typename PolOf<TI>::type;
     using Frag = typename Pol::Frag;
+    using Pair = typename Pol::Pair;
     using St = typename Pol::Store;
     using Sh = StateShape<DK, DV, BV>;
-    constexpr int KS = Sh::KS, NVT = Sh::NVT, NCT = Sh::NCT, CTW = Sh::CTW;
+    using Ly = WsLayout<Pol::kPairBytes, DK, DV>;
+    constexpr int KS = Sh::KS, NP = Sh::NP, NVT = Sh::NVT, NCT = Sh::NCT, CTW = Sh::CTW;
     constexpr int P = Pol::kPlanes;
     __shared__ St SLs[P][BV][Sh::SST];     // operand copy of S [value][channel]
     __shared__ St ELs[P][BV][Sh::EST];     // E [value][token]
@@ -685,14 +653,15 @@ __global__ __launch_bounds__(512) void state_kernel(
     const int n = hc / H, h = hc % H;
     const int v0 = vt * BV;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = lane & 15, grp = lane >> 4;
-    const bool erole = wave < 4;
-    const int tw = wave & 3;                       // token tile (E role) / S-role index
-    const bool owns = !erole && (NCT >= 4 || tw < NCT);
+    const int role = wave >> 2;                    // 0: E, 1: S, 2: O
+    const int tw = wave & 3;                       // token tile (E, O) / S-role index
+    const bool owns = role == 1 && (NCT >= 4 || tw < NCT);
 
     // zero the pad channels of the S copy once (only read when DK < 32)
-    for (int idx = tid; idx < BV * (Sh::SST - DK); idx += 512) {
+    for (int idx = tid; idx < BV * (Sh::SST - DK); idx += 768) {
         const int r = idx / (Sh::SST - DK), c = DK + idx % (Sh::SST - DK);
         Pol::put(SL, (size_t)r * Sh::SST + c, psS, 0.f);
     }
@@ -719,146 +688,237 @@ __global__ __launch_bounds__(512) void state_kernel(
 
     // The chunks of sequence n are the consecutive slots [c_beg, c_end); chunk c covers
     // tokens [s_beg + 64 (c - c_beg), min(+64, s_end)). No per-chunk table reads happen in
-    // the loop (a scalar load there would share lgkmcnt with the LDS traffic and stall it).
+    // the loop (a scalar load there would share lgkmcnt with the LDS traffic). Prefetches
+    // are unconditional (index clamped to the last chunk) so the loop has no branches
+    // around loads.
     const int c_beg = seq_off[n], c_end = seq_off[n + 1];
     const int s_beg = cu ? cu[n] : n * T, s_end = cu ? cu[n + 1] : (n + 1) * T;
+    const int last = c_end - 1;
     const size_t rowo = (size_t)H * DV;
-
-    // E role: E = U - W S into LDS; O = Qd S + A_qk E to memory. Tiles (token tile tw,
-    // value tile vr): for E, lane (n = value, grp) holds tokens 16 tw + 4 grp + r; O is
-    // formed transposed, so lane (n = token, grp) holds values 16 vr + 4 grp + r (16-byte
-    // output stores).
-    auto e_phase1 = [&](const EOps<Pol, DK, DV, BV>& cur, floatx4 (&accO)[NVT]) {
-        floatx4 accE[NVT];
+    auto block = [&](int c) { return ws + ((size_t)c * H + h) * Ly::BYTES; };
+    __syncthreads();                               // S copy initialised
+    if (c_beg >= c_end) {
+        // empty sequence: the state passes through
+    } else if (role == 0) {
+        // ---- E role: E = U - W S ----
+        struct Raw {
+            Pair w[NP];
+            typename Pol::Raw4 u[NVT];
+        };
+        Raw R0, R1;                                // raw operands of two later chunks
+        Frag wd[KS];                               // decoded W of the current chunk
+        float4 ud[NVT];
+        auto issue = [&](Raw& r, int c) {
+            const uint8_t* blk = block(c);
 #pragma unroll
-        for (int vr = 0; vr < NVT; ++vr) {
-            accE[vr] = floatx4{0.f, 0.f, 0.f, 0.f};
-            accO[vr] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int kap = 0; kap < KS; ++kap) {
-            const int c0 = 32 * kap + 8 * grp;
-#pragma unroll
-            for (int vr = 0; vr < NVT; ++vr) {
-                Frag b;
-                Pol::load(b, SL, (size_t)(16 * vr + m) * Sh::SST + c0, psS);
-                Pol::mma(accE[vr], cur.w[kap], b);
-                Pol::mma(accO[vr], b, cur.qd[kap]);       // O^T: rows = values
-            }
-        }
-#pragma unroll
-        for (int vr = 0; vr < NVT; ++vr) {
-            const float4 u = Pol::raw4f(cur.u[vr]);
-            Pol::store4(EL, (size_t)(16 * vr + m) * Sh::EST + 16 * tw + 4 * grp, psE,
-                        u.x - accE[vr][0], u.y - accE[vr][1], u.z - accE[vr][2],
-                        u.w - accE[vr][3]);
-        }
-    };
-    auto e_phase2 = [&](const EOps<Pol, DK, DV, BV>& cur, floatx4 (&accO)[NVT], int cidx) {
-        const int t0 = s_beg + kChunk * (cidx - c_beg);
-        const int len = s_end - t0 < kChunk ? s_end - t0 : kChunk;
-        const int nks = tw < 2 ? 1 : 2;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            if (s2 < nks) {
-#pragma unroll
-                for (int vr = 0; vr < NVT; ++vr) {
-                    Frag b;
-                    Pol::load(b, EL, (size_t)(16 * vr + m) * Sh::EST + 32 * s2 + 8 * grp, psE);
-                    Pol::mma(accO[vr], b, cur.aq[s2]);
-                }
-            }
-        }
-        const int tok = 16 * tw + m;
-        if (tok < len) {
-            TO* orow = o + (size_t)(t0 + tok) * rowo + (size_t)h * DV + v0 + 4 * grp;
+            for (int p = 0; p < NP; ++p)
+                Pol::pair_load(r.w[p], blk + Ly::W + (tw * NP + p) * Ly::PT, lane);
 #pragma unroll
             for (int vr = 0; vr < NVT; ++vr)
-                store4(orow + 16 * vr, accO[vr][0], accO[vr][1], accO[vr][2], accO[vr][3]);
-        }
-    };
-    // S role: S = Diag(exp G_end) S + Kd^T E, then the operand copy of S
-    auto s_phase2 = [&](const SOps<Pol, DK, DV, BV>& cur) {
-        if (!owns) return;
-#pragma unroll
-        for (int j = 0; j < CTW; ++j) {
-            const int c = 16 * (tw + 4 * j) + 4 * grp;
-#pragma unroll
-            for (int vr = 0; vr < NVT; ++vr) {
-                S[j][vr][0] *= cur.gd[j].x;
-                S[j][vr][1] *= cur.gd[j].y;
-                S[j][vr][2] *= cur.gd[j].z;
-                S[j][vr][3] *= cur.gd[j].w;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    Frag b;
-                    Pol::load(b, EL, (size_t)(16 * vr + m) * Sh::EST + 32 * ks + 8 * grp, psE);
-                    Pol::mma(S[j][vr], cur.kd[j][ks], b);
-                }
-                Pol::store4(SL, (size_t)(16 * vr + m) * Sh::SST + c, psS, S[j][vr][0],
-                            S[j][vr][1], S[j][vr][2], S[j][vr][3]);
-            }
-        }
-    };
-
-    // Chunks go in pairs (operand sets A and B alternate); every prefetch is unconditional
-    // (index clamped to the last chunk) so that the loop has no branches around loads.
-    const int last = c_end - 1;
-    if (erole) {
-        EOps<Pol, DK, DV, BV> A, B;
-        floatx4 accO[NVT];
-        if (c_beg < c_end) { load_e_ops(A, ws, c_beg, h, H, v0, tw, lane); issue_fence(); }
-        __syncthreads();                                  // S copy initialised
-        int cidx = c_beg;
-        for (; cidx + 1 < c_end; cidx += 2) {
-            load_e_ops(B, ws, cidx + 1, h, H, v0, tw, lane);
+                Pol::quad_load(r.u[vr], blk + Ly::U + ((v0 / 16 + vr) * 4 + tw) * Ly::QT, lane);
             issue_fence();
-            e_phase1(A, accO);
-            __syncthreads();                              // E complete
-            e_phase2(A, accO, cidx);
-            __syncthreads();                              // S updated, E consumed
-            load_e_ops(A, ws, min(cidx + 2, last), h, H, v0, tw, lane);
-            issue_fence();
-            e_phase1(B, accO);
-            __syncthreads();
-            e_phase2(B, accO, cidx + 1);
-            __syncthreads();
-        }
-        if (cidx < c_end) {
-            e_phase1(A, accO);
-            __syncthreads();
-            e_phase2(A, accO, cidx);
-            __syncthreads();
-        }
-    } else {
-        SOps<Pol, DK, DV, BV> A, B;
-        if (c_beg < c_end && owns) { load_s_ops(A, ws, c_beg, h, H, tw, lane); issue_fence(); }
-        __syncthreads();
-        int cidx = c_beg;
-        for (; cidx + 1 < c_end; cidx += 2) {
-            if (owns) { load_s_ops(B, ws, cidx + 1, h, H, tw, lane); issue_fence(); }
-            __syncthreads();                              // E complete
-            s_phase2(A);
-            __syncthreads();
-            if (owns) { load_s_ops(A, ws, min(cidx + 2, last), h, H, tw, lane); issue_fence(); }
-            __syncthreads();
-            s_phase2(B);
-            __syncthreads();
-        }
-        if (cidx < c_end) {
-            __syncthreads();
-            s_phase2(A);
-            __syncthreads();
-        }
-        if (ht && owns) {
+        };
+        auto decode = [&](const Raw& r) {
+            decode_pairs<Pol, KS, NP>(wd, r.w);
 #pragma unroll
-            for (int j = 0; j < CTW; ++j) {
+            for (int vr = 0; vr < NVT; ++vr) ud[vr] = Pol::raw4f(r.u[vr]);
+#pragma unroll
+            for (int kap = 0; kap < KS; ++kap) wd[kap].pin_regs();
+#pragma unroll
+            for (int vr = 0; vr < NVT; ++vr) pin(ud[vr]);
+        };
+        // one chunk: E to LDS; then, off the chain, loads of chunk c + 2 into `next` and
+        // the decode of chunk c + 1 from `cur1`
+        auto chunk = [&](int c, Raw& next, const Raw& cur1) {
+            floatx4 accE[NVT];
+#pragma unroll
+            for (int vr = 0; vr < NVT; ++vr) accE[vr] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kap = 0; kap < KS; ++kap) {
 #pragma unroll
                 for (int vr = 0; vr < NVT; ++vr) {
-                    const int c = 16 * (tw + 4 * j) + 4 * grp, vv = v0 + 16 * vr + m;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) ht[sbase + (size_t)(c + r) * DV + vv] = S[j][vr][r];
+                    Frag bS;
+                    Pol::load(bS, SL, (size_t)(16 * vr + m) * Sh::SST + 32 * kap + 8 * grp, psS);
+                    Pol::mma(accE[vr], wd[kap], bS);
                 }
+            }
+            // lane (n = value, grp) holds E[tokens 16 tw + 4 grp + r][value]
+#pragma unroll
+            for (int vr = 0; vr < NVT; ++vr)
+                Pol::store4(EL, (size_t)(16 * vr + m) * Sh::EST + 16 * tw + 4 * grp, psE,
+                            ud[vr].x - accE[vr][0], ud[vr].y - accE[vr][1],
+                            ud[vr].z - accE[vr][2], ud[vr].w - accE[vr][3]);
+            __syncthreads();                       // phase B: E published
+            issue(next, min(c + 2, last));
+            decode(cur1);                          // chunk c + 1
+            __syncthreads();                       // phase A: S_{c+1} published
+        };
+        issue(R0, c_beg);
+        issue(R1, min(c_beg + 1, last));
+        decode(R0);
+        int c = c_beg;
+#pragma unroll 1
+        for (; c + 1 < c_end; c += 2) {
+            chunk(c, R0, R1);
+            chunk(c + 1, R1, R0);
+        }
+        if (c < c_end) chunk(c, R0, R1);
+    } else if (role == 1) {
+        // ---- S role: S' = Diag(exp G_end) S + Kd^T E ----
+        struct Raw {
+            Pair k[CTW];
+            float4 g[CTW];
+        };
+        Raw R0, R1;                                // raw operands of two later chunks
+        Frag kd[CTW][2];                           // decoded Kd^T of the current chunk
+        float4 gd[CTW];
+        auto issue = [&](Raw& r, int c) {
+            if (owns) {
+                const uint8_t* blk = block(c);
+                const float* gGend = reinterpret_cast<const float*>(blk + Ly::GEND);
+#pragma unroll
+                for (int j = 0; j < CTW; ++j) {
+                    const int ct = tw + 4 * j;
+                    r.g[j] = *reinterpret_cast<const float4*>(gGend + 16 * ct + 4 * grp);
+                    Pol::pair_load(r.k[j], blk + Ly::KDT + ct * Ly::PT, lane);
+                }
+                issue_fence();
+            }
+        };
+        auto decode = [&](const Raw& r) {
+            if (owns) {
+#pragma unroll
+                for (int j = 0; j < CTW; ++j) {
+                    Pol::template pair_decode<0>(kd[j][0], r.k[j]);
+                    Pol::template pair_decode<1>(kd[j][1], r.k[j]);
+                    gd[j] = r.g[j];
+                    kd[j][0].pin_regs();
+                    kd[j][1].pin_regs();
+                    pin(gd[j]);
+                }
+            }
+        };
+        auto chunk = [&](int c, Raw& next, const Raw& cur1) {
+            __syncthreads();                       // phase B: E published
+            if (owns) {
+#pragma unroll
+                for (int j = 0; j < CTW; ++j) {
+                    const int cc = 16 * (tw + 4 * j) + 4 * grp;
+#pragma unroll
+                    for (int vr = 0; vr < NVT; ++vr) {
+                        S[j][vr][0] *= gd[j].x;
+                        S[j][vr][1] *= gd[j].y;
+                        S[j][vr][2] *= gd[j].z;
+                        S[j][vr][3] *= gd[j].w;
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) {
+                            Frag bE;
+                            Pol::load(bE, EL, (size_t)(16 * vr + m) * Sh::EST + 32 * ks + 8 * grp, psE);
+                            Pol::mma(S[j][vr], kd[j][ks], bE);
+                        }
+                        Pol::store4(SL, (size_t)(16 * vr + m) * Sh::SST + cc, psS, S[j][vr][0],
+                                    S[j][vr][1], S[j][vr][2], S[j][vr][3]);
+                    }
+                }
+            }
+            __syncthreads();                       // phase A: S_{c+1} published
+            issue(next, min(c + 2, last));
+            decode(cur1);                          // chunk c + 1
+        };
+        issue(R0, c_beg);
+        issue(R1, min(c_beg + 1, last));
+        decode(R0);
+        int c = c_beg;
+#pragma unroll 1
+        for (; c + 1 < c_end; c += 2) {
+            chunk(c, R0, R1);
+            chunk(c + 1, R1, R0);
+        }
+        if (c < c_end) chunk(c, R0, R1);
+    } else {
+        // ---- O role: O^T = S^T Qd^T + E^T A_qk^T; lane (n = token, grp) holds values
+        //      16 vr + 4 grp + r ----
+        struct Raw {
+            Pair q[NP];
+            Pair a;
+        };
+        Raw R0, R1;                                // raw operands of two later chunks
+        Frag qd[KS], aq[2];                        // decoded, current chunk
+        auto issue = [&](Raw& r, int c) {
+            const uint8_t* blk = block(c);
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+                Pol::pair_load(r.q[p], blk + Ly::QD + (tw * NP + p) * Ly::PT, lane);
+            Pol::pair_load(r.a, blk + Ly::AQ + tw * Ly::PT, lane);
+            issue_fence();
+        };
+        auto decode = [&](const Raw& r) {
+            decode_pairs<Pol, KS, NP>(qd, r.q);
+            Pol::template pair_decode<0>(aq[0], r.a);
+            Pol::template pair_decode<1>(aq[1], r.a);
+#pragma unroll
+            for (int kap = 0; kap < KS; ++kap) qd[kap].pin_regs();
+            aq[0].pin_regs();
+            aq[1].pin_regs();
+        };
+        const int nks = tw < 2 ? 1 : 2;            // nonzero column halves of A_qk rows
+        auto chunk = [&](int c, Raw& next, const Raw& cur1) {
+            floatx4 accO[NVT];
+#pragma unroll
+            for (int vr = 0; vr < NVT; ++vr) accO[vr] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kap = 0; kap < KS; ++kap) {
+#pragma unroll
+                for (int vr = 0; vr < NVT; ++vr) {
+                    Frag bS;
+                    Pol::load(bS, SL, (size_t)(16 * vr + m) * Sh::SST + 32 * kap + 8 * grp, psS);
+                    Pol::mma(accO[vr], bS, qd[kap]);
+                }
+            }
+            __syncthreads();                       // phase B: E published
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (s2 < nks) {
+#pragma unroll
+                    for (int vr = 0; vr < NVT; ++vr) {
+                        Frag bE;
+                        Pol::load(bE, EL, (size_t)(16 * vr + m) * Sh::EST + 32 * s2 + 8 * grp, psE);
+                        Pol::mma(accO[vr], bE, aq[s2]);
+                    }
+                }
+            }
+            const int t0 = s_beg + kChunk * (c - c_beg);
+            const int len = s_end - t0 < kChunk ? s_end - t0 : kChunk;
+            const int tok = 16 * tw + m;
+            if (tok < len) {
+                TO* orow = o + (size_t)(t0 + tok) * rowo + (size_t)h * DV + v0 + 4 * grp;
+#pragma unroll
+                for (int vr = 0; vr < NVT; ++vr)
+                    store4(orow + 16 * vr, accO[vr][0], accO[vr][1], accO[vr][2], accO[vr][3]);
+            }
+            issue(next, min(c + 2, last));
+            decode(cur1);                          // chunk c + 1
+            __syncthreads();                       // phase A: S_{c+1} published
+        };
+        issue(R0, c_beg);
+        issue(R1, min(c_beg + 1, last));
+        decode(R0);
+        int c = c_beg;
+#pragma unroll 1
+        for (; c + 1 < c_end; c += 2) {
+            chunk(c, R0, R1);
+            chunk(c + 1, R1, R0);
+        }
+        if (c < c_end) chunk(c, R0, R1);
+    }
+    if (ht && owns) {
+#pragma unroll
+        for (int j = 0; j < CTW; ++j) {
+#pragma unroll
+            for (int vr = 0; vr < NVT; ++vr) {
+                const int c = 16 * (tw + 4 * j) + 4 * grp, vv = v0 + 16 * vr + m;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ht[sbase + (size_t)(c + r) * DV + vv] = S[j][vr][r];
             }
         }
     }
@@ -889,7 +949,7 @@ static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, 
     constexpr int VT = DV / BV;
     const long long chains = (long long)N * H;
     const long long nblk = ((chains + 7) / 8) * 8 * VT;
-    hipLaunchKernelGGL((state_kernel<TI, TO, DK, DV, BV>), dim3((unsigned)nblk), dim3(512), 0, s,
+    hipLaunchKernelGGL((state_kernel<TI, TO, DK, DV, BV>), dim3((unsigned)nblk), dim3(768), 0, s,
                        cu, T, seq_off, (const uint8_t*)blocks, h0, ht, (TO*)o, N, H);
     return hipGetLastError();
 }
