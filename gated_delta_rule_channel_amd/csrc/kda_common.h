@@ -382,8 +382,9 @@ struct PolSplit {
         u32x2 ew;
         ew[0] = ext4(r[0], r[1], r[2], r[3]);
         ew[1] = ext4(r[4], r[5], r[6], r[7]);
-        reinterpret_cast<u32x4*>(t)[64 * which + lane] = hw;
-        reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(t) + 2048)[2 * lane + which] = ew;
+        __builtin_nontemporal_store(hw, reinterpret_cast<u32x4*>(t) + 64 * which + lane);
+        __builtin_nontemporal_store(
+            ew, reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(t) + 2048) + 2 * lane + which);
     }
     __device__ static __forceinline__ void pair_store_quad(void* t, int lane, int which, int half,
                                                            float a, float b, float c, float d) {
@@ -391,9 +392,10 @@ struct PolSplit {
         u32x2 hw;
         hw[0] = (r0 >> 16) | (r1 & 0xffff0000u);
         hw[1] = (r2 >> 16) | (r3 & 0xffff0000u);
-        reinterpret_cast<u32x2*>(t)[128 * which + 2 * lane + half] = hw;
-        reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(t) + 2048)[4 * lane + 2 * which + half] =
-            ext4(r0, r1, r2, r3);
+        __builtin_nontemporal_store(hw, reinterpret_cast<u32x2*>(t) + 128 * which + 2 * lane + half);
+        __builtin_nontemporal_store(
+            ext4(r0, r1, r2, r3),
+            reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(t) + 2048) + 4 * lane + 2 * which + half);
     }
     __device__ static __forceinline__ void pair_load(Pair& r, const void* t, int lane) {
         const bf16x8* p = reinterpret_cast<const bf16x8*>(t);
@@ -417,7 +419,7 @@ struct PolSplit {
         bf16x8 x;
         x[0] = h[0]; x[1] = h[1]; x[2] = h[2]; x[3] = h[3];
         x[4] = l[0]; x[5] = l[1]; x[6] = l[2]; x[7] = l[3];
-        reinterpret_cast<bf16x8*>(t)[lane] = x;
+        __builtin_nontemporal_store(x, reinterpret_cast<bf16x8*>(t) + lane);
     }
     __device__ static __forceinline__ void split4(bf16x4& h, bf16x4& l, float a, float b, float c,
                                                   float d) {

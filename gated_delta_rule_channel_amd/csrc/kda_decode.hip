@@ -14,7 +14,8 @@
 // consecutive value columns (one 16-byte vector per state row) of rows
 // rs, rs + RS, ...; a wavefront therefore streams whole contiguous rows. The
 // column sums of v^ and r are reduced across rows with lane shuffles inside a
-// wavefront and through LDS across wavefronts.
+// wavefront and through LDS across wavefronts. State loads and stores are
+// nontemporal: each state is touched once per step.
 #include "kda_common.h"
 
 namespace kda {
@@ -58,7 +59,9 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rs + RS * i;
-        s[i] = reinterpret_cast<const float4*>(S + (size_t)r * DV)[cg];
+        // streamed once: nontemporal (no reuse in the caches)
+        const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(S + (size_t)r * DV) + cg);
+        s[i] = make_float4(t[0], t[1], t[2], t[3]);
     }
     float4 vh = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 rq = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -112,7 +115,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
         const int r = rs + RS * i;
         float4 x = s[i];
         x.x += kr[i] * e.x; x.y += kr[i] * e.y; x.z += kr[i] * e.z; x.w += kr[i] * e.w;
-        reinterpret_cast<float4*>(S + (size_t)r * DV)[cg] = x;
+        __builtin_nontemporal_store(floatx4{x.x, x.y, x.z, x.w},
+                                    reinterpret_cast<floatx4*>(S + (size_t)r * DV) + cg);
     }
     if (rs == 0) {                                                 // (5) read
         store4(o + (size_t)head * DV + 4 * cg, rq.x + kq * e.x, rq.y + kq * e.y,

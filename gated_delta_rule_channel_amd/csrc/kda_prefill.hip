@@ -173,8 +173,8 @@ template <typename T> struct In32;
 template <> struct In32<bf16> {
     u32x16 w;                                            // two bfloat16 per word
     __device__ __forceinline__ void load(int I, const bf16* p) {
-        const uint4 x = *reinterpret_cast<const uint4*>(p);
-        w[4 * I] = x.x; w[4 * I + 1] = x.y; w[4 * I + 2] = x.z; w[4 * I + 3] = x.w;
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        w[4 * I] = x[0]; w[4 * I + 1] = x[1]; w[4 * I + 2] = x[2]; w[4 * I + 3] = x[3];
     }
     __device__ __forceinline__ void zero(int I) {
         w[4 * I] = 0u; w[4 * I + 1] = 0u; w[4 * I + 2] = 0u; w[4 * I + 3] = 0u;
@@ -269,10 +269,10 @@ __global__ __launch_bounds__(256) void prep_kernel(
         const int row = 16 * I + m;
         if (cvalid && row < L) {
             const size_t off = (size_t)(t0 + row) * rowq + (size_t)h * DK + c0;
-            const float4 g0 = reinterpret_cast<const float4*>(g + off)[0];
-            const float4 g1 = reinterpret_cast<const float4*>(g + off)[1];
-            G[8 * I] = g0.x; G[8 * I + 1] = g0.y; G[8 * I + 2] = g0.z; G[8 * I + 3] = g0.w;
-            G[8 * I + 4] = g1.x; G[8 * I + 5] = g1.y; G[8 * I + 6] = g1.z; G[8 * I + 7] = g1.w;
+            const floatx4 g0 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(g + off));
+            const floatx4 g1 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(g + off) + 1);
+            G[8 * I] = g0[0]; G[8 * I + 1] = g0[1]; G[8 * I + 2] = g0[2]; G[8 * I + 3] = g0[3];
+            G[8 * I + 4] = g1[0]; G[8 * I + 5] = g1[1]; G[8 * I + 6] = g1[2]; G[8 * I + 7] = g1[3];
             K.load(I, k + off);
             Q.load(I, q + off);
         } else {
