@@ -228,7 +228,7 @@ __device__ __forceinline__ typename Pol::Frag4 frag4_of(const floatx4& d) {
 }
 
 template <typename TI, int DK, int DV>
-__global__ __launch_bounds__(256) void prep_kernel(
+__global__ __launch_bounds__(256, 3) void prep_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
     const float* __restrict__ g, const TI* __restrict__ beta, float scale,
     const int4* __restrict__ tab, uint8_t* __restrict__ ws, int H) {
@@ -244,6 +244,8 @@ __global__ __launch_bounds__(256) void prep_kernel(
     __shared__ float sQK[10][16][20];                     // A_qk lower blocks
     __shared__ float sT[10][16][20];                      // T = (I + A_kk)^-1 lower blocks
     __shared__ float sBeta[64];
+    __shared__ float4 sCE[4][NSL * 8];                    // cumulative log-decay at block ends
+    __shared__ Frag4 sTp[10][64];                         // T' = T diag(beta) as fragments
 
     const int slot = blockIdx.x, h = blockIdx.y;
     const int4 ci = tab[slot];
@@ -289,21 +291,39 @@ __global__ __launch_bounds__(256) void prep_kernel(
         (&sQK[0][0][0])[idx] = 0.f;
     }
 
-    // ---- block-local prefix sums (log2 units); CE = cumulative value at each block end ----
-    floatx32 CE;
+    // ---- block-local prefix sums (log2 units); the cumulative value at each block end goes
+    //      to LDS (all 16 lanes of a row hold it), the chunk total stays in registers ----
+    float gtot[8];
+    {
+        float ce[4][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float acc = 0.f;
+        for (int e = 0; e < 8; ++e) {
+            float acc = 0.f;
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            G[8 * I + e] = row_scan16(G[8 * I + e] * kLog2e);
-            acc += row_bcast<15>(G[8 * I + e]);
-            CE[8 * I + e] = acc;
+            for (int I = 0; I < 4; ++I) {
+                G[8 * I + e] = row_scan16(G[8 * I + e] * kLog2e);
+                acc += row_bcast<15>(G[8 * I + e]);
+                ce[I][e] = acc;
+            }
+            gtot[e] = acc;
+        }
+        if (cs && m == 0) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                sCE[I][2 * (c0 / 8)] = make_float4(ce[I][0], ce[I][1], ce[I][2], ce[I][3]);
+                sCE[I][2 * (c0 / 8) + 1] = make_float4(ce[I][4], ce[I][5], ce[I][6], ce[I][7]);
+            }
         }
     }
+    // the 8 cumulative values of this lane's channels at the end of block I
+    auto ce8 = [&](int I, float* o) {
+        const float4 a = sCE[I][2 * (c0 / 8)], b = sCE[I][2 * (c0 / 8) + 1];
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+        o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    };
     if (cvalid && m == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) gGend[c0 + e] = fast_exp2(CE[24 + e]);
+        for (int e = 0; e < 8; ++e) gGend[c0 + e] = fast_exp2(gtot[e]);
     }
     // identity slices: Eid[hh] as a B operand maps K index 16 hh + n to column n
     Frag Eid[2];
@@ -324,10 +344,11 @@ __global__ __launch_bounds__(256) void prep_kernel(
             float Gl[8], kk[8], qq[8], pf[8];
             K.get8(I, kk);
             Q.get8(I, qq);
+            ce8(Ip, pf);                                  // cumulative value before block I
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 Gl[e] = G[8 * I + e];
-                pf[e] = I > 0 ? CE[8 * Ip + e] : 0.f;     // cumulative value before block I
+                if (I == 0) pf[e] = 0.f;
             }
             // (a) chunk-start / chunk-end references: Qd and Kd^T to the workspace
             {
@@ -336,7 +357,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float Gc = pf[e] + Gl[e];
-                    const float ec = fast_exp2(Gc), ed = fast_exp2(CE[24 + e] - Gc);
+                    const float ec = fast_exp2(Gc), ed = fast_exp2(gtot[e] - Gc);
                     qdv[e] = scale * qq[e] * ec;
                     Kd.set(e, kk[e] * ed);
                 }
@@ -423,13 +444,14 @@ __global__ __launch_bounds__(256) void prep_kernel(
                 for (int J = 0; J < I; ++J) {
                     // k of block J decayed to the start of block I
                     const int Jp = __builtin_amdgcn_readfirstlane(J > 0 ? J - 1 : 0);
-                    float kJ[8];
+                    float kJ[8], ceJ[8];
                     K.get8(J, kJ);
+                    ce8(Jp, ceJ);
                     Frag b;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float ceJ = J > 0 ? CE[8 * Jp + e] : 0.f;
-                        b.set(e, kJ[e] * fast_exp2(pf[e] - ceJ - G[8 * J + e]));
+                        const float cj = J > 0 ? ceJ[e] : 0.f;
+                        b.set(e, kJ[e] * fast_exp2(pf[e] - cj - G[8 * J + e]));
                     }
                     floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
                     Pol::mma(akk, b, KA);
@@ -513,18 +535,18 @@ __global__ __launch_bounds__(256) void prep_kernel(
     }
     __syncthreads();
 
-    // ---- T' = T diag(beta) as operand fragments: lane (m, grp) holds T'[16I + m][16J + 4grp + r]
-    Frag4 Tp[10];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-#pragma unroll
-        for (int J = 0; J <= I; ++J) {
-            const float4 t = *reinterpret_cast<const float4*>(&sT[tri_tile(I, J)][m][4 * grp]);
-            const float4 bb = *reinterpret_cast<const float4*>(&sBeta[16 * J + 4 * grp]);
-            Frag4& f = Tp[tri_tile(I, J)];
-            f.set(0, t.x * bb.x); f.set(1, t.y * bb.y); f.set(2, t.z * bb.z); f.set(3, t.w * bb.w);
-        }
+    // ---- T' = T diag(beta) as operand fragments in LDS, converted once: lane (m, grp) of
+    //      tile (I, J) holds T'[16I + m][16J + 4grp + r] ----
+    for (int tile = wave; tile < 10; tile += 4) {
+        const int I = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+        const int J = tile - I * (I + 1) / 2;
+        const float4 t = *reinterpret_cast<const float4*>(&sT[tile][m][4 * grp]);
+        const float4 bb = *reinterpret_cast<const float4*>(&sBeta[16 * J + 4 * grp]);
+        Frag4 f;
+        f.set(0, t.x * bb.x); f.set(1, t.y * bb.y); f.set(2, t.z * bb.z); f.set(3, t.w * bb.w);
+        sTp[tile][lane] = f;
     }
+    __syncthreads();
 
     // ---- W = T' (k exp G): W^T(channel half, I) = sum_{J <= I} (k exp G)_J^T T'_IJ^T; the
     //      result lane (m = token, grp) holds W[16 I + m][4 channels] ----
@@ -537,19 +559,20 @@ __global__ __launch_bounds__(256) void prep_kernel(
             if (32 * wave + 16 * hh < DK) {
 #pragma unroll
                 for (int J = 0; J < 4; ++J) {
-                    float kJ[8];
+                    float kJ[8], ceJ[8];
                     K.get8(J, kJ);
+                    ce8(J > 0 ? J - 1 : 0, ceJ);
                     Frag kg;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float ceJ = J > 0 ? CE[8 * (J - 1) + e] : 0.f;
-                        kg.set(e, kJ[e] * fast_exp2(ceJ + G[8 * J + e]));
+                        const float cj = J > 0 ? ceJ[e] : 0.f;
+                        kg.set(e, kJ[e] * fast_exp2(cj + G[8 * J + e]));
                     }
                     floatx4 t = {0.f, 0.f, 0.f, 0.f};
                     Pol::mma_exact(t, kg, Eid[hh]);       // lane (channel n, grp): tokens 4 grp + r
                     const Frag4 a = frag4_of<Pol>(t);
 #pragma unroll
-                    for (int I = J; I < 4; ++I) Pol::mma16(accW[I], a, Tp[tri_tile(I, J)]);
+                    for (int I = J; I < 4; ++I) Pol::mma16(accW[I], a, sTp[tri_tile(I, J)][lane]);
                 }
             }
 #pragma unroll
@@ -575,7 +598,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
                     Pol::mma_copy(t, vb, Eid[hh]);        // lane (value n, grp): tokens 4 grp + r
                     const Frag4 b = frag4_of<Pol>(t);
 #pragma unroll
-                    for (int I = J; I < 4; ++I) Pol::mma16_exact(accU[I], Tp[tri_tile(I, J)], b);
+                    for (int I = J; I < 4; ++I) Pol::mma16_exact(accU[I], sTp[tri_tile(I, J)][lane], b);
                 }
 #pragma unroll
                 for (int I = 0; I < 4; ++I)
