@@ -549,38 +549,42 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(
     __syncthreads();
 
     // ---- W = T' (k exp G): W^T(channel half, I) = sum_{J <= I} (k exp G)_J^T T'_IJ^T; the
-    //      result lane (m = token, grp) holds W[16 I + m][4 channels] ----
+    //      result lane (m = token, grp) holds W[16 I + m][4 channels]. The operand of block
+    //      J is built once and transposed for both 16-channel halves ----
     if (cs) {
+        constexpr int NH = DK >= 32 ? 2 : 1;              // channel halves with data
+        floatx4 accW[2][4];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            floatx4 accW[4];
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int I = 0; I < 4; ++I) accW[I] = floatx4{0.f, 0.f, 0.f, 0.f};
-            if (32 * wave + 16 * hh < DK) {
+            for (int I = 0; I < 4; ++I) accW[hh][I] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int J = 0; J < 4; ++J) {
-                    float kJ[8], ceJ[8];
-                    K.get8(J, kJ);
-                    ce8(J > 0 ? J - 1 : 0, ceJ);
-                    Frag kg;
+        for (int J = 0; J < 4; ++J) {
+            float kJ[8], ceJ[8];
+            K.get8(J, kJ);
+            ce8(J > 0 ? J - 1 : 0, ceJ);
+            Frag kg;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float cj = J > 0 ? ceJ[e] : 0.f;
-                        kg.set(e, kJ[e] * fast_exp2(cj + G[8 * J + e]));
-                    }
-                    floatx4 t = {0.f, 0.f, 0.f, 0.f};
-                    Pol::mma_exact(t, kg, Eid[hh]);       // lane (channel n, grp): tokens 4 grp + r
-                    const Frag4 a = frag4_of<Pol>(t);
-#pragma unroll
-                    for (int I = J; I < 4; ++I) Pol::mma16(accW[I], a, sTp[tri_tile(I, J)][lane]);
-                }
+            for (int e = 0; e < 8; ++e) {
+                const float cj = J > 0 ? ceJ[e] : 0.f;
+                kg.set(e, kJ[e] * fast_exp2(cj + G[8 * J + e]));
             }
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh) {
+                floatx4 t = {0.f, 0.f, 0.f, 0.f};
+                Pol::mma_exact(t, kg, Eid[hh]);           // lane (channel n, grp): tokens 4 grp + r
+                const Frag4 a = frag4_of<Pol>(t);
+#pragma unroll
+                for (int I = J; I < 4; ++I) Pol::mma16(accW[hh][I], a, sTp[tri_tile(I, J)][lane]);
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int I = 0; I < 4; ++I)
                 Pol::pair_store_quad(blk + Ly::W + (I * Ly::NP + (wave >> 1)) * Ly::PT,
                                      m + 16 * (2 * hh + (grp >> 1)), wave & 1, grp & 1,
-                                     accW[I][0], accW[I][1], accW[I][2], accW[I][3]);
-        }
+                                     accW[hh][I][0], accW[hh][I][1], accW[hh][I][2], accW[hh][I][3]);
     }
     // ---- U = T' v: lane (m = value, grp) of tile (value tile, I) holds U[16 I + 4 grp + r][value] ----
     if (wave < NVS) {
