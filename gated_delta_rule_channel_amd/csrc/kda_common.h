@@ -314,11 +314,10 @@ struct PolSplit {
     // values of every lane (16 B), part 1 (512 B) their extension bytes (8 B) ----
     static constexpr int kTileBytes = 1536;
     struct Tile { bf16x8 hi; u32x2 ext; };
-    // x rounded to nearest even at bit 8: 24 bits of float32, 16 significant bits
+    // x rounded to 24 bits of float32 (16 significant bits), half-way cases away from zero;
+    // the low byte is left as is (callers take bytes 1..3 only)
     __device__ static __forceinline__ unsigned round24(float x) {
-        unsigned u = __float_as_uint(x);
-        u += 0x7fu + ((u >> 8) & 1u);
-        return u & 0xffffff00u;
+        return __float_as_uint(x) + 0x80u;
     }
     __device__ static __forceinline__ unsigned ext4(unsigned a, unsigned b, unsigned c,
                                                     unsigned d) {
