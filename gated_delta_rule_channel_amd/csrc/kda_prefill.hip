@@ -375,24 +375,45 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(
                     }
                 }
             }
-            // (b) diagonal block (midpoint reference, or pairwise when out of range)
+            // row operands with the block-start reference, exp(G_i - G_r) <= 1 (r = end of
+            // block I - 1): shared by the diagonal and the off-diagonal blocks of row I
+            Frag KA, QA;
+            bool far = false;                             // block decays beyond 2^120
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float ea = fast_exp2(Gl[e]);
+                KA.set(e, bi * kk[e] * ea);
+                QA.set(e, scale * qq[e] * ea);
+                far |= Gl[e] < -120.f;
+            }
+            // (b) diagonal block: block-start reference (column factor exp(G_r - G_j) <= 2^120),
+            //     else the midpoint of the block, else pairwise
             {
                 floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
-                Frag KE, QE, KR;
                 bool bad = false;
+                if (!__any(far)) {
+                    Frag KC;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = Gl[e] - row_bcast<7>(Gl[e]);
-                    bad |= fabsf(x) > 120.f;
-                    const float e1 = fast_exp2(x), e2 = fast_exp2(-x);
-                    KE.set(e, bi * kk[e] * e1);
-                    QE.set(e, scale * qq[e] * e1);
-                    KR.set(e, kk[e] * e2);
-                }
-                if (!__any(bad)) {
-                    Pol::mma(akk, KR, KE);
-                    Pol::mma(aqk, KR, QE);
+                    for (int e = 0; e < 8; ++e) KC.set(e, kk[e] * fast_exp2(-Gl[e]));
+                    Pol::mma(akk, KC, KA);
+                    Pol::mma(aqk, KC, QA);
                 } else {
+                    Frag KE, QE, KR;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float x = Gl[e] - row_bcast<7>(Gl[e]);
+                        bad |= fabsf(x) > 120.f;
+                        const float e1 = fast_exp2(x), e2 = fast_exp2(-x);
+                        KE.set(e, bi * kk[e] * e1);
+                        QE.set(e, scale * qq[e] * e1);
+                        KR.set(e, kk[e] * e2);
+                    }
+                    if (!__any(bad)) {
+                        Pol::mma(akk, KR, KE);
+                        Pol::mma(aqk, KR, QE);
+                    }
+                }
+                if (__any(bad)) {
                     // exact pairwise sums over this slice: entry (i = m, j = jj)
 #pragma unroll 1
                     for (int jj = 0; jj < 16; ++jj) {
@@ -433,13 +454,6 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(
             }
             // (c) off-diagonal blocks J < I: reference at the end of block I - 1
             if (I > 0) {
-                Frag KA, QA;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float ea = fast_exp2(Gl[e]);
-                    KA.set(e, bi * kk[e] * ea);
-                    QA.set(e, scale * qq[e] * ea);
-                }
 #pragma unroll 1
                 for (int J = 0; J < I; ++J) {
                     // k of block J decayed to the start of block I
