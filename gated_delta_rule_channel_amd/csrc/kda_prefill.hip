@@ -228,7 +228,7 @@ __device__ __forceinline__ typename Pol::Frag4 frag4_of(const floatx4& d) {
 }
 
 template <typename TI, int DK, int DV>
-__global__ __launch_bounds__(256, 3) void prep_kernel(
+__global__ __launch_bounds__(256, 2) void prep_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
     const float* __restrict__ g, const TI* __restrict__ beta, float scale,
     const int4* __restrict__ tab, uint8_t* __restrict__ ws, int H) {
