@@ -452,32 +452,53 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                 *pk = a;
                 *pq = c;
             }
-            // (c) off-diagonal blocks J < I: reference at the end of block I - 1
+            // (c) off-diagonal blocks J < I: reference at the end of block I - 1. The pair
+            //     (3, 0) is taken by the wave holding row block 0 in this step (that wave has
+            //     no other off-diagonal pair), which balances the steps; every pair still gets
+            //     one partial per wave and no two waves write one block in the same step.
+            // partial of pair (II, J) with row operands KA, QA of block II (pfI = cumulative
+            // value before block II)
+            auto offdiag = [&](int II, int J, const Frag& KA2, const Frag& QA2, const float* pfI) {
+                // k of block J decayed to the start of block II
+                const int Jp = __builtin_amdgcn_readfirstlane(J > 0 ? J - 1 : 0);
+                float kJ[8], ceJ[8];
+                K.get8(J, kJ);
+                ce8(Jp, ceJ);
+                Frag b;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float cj = J > 0 ? ceJ[e] : 0.f;
+                    b.set(e, kJ[e] * fast_exp2(pfI[e] - cj - G[8 * J + e]));
+                }
+                floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+                Pol::mma(akk, b, KA2);
+                Pol::mma(aqk, b, QA2);
+                float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(II, J)][m][4 * grp]);
+                float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(II, J)][m][4 * grp]);
+                float4 a = *pk, c = *pq;
+                a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
+                c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
+                *pk = a;
+                *pq = c;
+            };
             if (I > 0) {
 #pragma unroll 1
-                for (int J = 0; J < I; ++J) {
-                    // k of block J decayed to the start of block I
-                    const int Jp = __builtin_amdgcn_readfirstlane(J > 0 ? J - 1 : 0);
-                    float kJ[8], ceJ[8];
-                    K.get8(J, kJ);
-                    ce8(Jp, ceJ);
-                    Frag b;
+                for (int J = I == 3 ? 1 : 0; J < I; ++J) offdiag(I, J, KA, QA, pf);
+            } else {
+                // row block 3 of this slice (static registers)
+                float k3[8], q3[8], pf3[8];
+                K.get8(3, k3);
+                Q.get8(3, q3);
+                ce8(2, pf3);
+                const float b3 = sBeta[48 + m];
+                Frag KA3, QA3;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float cj = J > 0 ? ceJ[e] : 0.f;
-                        b.set(e, kJ[e] * fast_exp2(pf[e] - cj - G[8 * J + e]));
-                    }
-                    floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
-                    Pol::mma(akk, b, KA);
-                    Pol::mma(aqk, b, QA);
-                    float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(I, J)][m][4 * grp]);
-                    float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(I, J)][m][4 * grp]);
-                    float4 a = *pk, c = *pq;
-                    a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
-                    c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
-                    *pk = a;
-                    *pq = c;
+                for (int e = 0; e < 8; ++e) {
+                    const float ea = fast_exp2(G[24 + e]);
+                    KA3.set(e, b3 * k3[e] * ea);
+                    QA3.set(e, scale * q3[e] * ea);
                 }
+                offdiag(3, 0, KA3, QA3, pf3);
             }
         }
         __syncthreads();
