@@ -95,11 +95,15 @@ kda_status kda_fwd_chunked(const void* q, const void* k, const void* v, const fl
         return KDA_ERROR_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    void* tab = ws + p.tab_off;
-    int32_t* seq_off = reinterpret_cast<int32_t*>(ws + p.seq_off);
-    if (kda::launch_chunk_map(cu_seqlens, p.nseq, T, (int)p.max_slots, tab, seq_off, s) !=
-        hipSuccess)
-        return KDA_ERROR_LAUNCH;
+    void* tab = nullptr;
+    int32_t* seq_off = nullptr;
+    if (cu_seqlens) {                          // packed sequences: chunk table on the device
+        tab = ws + p.tab_off;
+        seq_off = reinterpret_cast<int32_t*>(ws + p.seq_off);
+        if (kda::launch_chunk_map(cu_seqlens, p.nseq, T, (int)p.max_slots, tab, seq_off, s) !=
+            hipSuccess)
+            return KDA_ERROR_LAUNCH;
+    }
     if (kda::launch_prefill(dtype == KDA_DTYPE_BF16, o_dtype == KDA_DTYPE_BF16, Dk, Dv, q, k, v,
                             g, beta, scale, h0, ht, o, cu_seqlens, T, tab, seq_off,
                             ws + p.blocks_off, p.nseq, H, (int)p.max_slots, s) != hipSuccess)

@@ -18,9 +18,10 @@
 //   S' = Diag(exp(G_end)) S + (k exp(G_end - G))^T E
 //
 // Kernels
-//  * chunk_map_kernel:  cu_seqlens -> table of (token start, length, seq) per
-//    chunk slot and the first slot of every sequence, on the device (the host
-//    never reads cu_seqlens).
+//  * chunk_map_kernel (packed sequences only):  cu_seqlens -> table of (token
+//    start, length, seq) per chunk slot and the first slot of every sequence, on
+//    the device (the host never reads cu_seqlens). A fixed-length batch maps
+//    slots arithmetically.
 //  * prep_kernel: one workgroup per (chunk, head), fully parallel. Computes
 //    everything that does not depend on S and writes it to the workspace:
 //    W [64][Dk], Qd = scale q exp(G) [64][Dk], KdT = (k exp(G_end-G))^T
@@ -231,7 +232,7 @@ template <typename TI, int DK, int DV>
 __global__ __launch_bounds__(256, 2) void prep_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
     const float* __restrict__ g, const TI* __restrict__ beta, float scale,
-    const int4* __restrict__ tab, uint8_t* __restrict__ ws, int H) {
+    const int4* __restrict__ tab, int T, uint8_t* __restrict__ ws, int H) {
     using Pol = typename PolOf<TI>::type;
     using Frag = typename Pol::Frag;
     using Frag4 = typename Pol::Frag4;
@@ -248,8 +249,16 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     __shared__ Frag4 sTp[10][64];                         // T' = T diag(beta) as fragments
 
     const int slot = blockIdx.x, h = blockIdx.y;
-    const int4 ci = tab[slot];
-    const int t0 = ci.x, L = ci.y;
+    int t0, L;
+    if (tab) {                                            // packed sequences: chunk table
+        const int4 ci = tab[slot];
+        t0 = ci.x;
+        L = ci.y;
+    } else {                                              // B rows of T tokens
+        const int nck = (T + kChunk - 1) / kChunk, row = slot / nck, c = slot % nck;
+        t0 = row * T + kChunk * c;
+        L = T - kChunk * c < kChunk ? T - kChunk * c : kChunk;
+    }
     if (L <= 0) return;                                   // uniform per workgroup
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -754,7 +763,8 @@ __global__ __launch_bounds__(768) void state_kernel(
     // the loop (a scalar load there would share lgkmcnt with the LDS traffic). Prefetches
     // are unconditional (index clamped to the last chunk) so the loop has no branches
     // around loads.
-    const int c_beg = seq_off[n], c_end = seq_off[n + 1];
+    const int nck = (T + kChunk - 1) / kChunk;
+    const int c_beg = seq_off ? seq_off[n] : n * nck, c_end = seq_off ? seq_off[n + 1] : (n + 1) * nck;
     const int s_beg = cu ? cu[n] : n * T, s_end = cu ? cu[n + 1] : (n + 1) * T;
     const int last = c_end - 1;
     const size_t rowo = (size_t)H * DV;
@@ -1013,7 +1023,7 @@ static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, 
                                    int max_slots, hipStream_t s) {
     hipLaunchKernelGGL((prep_kernel<TI, DK, DV>), dim3(max_slots, H), dim3(256), 0, s,
                        (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
-                       (const int4*)tab, blocks, H);
+                       (const int4*)tab, T, blocks, H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int BV = DV >= 32 ? 32 : DV;
