@@ -303,8 +303,8 @@ def main():
                    "frac_of_peak": dc_gbs / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": pf_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": pf_gbs / HBM_PEAK_GBS, "traffic": traffic_pf,
-                     "kernel": "kda_fwd_chunked call (chunk_map_kernel + prep_kernel + "
-                               "state_kernel), one launch sequence per step"},
+                     "kernel": "kda_fwd_chunked call (prep_kernel + state_kernel; packed "
+                               "input adds chunk_map_kernel), one launch sequence per step"},
         "roofline_decode": {"bound": "hbm", "achieved": dc_gbs, "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": dc_gbs / HBM_PEAK_GBS, "traffic": traffic_dc,
                             "kernel": "decode_kernel"},
