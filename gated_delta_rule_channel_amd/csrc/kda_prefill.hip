@@ -713,6 +713,7 @@ __global__ __launch_bounds__(768) void state_kernel(
     __shared__ St SLs[P][BV][Sh::SST];     // operand copy of S [value][channel]
     __shared__ St ELs[P][BV][Sh::EST];     // E [value][token]
     __shared__ float4 OLs[4][NVT][64];     // Qd S per token tile, in the O lane layout
+    __shared__ float4 sGd[DK / 4];         // exp(G_end) of the chunk in phase B
     St* const SL = &SLs[0][0][0];
     St* const EL = &ELs[0][0][0];
     constexpr size_t psS = (size_t)BV * Sh::SST, psE = (size_t)BV * Sh::EST;
@@ -869,38 +870,40 @@ __global__ __launch_bounds__(768) void state_kernel(
         }
         if (c < c_end) chunk(c, R0, R1);
     } else if (role == 1) {
-        // ---- S role: S' = Diag(exp G_end) S + Kd^T E ----
+        // ---- S role: S' = Diag(exp G_end) S + Kd^T E. exp(G_end) (Dk floats) is fetched by
+        //      the first S-role wave alone and shared through LDS ----
         struct Raw {
             Pair k[CTW];
-            float4 g[CTW];
+            float2 g;                              // exp(G_end)[2 lane, 2 lane + 1] (wave 4)
         };
         Raw R0, R1;                                // raw operands of two later chunks
         Frag kd[CTW][2];                           // decoded Kd^T of the current chunk
-        float4 gd[CTW];
+        const bool gload = tw == 0 && 2 * lane < DK;
         auto issue = [&](Raw& r, int c) {
             if (owns) {
                 const uint8_t* blk = block(c);
                 const float* gGend = reinterpret_cast<const float*>(blk + Ly::GEND);
+                if (tw == 0) r.g = reinterpret_cast<const float2*>(gGend)[gload ? lane : 0];
 #pragma unroll
                 for (int j = 0; j < CTW; ++j) {
                     const int ct = tw + 4 * j;
-                    r.g[j] = *reinterpret_cast<const float4*>(gGend + 16 * ct + 4 * grp);
                     Pol::pair_load(r.k[j], blk + Ly::KDT + ct * Ly::PT, lane);
                 }
                 issue_fence();
             }
         };
+        // decodes the next chunk's Kd^T and publishes its exp(G_end) (read after the next
+        // phase-B barrier; the current values were read before the last one)
         auto decode = [&](const Raw& r) {
             if (owns) {
 #pragma unroll
                 for (int j = 0; j < CTW; ++j) {
                     Pol::template pair_decode<0>(kd[j][0], r.k[j]);
                     Pol::template pair_decode<1>(kd[j][1], r.k[j]);
-                    gd[j] = r.g[j];
                     kd[j][0].pin_regs();
                     kd[j][1].pin_regs();
-                    pin(gd[j]);
                 }
+                if (gload) reinterpret_cast<float2*>(&sGd[0])[lane] = r.g;
             }
         };
         auto chunk = [&](int c, Raw& next, const Raw& cur1) {
@@ -909,12 +912,13 @@ __global__ __launch_bounds__(768) void state_kernel(
 #pragma unroll
                 for (int j = 0; j < CTW; ++j) {
                     const int cc = 16 * (tw + 4 * j) + 4 * grp;
+                    const float4 gd = sGd[4 * (tw + 4 * j) + grp];
 #pragma unroll
                     for (int vr = 0; vr < NVT; ++vr) {
-                        S[j][vr][0] *= gd[j].x;
-                        S[j][vr][1] *= gd[j].y;
-                        S[j][vr][2] *= gd[j].z;
-                        S[j][vr][3] *= gd[j].w;
+                        S[j][vr][0] *= gd.x;
+                        S[j][vr][1] *= gd.y;
+                        S[j][vr][2] *= gd.z;
+                        S[j][vr][3] *= gd.w;
 #pragma unroll
                         for (int ks = 0; ks < 2; ++ks) {
                             Frag bE;
