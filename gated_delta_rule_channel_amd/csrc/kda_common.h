@@ -391,8 +391,8 @@ struct PolSplit {
         ew[0] = ext4(r[0], r[1], r[2], r[3]);
         ew[1] = ext4(r[4], r[5], r[6], r[7]);
         __builtin_nontemporal_store(hw, reinterpret_cast<u32x4*>(t) + 64 * which + lane);
-        __builtin_nontemporal_store(
-            ew, reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(t) + 2048) + 2 * lane + which);
+        // half of every 16 B: the other wave of the pair writes the rest, merged in L2
+        reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(t) + 2048)[2 * lane + which] = ew;
     }
     __device__ static __forceinline__ void pair_store_quad(void* t, int lane, int which, int half,
                                                            float a, float b, float c, float d) {
@@ -400,10 +400,11 @@ struct PolSplit {
         u32x2 hw;
         hw[0] = (r0 >> 16) | (r1 & 0xffff0000u);
         hw[1] = (r2 >> 16) | (r3 & 0xffff0000u);
-        __builtin_nontemporal_store(hw, reinterpret_cast<u32x2*>(t) + 128 * which + 2 * lane + half);
-        __builtin_nontemporal_store(
-            ext4(r0, r1, r2, r3),
-            reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(t) + 2048) + 4 * lane + 2 * which + half);
+        // partial 16-byte groups (the other halves come from other lanes or waves): plain
+        // stores, merged in L2
+        reinterpret_cast<u32x2*>(t)[128 * which + 2 * lane + half] = hw;
+        reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(t) + 2048)[4 * lane + 2 * which + half] =
+            ext4(r0, r1, r2, r3);
     }
     __device__ static __forceinline__ void pair_load(Pair& r, const void* t, int lane) {
         const bf16x8* p = reinterpret_cast<const bf16x8*>(t);
