@@ -72,15 +72,6 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
-// Stores of outputs that are not read again by this kernel (nontemporal)
-__device__ __forceinline__ void store4_nt(bf16* p, float a, float b, float c, float d) {
-    bf16x4 x;
-    x[0] = (bf16)a; x[1] = (bf16)b; x[2] = (bf16)c; x[3] = (bf16)d;
-    __builtin_nontemporal_store(x, reinterpret_cast<bf16x4*>(p));
-}
-__device__ __forceinline__ void store4_nt(float* p, float a, float b, float c, float d) {
-    __builtin_nontemporal_store(floatx4{a, b, c, d}, reinterpret_cast<floatx4*>(p));
-}
 __device__ __forceinline__ float4 load4f(const bf16* p) {
     const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
     return make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);

@@ -853,7 +853,7 @@ __global__ __launch_bounds__(768) void state_kernel(
                 TO* orow = o + (size_t)(t0 + tok) * rowo + (size_t)h * DV + v0 + 4 * grp;
 #pragma unroll
                 for (int vr = 0; vr < NVT; ++vr)
-                    store4_nt(orow + 16 * vr, acc[vr][0], acc[vr][1], acc[vr][2], acc[vr][3]);
+                    store4(orow + 16 * vr, acc[vr][0], acc[vr][1], acc[vr][2], acc[vr][3]);
             }
             issue(next, min(c + 2, last));
             decode(cur1);                          // chunk c + 1
