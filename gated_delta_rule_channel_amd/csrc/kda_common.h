@@ -381,7 +381,7 @@ struct PolSplit {
         u32x2 ew;
         ew[0] = ext4(r[0], r[1], r[2], r[3]);
         ew[1] = ext4(r[4], r[5], r[6], r[7]);
-        __builtin_nontemporal_store(hw, reinterpret_cast<u32x4*>(t) + 64 * which + lane);
+        reinterpret_cast<u32x4*>(t)[64 * which + lane] = hw;
         // half of every 16 B: the other wave of the pair writes the rest, merged in L2
         reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(t) + 2048)[2 * lane + which] = ew;
     }
@@ -419,7 +419,7 @@ struct PolSplit {
         bf16x8 x;
         x[0] = h[0]; x[1] = h[1]; x[2] = h[2]; x[3] = h[3];
         x[4] = l[0]; x[5] = l[1]; x[6] = l[2]; x[7] = l[3];
-        __builtin_nontemporal_store(x, reinterpret_cast<bf16x8*>(t) + lane);
+        reinterpret_cast<bf16x8*>(t)[lane] = x;
     }
     __device__ static __forceinline__ void split4(bf16x4& h, bf16x4& l, float a, float b, float c,
                                                   float d) {

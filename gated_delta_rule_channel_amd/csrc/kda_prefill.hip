@@ -174,7 +174,7 @@ template <typename T> struct In32;
 template <> struct In32<bf16> {
     u32x16 w;                                            // two bfloat16 per word
     __device__ __forceinline__ void load(int I, const bf16* p) {
-        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        const u32x4 x = *reinterpret_cast<const u32x4*>(p);
         w[4 * I] = x[0]; w[4 * I + 1] = x[1]; w[4 * I + 2] = x[2]; w[4 * I + 3] = x[3];
     }
     __device__ __forceinline__ void zero(int I) {
@@ -280,8 +280,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         const int row = 16 * I + m;
         if (cvalid && row < L) {
             const size_t off = (size_t)(t0 + row) * rowq + (size_t)h * DK + c0;
-            const floatx4 g0 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(g + off));
-            const floatx4 g1 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(g + off) + 1);
+            const floatx4 g0 = *reinterpret_cast<const floatx4*>(g + off);
+            const floatx4 g1 = *(reinterpret_cast<const floatx4*>(g + off) + 1);
             G[8 * I] = g0[0]; G[8 * I + 1] = g0[1]; G[8 * I + 2] = g0[2]; G[8 * I + 3] = g0[3];
             G[8 * I + 4] = g1[0]; G[8 * I + 5] = g1[1]; G[8 * I + 6] = g1[2]; G[8 * I + 7] = g1[3];
             K.load(I, k + off);
