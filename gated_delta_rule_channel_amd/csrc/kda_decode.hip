@@ -14,8 +14,9 @@
 // consecutive value columns (one 16-byte vector per state row) of rows
 // rs, rs + RS, ...; a wavefront therefore streams whole contiguous rows. The
 // column sums of v^ and r are reduced across rows with lane shuffles inside a
-// wavefront and through LDS across wavefronts. State loads and stores are
-// nontemporal: each state is touched once per step.
+// wavefront and through LDS across wavefronts. State stores are nontemporal
+// (each state is written once per step); plain loads measured faster than
+// nontemporal ones.
 #include "kda_common.h"
 
 namespace kda {
@@ -59,8 +60,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rs + RS * i;
-        // streamed once: nontemporal (no reuse in the caches)
-        const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(S + (size_t)r * DV) + cg);
+        const floatx4 t = reinterpret_cast<const floatx4*>(S + (size_t)r * DV)[cg];
         s[i] = make_float4(t[0], t[1], t[2], t[3]);
     }
     float4 vh = make_float4(0.f, 0.f, 0.f, 0.f);
