@@ -43,6 +43,8 @@
 // The in-chunk prefix sums are computed per 16-token block (log-space prefix
 // sums, as the page's "real Triton implementation" paragraph describes), and
 // cross-block factors come from block totals.
+#include <atomic>
+
 #include "kda_common.h"
 
 namespace kda {
@@ -150,7 +152,12 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
 // ------------------------------------------------------------------------------------------
 // prep kernel
 // ------------------------------------------------------------------------------------------
-// One workgroup (4 waves) per (chunk, head). Wave w owns the 32-channel slice
+// Persistent workgroups (4 waves, two per CU) walk the (chunk, head) tasks with a stride of
+// the grid size; consecutive workgroups take the heads of one chunk, so the tasks in flight
+// read neighbouring token rows. For bf16 input the next task's g, k, q and beta are copied
+// global -> LDS (direct-to-LDS loads, 16 B per lane) while the current task forms W and U,
+// into the LDS region that holds the A and T blocks earlier in the task, so a task starts
+// from LDS instead of waiting on HBM. Within a task, wave w owns the 32-channel slice
 // [32 w, 32 w + 32) of the keys for all 64 tokens, held in MFMA fragment layout: lane
 // (m, grp) holds token 16 I + m of every 16-token block I and the 8 channels
 // 32 w + 8 grp + e. In-chunk prefix sums are DPP scans across the 16 lanes of a row.
@@ -179,6 +186,9 @@ template <> struct In32<bf16> {
     }
     __device__ __forceinline__ void zero(int I) {
         w[4 * I] = 0u; w[4 * I + 1] = 0u; w[4 * I + 2] = 0u; w[4 * I + 3] = 0u;
+    }
+    __device__ __forceinline__ void set(int I, const u32x4& x) {
+        w[4 * I] = x[0]; w[4 * I + 1] = x[1]; w[4 * I + 2] = x[2]; w[4 * I + 3] = x[3];
     }
     __device__ __forceinline__ void get8(int I, float* o) const {
 #pragma unroll
@@ -220,6 +230,27 @@ template <> struct In32<float> {
     }
 };
 
+// Input staging: bf16 input stages g, k, q (64 KB per task) in LDS; fp32 input (96 KB)
+// loads them from global memory at the start of each task.
+template <typename TI> struct PrepStage { static constexpr int kBytes = 0; };
+template <> struct PrepStage<bf16> {
+    static constexpr int kBytes = 65536;
+    // byte offsets of wave w's 1 KB parts: g (block I, half), k (block I), q (block I)
+    __device__ static constexpr int g_off(int w, int I, int half) { return ((w * 4 + I) * 2 + half) * 1024; }
+    __device__ static constexpr int k_off(int w, int I) { return 32768 + (w * 4 + I) * 1024; }
+    __device__ static constexpr int q_off(int w, int I) { return 49152 + (w * 4 + I) * 1024; }
+};
+typedef __attribute__((address_space(3))) void* lds_ptr;
+// 16 (or 4) bytes per lane from global memory to LDS at dst + 16 lane (4 lane); dst is
+// wave-uniform. Completion is counted by vmcnt.
+__device__ __forceinline__ void lds_load16(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
 template <typename Pol>
 __device__ __forceinline__ typename Pol::Frag4 frag4_of(const floatx4& d) {
     typename Pol::Frag4 f;
@@ -232,428 +263,513 @@ template <typename TI, int DK, int DV>
 __global__ __launch_bounds__(256, 2) void prep_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
     const float* __restrict__ g, const TI* __restrict__ beta, float scale,
-    const int4* __restrict__ tab, int T, uint8_t* __restrict__ ws, int H) {
+    const int4* __restrict__ tab, int T, int nslots, uint8_t* __restrict__ ws, int H) {
     using Pol = typename PolOf<TI>::type;
     using Frag = typename Pol::Frag;
     using Frag4 = typename Pol::Frag4;
     using Ly = WsLayout<Pol::kPairBytes, DK, DV>;
+    using Stg = PrepStage<TI>;
     constexpr int NSL = DK >= 32 ? DK / 32 : 1;          // channel slices (32 wide, padded)
     constexpr int NVS = DV >= 32 ? DV / 32 : 1;          // value slices
     // lower 16x16 blocks, rows padded to 20 floats so that 16 lanes reading 4 floats of
-    // 16 different rows hit distinct LDS banks
-    __shared__ float sKK[10][16][20];                     // A_kk lower blocks
-    __shared__ float sQK[10][16][20];                     // A_qk lower blocks
-    __shared__ float sT[10][16][20];                      // T = (I + A_kk)^-1 lower blocks
+    // 16 different rows hit distinct LDS banks: A_kk, A_qk and T = (I + A_kk)^-1. The same
+    // region receives the next task's staged inputs once T' is formed.
+    constexpr int kABytes = 3 * 10 * 16 * 20 * 4;
+    constexpr int kRBytes = kABytes > Stg::kBytes ? kABytes : Stg::kBytes;
+    __shared__ __attribute__((aligned(16))) float sR[kRBytes / 4];
+    float (*const sKK)[16][20] = reinterpret_cast<float (*)[16][20]>(sR);
+    float (*const sQK)[16][20] = reinterpret_cast<float (*)[16][20]>(sR + 10 * 16 * 20);
+    float (*const sT)[16][20] = reinterpret_cast<float (*)[16][20]>(sR + 2 * 10 * 16 * 20);
+    uint8_t* const sRb = reinterpret_cast<uint8_t*>(sR);
     __shared__ float sBeta[64];
+    __shared__ unsigned sBetaRaw[64];                     // staged word holding beta of token t
     __shared__ float4 sCE[4][NSL * 8];                    // cumulative log-decay at block ends
     __shared__ Frag4 sTp[10][64];                         // T' = T diag(beta) as fragments
-
-    const int slot = blockIdx.x, h = blockIdx.y;
-    int t0, L;
-    if (tab) {                                            // packed sequences: chunk table
-        const int4 ci = tab[slot];
-        t0 = ci.x;
-        L = ci.y;
-    } else {                                              // B rows of T tokens
-        const int nck = (T + kChunk - 1) / kChunk, row = slot / nck, c = slot % nck;
-        t0 = row * T + kChunk * c;
-        L = T - kChunk * c < kChunk ? T - kChunk * c : kChunk;
-    }
-    if (L <= 0) return;                                   // uniform per workgroup
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = lane & 15, grp = lane >> 4;
     const size_t rowq = (size_t)H * DK, rowv = (size_t)H * DV;
-    uint8_t* blk = ws + ((size_t)slot * H + h) * Ly::BYTES;
-    float* gGend = reinterpret_cast<float*>(blk + Ly::GEND);
-
     const bool cs = wave < NSL;                  // this wave owns a channel slice
     const int c0 = 32 * wave + 8 * grp;          // first of this lane's 8 channels
     const bool cvalid = cs && c0 < DK;
+    const int ntasks = nslots * H;
 
-    // ---- loads: g, k, q of the slice for all 64 tokens; beta of the chunk to LDS ----
-    floatx32 G;
-    In32<TI> K, Q;
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        const int row = 16 * I + m;
-        if (cvalid && row < L) {
-            const size_t off = (size_t)(t0 + row) * rowq + (size_t)h * DK + c0;
-            const floatx4 g0 = *reinterpret_cast<const floatx4*>(g + off);
-            const floatx4 g1 = *(reinterpret_cast<const floatx4*>(g + off) + 1);
-            G[8 * I] = g0[0]; G[8 * I + 1] = g0[1]; G[8 * I + 2] = g0[2]; G[8 * I + 3] = g0[3];
-            G[8 * I + 4] = g1[0]; G[8 * I + 5] = g1[1]; G[8 * I + 6] = g1[2]; G[8 * I + 7] = g1[3];
-            K.load(I, k + off);
-            Q.load(I, q + off);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) G[8 * I + e] = 0.f;
-            K.zero(I);
-            Q.zero(I);
+    // token range of a chunk slot
+    auto chunk_of = [&](int slot, int& t0, int& L) {
+        if (tab) {                                        // packed sequences: chunk table
+            const int4 ci = tab[slot];
+            t0 = ci.x;
+            L = ci.y;
+        } else {                                          // B rows of T tokens
+            const int nck = (T + kChunk - 1) / kChunk, row = slot / nck, c = slot % nck;
+            t0 = row * T + kChunk * c;
+            L = T - kChunk * c < kChunk ? T - kChunk * c : kChunk;
         }
-    }
-    if (tid < 64) sBeta[tid] = tid < L ? to_f(beta[(size_t)(t0 + tid) * H + h]) : 0.f;
-    // zero the A accumulators while the loads are in flight
-    for (int idx = tid; idx < 10 * 16 * 20; idx += 256) {
-        (&sKK[0][0][0])[idx] = 0.f;
-        (&sQK[0][0][0])[idx] = 0.f;
-    }
-
-    // ---- block-local prefix sums (log2 units); the cumulative value at each block end goes
-    //      to LDS (all 16 lanes of a row hold it), the chunk total stays in registers ----
-    float gtot[8];
-    {
-        float ce[4][8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float acc = 0.f;
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                G[8 * I + e] = row_scan16(G[8 * I + e] * kLog2e);
-                acc += row_bcast<15>(G[8 * I + e]);
-                ce[I][e] = acc;
-            }
-            gtot[e] = acc;
-        }
-        if (cs && m == 0) {
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                sCE[I][2 * (c0 / 8)] = make_float4(ce[I][0], ce[I][1], ce[I][2], ce[I][3]);
-                sCE[I][2 * (c0 / 8) + 1] = make_float4(ce[I][4], ce[I][5], ce[I][6], ce[I][7]);
-            }
-        }
-    }
-    // the 8 cumulative values of this lane's channels at the end of block I
-    auto ce8 = [&](int I, float* o) {
-        const float4 a = sCE[I][2 * (c0 / 8)], b = sCE[I][2 * (c0 / 8) + 1];
-        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-        o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
     };
-    if (cvalid && m == 0) {
+    // issues the staged loads of a task (bf16 input only)
+    auto stage = [&](int t0, int L, int h) {
+        if constexpr (Stg::kBytes > 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) gGend[c0 + e] = fast_exp2(gtot[e]);
-    }
+            for (int I = 0; I < 4; ++I) {
+                const int row = 16 * I + m;
+                if (cvalid && row < L) {
+                    const size_t off = (size_t)(t0 + row) * rowq + (size_t)h * DK + c0;
+                    lds_load16(g + off, sRb + Stg::g_off(wave, I, 0));
+                    lds_load16(g + off + 4, sRb + Stg::g_off(wave, I, 1));
+                    lds_load16(k + off, sRb + Stg::k_off(wave, I));
+                    lds_load16(q + off, sRb + Stg::q_off(wave, I));
+                }
+            }
+            if (wave == 0 && lane < L) {
+                const size_t e = (size_t)(t0 + lane) * H + h;       // beta element index
+                lds_load4(reinterpret_cast<const unsigned*>(beta) + (e >> 1), sBetaRaw);
+            }
+        }
+    };
     // identity slices: Eid[hh] as a B operand maps K index 16 hh + n to column n
     Frag Eid[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int e = 0; e < 8; ++e) Eid[hh].set(e, (8 * grp + e == 16 * hh + m) ? 1.f : 0.f);
-    __syncthreads();                                    // A accumulators zeroed, beta in LDS
 
-    // ---- rotated pass over the row blocks: Qd, Kd^T, partial A blocks ----
+    bool staged = false;                                  // the task's inputs are in LDS
 #pragma unroll 1
-    for (int st = 0; st < 4; ++st) {
-        if (cs) {
-            const int I = (wave + st) & 3;                // wave-uniform
-            const int Ip = __builtin_amdgcn_readfirstlane(I > 0 ? I - 1 : 0);
-            const int row = 16 * I + m;
-            const float bi = sBeta[row];
-            float Gl[8], kk[8], qq[8], pf[8];
-            K.get8(I, kk);
-            Q.get8(I, qq);
-            ce8(Ip, pf);                                  // cumulative value before block I
+    for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
+        const int slot = task / H, h = task % H;
+        int t0, L;
+        chunk_of(slot, t0, L);
+        if (L <= 0) {                                         // unused slot (uniform)
+            staged = false;
+            continue;
+        }
+        uint8_t* blk = ws + ((size_t)slot * H + h) * Ly::BYTES;
+        float* gGend = reinterpret_cast<float*>(blk + Ly::GEND);
+
+        // ---- inputs: g, k, q of the slice for all 64 tokens; beta of the chunk to LDS ----
+        floatx32 G;
+        In32<TI> K, Q;
+        if constexpr (Stg::kBytes > 0) {
+            if (!staged) {
+                stage(t0, L, h);
+                wait_all_memory();
+            }
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int row = 16 * I + m;
+                if (cvalid && row < L) {
+                    const floatx4 g0 = reinterpret_cast<const floatx4*>(sRb + Stg::g_off(wave, I, 0))[lane];
+                    const floatx4 g1 = reinterpret_cast<const floatx4*>(sRb + Stg::g_off(wave, I, 1))[lane];
+                    G[8 * I] = g0[0]; G[8 * I + 1] = g0[1]; G[8 * I + 2] = g0[2]; G[8 * I + 3] = g0[3];
+                    G[8 * I + 4] = g1[0]; G[8 * I + 5] = g1[1]; G[8 * I + 6] = g1[2]; G[8 * I + 7] = g1[3];
+                    K.set(I, reinterpret_cast<const u32x4*>(sRb + Stg::k_off(wave, I))[lane]);
+                    Q.set(I, reinterpret_cast<const u32x4*>(sRb + Stg::q_off(wave, I))[lane]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) G[8 * I + e] = 0.f;
+                    K.zero(I);
+                    Q.zero(I);
+                }
+            }
+            if (tid < 64) {
+                const size_t e = (size_t)(t0 + tid) * H + h;
+                const unsigned w = sBetaRaw[tid];
+                sBeta[tid] = tid < L ? __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)) : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int row = 16 * I + m;
+                if (cvalid && row < L) {
+                    const size_t off = (size_t)(t0 + row) * rowq + (size_t)h * DK + c0;
+                    const floatx4 g0 = reinterpret_cast<const floatx4*>(g + off)[0];
+                    const floatx4 g1 = reinterpret_cast<const floatx4*>(g + off)[1];
+                    G[8 * I] = g0[0]; G[8 * I + 1] = g0[1]; G[8 * I + 2] = g0[2]; G[8 * I + 3] = g0[3];
+                    G[8 * I + 4] = g1[0]; G[8 * I + 5] = g1[1]; G[8 * I + 6] = g1[2]; G[8 * I + 7] = g1[3];
+                    K.load(I, k + off);
+                    Q.load(I, q + off);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) G[8 * I + e] = 0.f;
+                    K.zero(I);
+                    Q.zero(I);
+                }
+            }
+            if (tid < 64) sBeta[tid] = tid < L ? to_f(beta[(size_t)(t0 + tid) * H + h]) : 0.f;
+        }
+        // every wave has its inputs (and is past the previous task's reads of sCE): the staging
+        // region becomes the A accumulators
+        __syncthreads();
+        for (int idx = tid; idx < 10 * 16 * 20; idx += 256) {
+            (&sKK[0][0][0])[idx] = 0.f;
+            (&sQK[0][0][0])[idx] = 0.f;
+        }
+
+        // ---- block-local prefix sums (log2 units); the cumulative value at each block end goes
+        //      to LDS (all 16 lanes of a row hold it), the chunk total stays in registers ----
+        float gtot[8];
+        {
+            float ce[4][8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                Gl[e] = G[8 * I + e];
-                if (I == 0) pf[e] = 0.f;
+                float acc = 0.f;
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    G[8 * I + e] = row_scan16(G[8 * I + e] * kLog2e);
+                    acc += row_bcast<15>(G[8 * I + e]);
+                    ce[I][e] = acc;
+                }
+                gtot[e] = acc;
             }
-            // (a) chunk-start / chunk-end references: Qd and Kd^T to the workspace
-            {
-                Frag Kd;
-                float qdv[8];
+            if (cs && m == 0) {
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    sCE[I][2 * (c0 / 8)] = make_float4(ce[I][0], ce[I][1], ce[I][2], ce[I][3]);
+                    sCE[I][2 * (c0 / 8) + 1] = make_float4(ce[I][4], ce[I][5], ce[I][6], ce[I][7]);
+                }
+            }
+        }
+        // the 8 cumulative values of this lane's channels at the end of block I
+        auto ce8 = [&](int I, float* o) {
+            const float4 a = sCE[I][2 * (c0 / 8)], b = sCE[I][2 * (c0 / 8) + 1];
+            o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+            o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+        };
+        if (cvalid && m == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gGend[c0 + e] = fast_exp2(gtot[e]);
+        }
+        __syncthreads();                                    // A accumulators zeroed, beta in LDS
+
+        // ---- rotated pass over the row blocks: Qd, Kd^T, partial A blocks ----
+#pragma unroll 1
+        for (int st = 0; st < 4; ++st) {
+            if (cs) {
+                const int I = (wave + st) & 3;                // wave-uniform
+                const int Ip = __builtin_amdgcn_readfirstlane(I > 0 ? I - 1 : 0);
+                const int row = 16 * I + m;
+                const float bi = sBeta[row];
+                float Gl[8], kk[8], qq[8], pf[8];
+                K.get8(I, kk);
+                Q.get8(I, qq);
+                ce8(Ip, pf);                                  // cumulative value before block I
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float Gc = pf[e] + Gl[e];
-                    const float ec = fast_exp2(Gc), ed = fast_exp2(gtot[e] - Gc);
-                    qdv[e] = scale * qq[e] * ec;
-                    Kd.set(e, kk[e] * ed);
+                    Gl[e] = G[8 * I + e];
+                    if (I == 0) pf[e] = 0.f;
                 }
-                Pol::pair_store_vals(blk + Ly::QD + (I * Ly::NP + (wave >> 1)) * Ly::PT, lane,
-                                     wave & 1, qdv);
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    if (32 * wave + 16 * hh < DK) {
-                        floatx4 dk = {0.f, 0.f, 0.f, 0.f};
-                        Pol::mma_exact(dk, Kd, Eid[hh]);  // lane (channel n, grp): tokens 4 grp + r
-                        const int ct = 2 * wave + hh, ks = I >> 1;
-                        Pol::pair_store_quad(blk + Ly::KDT + ct * Ly::PT,
-                                             m + 16 * (2 * (I & 1) + (grp >> 1)), ks, grp & 1,
-                                             dk[0], dk[1], dk[2], dk[3]);
-                    }
-                }
-            }
-            // row operands with the block-start reference, exp(G_i - G_r) <= 1 (r = end of
-            // block I - 1): shared by the diagonal and the off-diagonal blocks of row I
-            Frag KA, QA;
-            bool far = false;                             // block decays beyond 2^120
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float ea = fast_exp2(Gl[e]);
-                KA.set(e, bi * kk[e] * ea);
-                QA.set(e, scale * qq[e] * ea);
-                far |= Gl[e] < -120.f;
-            }
-            // (b) diagonal block: block-start reference (column factor exp(G_r - G_j) <= 2^120),
-            //     else the midpoint of the block, else pairwise
-            {
-                floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
-                bool bad = false;
-                if (!__any(far)) {
-                    Frag KC;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) KC.set(e, kk[e] * fast_exp2(-Gl[e]));
-                    Pol::mma(akk, KC, KA);
-                    Pol::mma(aqk, KC, QA);
-                } else {
-                    Frag KE, QE, KR;
+                // (a) chunk-start / chunk-end references: Qd and Kd^T to the workspace
+                {
+                    Frag Kd;
+                    float qdv[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float x = Gl[e] - row_bcast<7>(Gl[e]);
-                        bad |= fabsf(x) > 120.f;
-                        const float e1 = fast_exp2(x), e2 = fast_exp2(-x);
-                        KE.set(e, bi * kk[e] * e1);
-                        QE.set(e, scale * qq[e] * e1);
-                        KR.set(e, kk[e] * e2);
+                        const float Gc = pf[e] + Gl[e];
+                        const float ec = fast_exp2(Gc), ed = fast_exp2(gtot[e] - Gc);
+                        qdv[e] = scale * qq[e] * ec;
+                        Kd.set(e, kk[e] * ed);
                     }
-                    if (!__any(bad)) {
-                        Pol::mma(akk, KR, KE);
-                        Pol::mma(aqk, KR, QE);
+                    Pol::pair_store_vals(blk + Ly::QD + (I * Ly::NP + (wave >> 1)) * Ly::PT, lane,
+                                         wave & 1, qdv);
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        if (32 * wave + 16 * hh < DK) {
+                            floatx4 dk = {0.f, 0.f, 0.f, 0.f};
+                            Pol::mma_exact(dk, Kd, Eid[hh]);  // lane (channel n, grp): tokens 4 grp + r
+                            const int ct = 2 * wave + hh, ks = I >> 1;
+                            Pol::pair_store_quad(blk + Ly::KDT + ct * Ly::PT,
+                                                 m + 16 * (2 * (I & 1) + (grp >> 1)), ks, grp & 1,
+                                                 dk[0], dk[1], dk[2], dk[3]);
+                        }
                     }
                 }
-                if (__any(bad)) {
-                    // exact pairwise sums over this slice: entry (i = m, j = jj)
-#pragma unroll 1
-                    for (int jj = 0; jj < 16; ++jj) {
-                        float skk = 0.f, sqk = 0.f;
-                        const int src = (lane & 48) | jj;
+                // row operands with the block-start reference, exp(G_i - G_r) <= 1 (r = end of
+                // block I - 1): shared by the diagonal and the off-diagonal blocks of row I
+                Frag KA, QA;
+                bool far = false;                             // block decays beyond 2^120
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float ea = fast_exp2(Gl[e]);
+                    KA.set(e, bi * kk[e] * ea);
+                    QA.set(e, scale * qq[e] * ea);
+                    far |= Gl[e] < -120.f;
+                }
+                // (b) diagonal block: block-start reference (column factor exp(G_r - G_j) <= 2^120),
+                //     else the midpoint of the block, else pairwise
+                {
+                    floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+                    bool bad = false;
+                    if (!__any(far)) {
+                        Frag KC;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) KC.set(e, kk[e] * fast_exp2(-Gl[e]));
+                        Pol::mma(akk, KC, KA);
+                        Pol::mma(aqk, KC, QA);
+                    } else {
+                        Frag KE, QE, KR;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const float Gj = __shfl(Gl[e], src);
-                            const float kj = __shfl(kk[e], src);
-                            const float d = jj <= m ? fast_exp2(Gl[e] - Gj) : 0.f;
-                            skk += kk[e] * kj * d;
-                            sqk += scale * qq[e] * kj * d;
+                            const float x = Gl[e] - row_bcast<7>(Gl[e]);
+                            bad |= fabsf(x) > 120.f;
+                            const float e1 = fast_exp2(x), e2 = fast_exp2(-x);
+                            KE.set(e, bi * kk[e] * e1);
+                            QE.set(e, scale * qq[e] * e1);
+                            KR.set(e, kk[e] * e2);
                         }
-                        skk += __shfl_xor(skk, 16);
-                        skk += __shfl_xor(skk, 32);
-                        sqk += __shfl_xor(sqk, 16);
-                        sqk += __shfl_xor(sqk, 32);
-                        if ((jj >> 2) == grp) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                if (r == (jj & 3)) { akk[r] = bi * skk; aqk[r] = sqk; }
+                        if (!__any(bad)) {
+                            Pol::mma(akk, KR, KE);
+                            Pol::mma(aqk, KR, QE);
                         }
                     }
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 4 * grp + r;
-                    if (!(j < m)) akk[r] = 0.f;
-                    if (!(j <= m)) aqk[r] = 0.f;
-                }
-                float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(I, I)][m][4 * grp]);
-                float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(I, I)][m][4 * grp]);
-                float4 a = *pk, c = *pq;
-                a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
-                c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
-                *pk = a;
-                *pq = c;
-            }
-            // (c) off-diagonal blocks J < I: reference at the end of block I - 1. The pair
-            //     (3, 0) is taken by the wave holding row block 0 in this step (that wave has
-            //     no other off-diagonal pair), which balances the steps; every pair still gets
-            //     one partial per wave and no two waves write one block in the same step.
-            // partial of pair (II, J) with row operands KA, QA of block II (pfI = cumulative
-            // value before block II)
-            auto offdiag = [&](int II, int J, const Frag& KA2, const Frag& QA2, const float* pfI) {
-                // k of block J decayed to the start of block II
-                const int Jp = __builtin_amdgcn_readfirstlane(J > 0 ? J - 1 : 0);
-                float kJ[8], ceJ[8];
-                K.get8(J, kJ);
-                ce8(Jp, ceJ);
-                Frag b;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float cj = J > 0 ? ceJ[e] : 0.f;
-                    b.set(e, kJ[e] * fast_exp2(pfI[e] - cj - G[8 * J + e]));
-                }
-                floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
-                Pol::mma(akk, b, KA2);
-                Pol::mma(aqk, b, QA2);
-                float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(II, J)][m][4 * grp]);
-                float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(II, J)][m][4 * grp]);
-                float4 a = *pk, c = *pq;
-                a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
-                c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
-                *pk = a;
-                *pq = c;
-            };
-            if (I > 0) {
+                    if (__any(bad)) {
+                        // exact pairwise sums over this slice: entry (i = m, j = jj)
 #pragma unroll 1
-                for (int J = I == 3 ? 1 : 0; J < I; ++J) offdiag(I, J, KA, QA, pf);
-            } else {
-                // row block 3 of this slice (static registers)
-                float k3[8], q3[8], pf3[8];
-                K.get8(3, k3);
-                Q.get8(3, q3);
-                ce8(2, pf3);
-                const float b3 = sBeta[48 + m];
-                Frag KA3, QA3;
+                        for (int jj = 0; jj < 16; ++jj) {
+                            float skk = 0.f, sqk = 0.f;
+                            const int src = (lane & 48) | jj;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float ea = fast_exp2(G[24 + e]);
-                    KA3.set(e, b3 * k3[e] * ea);
-                    QA3.set(e, scale * q3[e] * ea);
+                            for (int e = 0; e < 8; ++e) {
+                                const float Gj = __shfl(Gl[e], src);
+                                const float kj = __shfl(kk[e], src);
+                                const float d = jj <= m ? fast_exp2(Gl[e] - Gj) : 0.f;
+                                skk += kk[e] * kj * d;
+                                sqk += scale * qq[e] * kj * d;
+                            }
+                            skk += __shfl_xor(skk, 16);
+                            skk += __shfl_xor(skk, 32);
+                            sqk += __shfl_xor(sqk, 16);
+                            sqk += __shfl_xor(sqk, 32);
+                            if ((jj >> 2) == grp) {
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    if (r == (jj & 3)) { akk[r] = bi * skk; aqk[r] = sqk; }
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 4 * grp + r;
+                        if (!(j < m)) akk[r] = 0.f;
+                        if (!(j <= m)) aqk[r] = 0.f;
+                    }
+                    float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(I, I)][m][4 * grp]);
+                    float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(I, I)][m][4 * grp]);
+                    float4 a = *pk, c = *pq;
+                    a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
+                    c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
+                    *pk = a;
+                    *pq = c;
                 }
-                offdiag(3, 0, KA3, QA3, pf3);
+                // (c) off-diagonal blocks J < I: reference at the end of block I - 1. The pair
+                //     (3, 0) is taken by the wave holding row block 0 in this step (that wave has
+                //     no other off-diagonal pair), which balances the steps; every pair still gets
+                //     one partial per wave and no two waves write one block in the same step.
+                // partial of pair (II, J) with row operands KA, QA of block II (pfI = cumulative
+                // value before block II)
+                auto offdiag = [&](int II, int J, const Frag& KA2, const Frag& QA2, const float* pfI) {
+                    // k of block J decayed to the start of block II
+                    const int Jp = __builtin_amdgcn_readfirstlane(J > 0 ? J - 1 : 0);
+                    float kJ[8], ceJ[8];
+                    K.get8(J, kJ);
+                    ce8(Jp, ceJ);
+                    Frag b;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float cj = J > 0 ? ceJ[e] : 0.f;
+                        b.set(e, kJ[e] * fast_exp2(pfI[e] - cj - G[8 * J + e]));
+                    }
+                    floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+                    Pol::mma(akk, b, KA2);
+                    Pol::mma(aqk, b, QA2);
+                    float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(II, J)][m][4 * grp]);
+                    float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(II, J)][m][4 * grp]);
+                    float4 a = *pk, c = *pq;
+                    a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
+                    c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
+                    *pk = a;
+                    *pq = c;
+                };
+                if (I > 0) {
+#pragma unroll 1
+                    for (int J = I == 3 ? 1 : 0; J < I; ++J) offdiag(I, J, KA, QA, pf);
+                } else {
+                    // row block 3 of this slice (static registers)
+                    float k3[8], q3[8], pf3[8];
+                    K.get8(3, k3);
+                    Q.get8(3, q3);
+                    ce8(2, pf3);
+                    const float b3 = sBeta[48 + m];
+                    Frag KA3, QA3;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float ea = fast_exp2(G[24 + e]);
+                        KA3.set(e, b3 * k3[e] * ea);
+                        QA3.set(e, scale * q3[e] * ea);
+                    }
+                    offdiag(3, 0, KA3, QA3, pf3);
+                }
+            }
+            __syncthreads();
+        }
+
+        // ---- value slice of this wave (for U), loaded now so it lands during the inverse ----
+        const int vc0 = 32 * wave + 8 * grp;
+        const bool vvalid = wave < NVS && vc0 < DV;
+        In32<TI> V;
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const int row = 16 * I + m;
+            if (vvalid && row < L)
+                V.load(I, v + (size_t)(t0 + row) * rowv + (size_t)h * DV + vc0);
+            else
+                V.zero(I);
+        }
+        // A_qk fragment tiles of token tile tw = wave (upper blocks zero)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int J = 2 * s + (grp >> 1), jl = 8 * (grp & 1);
+            float a[8];
+            if (J <= wave) {
+                const float4 x0 = *reinterpret_cast<const float4*>(&sQK[tri_tile(wave, J)][m][jl]);
+                const float4 x1 = *reinterpret_cast<const float4*>(&sQK[tri_tile(wave, J)][m][jl + 4]);
+                a[0] = x0.x; a[1] = x0.y; a[2] = x0.z; a[3] = x0.w;
+                a[4] = x1.x; a[5] = x1.y; a[6] = x1.z; a[7] = x1.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] = 0.f;
+            }
+            Pol::pair_store_vals(blk + Ly::AQ + wave * Ly::PT, lane, s, a);
+        }
+
+        // ---- T = (I + A_kk)^-1: diagonal blocks by forward substitution (fp32) ----
+        if (lane < 16) {
+            const int I = wave, n = lane;
+            float x[16];
+#pragma unroll
+            for (int ii = 0; ii < 16; ++ii) {
+                float s = 0.f;
+#pragma unroll
+                for (int mm = 0; mm < ii; ++mm) s += sKK[tri_tile(I, I)][ii][mm] * x[mm];
+                x[ii] = (ii == n) ? 1.f : (ii > n ? -s : 0.f);
+            }
+#pragma unroll
+            for (int ii = 0; ii < 16; ++ii) sT[tri_tile(I, I)][ii][n] = x[ii];
+        }
+        __syncthreads();
+        // off-diagonal blocks, column block J = wave: T_IJ = -T_II sum_{M=J}^{I-1} A_IM T_MJ
+        {
+            const int J = wave;
+#pragma unroll 1
+            for (int I = J + 1; I < 4; ++I) {
+                floatx4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+                for (int M = J; M < I; ++M) {
+                    const float4 a = *reinterpret_cast<const float4*>(&sKK[tri_tile(I, M)][m][4 * grp]);
+                    const float* tb = &sT[tri_tile(M, J)][4 * grp][m];
+                    mma16_f32(Y, a, make_float4(tb[0], tb[20], tb[40], tb[60]));
+                }
+                // (T_II Y)^T = Y^T T_II^T: A = Y in its C layout, B = T_II read by rows
+                const float4 d = *reinterpret_cast<const float4*>(&sT[tri_tile(I, I)][m][4 * grp]);
+                floatx4 R = {0.f, 0.f, 0.f, 0.f};
+                mma16_f32(R, make_float4(Y[0], Y[1], Y[2], Y[3]), d);
+                *reinterpret_cast<float4*>(&sT[tri_tile(I, J)][m][4 * grp]) =
+                    make_float4(-R[0], -R[1], -R[2], -R[3]);
             }
         }
         __syncthreads();
-    }
 
-    // ---- value slice of this wave (for U), loaded now so it lands during the inverse ----
-    const int vc0 = 32 * wave + 8 * grp;
-    const bool vvalid = wave < NVS && vc0 < DV;
-    In32<TI> V;
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        const int row = 16 * I + m;
-        if (vvalid && row < L)
-            V.load(I, v + (size_t)(t0 + row) * rowv + (size_t)h * DV + vc0);
-        else
-            V.zero(I);
-    }
-    // A_qk fragment tiles of token tile tw = wave (upper blocks zero)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const int J = 2 * s + (grp >> 1), jl = 8 * (grp & 1);
-        float a[8];
-        if (J <= wave) {
-            const float4 x0 = *reinterpret_cast<const float4*>(&sQK[tri_tile(wave, J)][m][jl]);
-            const float4 x1 = *reinterpret_cast<const float4*>(&sQK[tri_tile(wave, J)][m][jl + 4]);
-            a[0] = x0.x; a[1] = x0.y; a[2] = x0.z; a[3] = x0.w;
-            a[4] = x1.x; a[5] = x1.y; a[6] = x1.z; a[7] = x1.w;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] = 0.f;
+        // ---- T' = T diag(beta) as operand fragments in LDS, converted once: lane (m, grp) of
+        //      tile (I, J) holds T'[16I + m][16J + 4grp + r] ----
+        for (int tile = wave; tile < 10; tile += 4) {
+            const int I = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+            const int J = tile - I * (I + 1) / 2;
+            const float4 t = *reinterpret_cast<const float4*>(&sT[tile][m][4 * grp]);
+            const float4 bb = *reinterpret_cast<const float4*>(&sBeta[16 * J + 4 * grp]);
+            Frag4 f;
+            f.set(0, t.x * bb.x); f.set(1, t.y * bb.y); f.set(2, t.z * bb.z); f.set(3, t.w * bb.w);
+            sTp[tile][lane] = f;
         }
-        Pol::pair_store_vals(blk + Ly::AQ + wave * Ly::PT, lane, s, a);
-    }
-
-    // ---- T = (I + A_kk)^-1: diagonal blocks by forward substitution (fp32) ----
-    if (lane < 16) {
-        const int I = wave, n = lane;
-        float x[16];
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) {
-            float s = 0.f;
-#pragma unroll
-            for (int mm = 0; mm < ii; ++mm) s += sKK[tri_tile(I, I)][ii][mm] * x[mm];
-            x[ii] = (ii == n) ? 1.f : (ii > n ? -s : 0.f);
-        }
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) sT[tri_tile(I, I)][ii][n] = x[ii];
-    }
-    __syncthreads();
-    // off-diagonal blocks, column block J = wave: T_IJ = -T_II sum_{M=J}^{I-1} A_IM T_MJ
-    {
-        const int J = wave;
-#pragma unroll 1
-        for (int I = J + 1; I < 4; ++I) {
-            floatx4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-            for (int M = J; M < I; ++M) {
-                const float4 a = *reinterpret_cast<const float4*>(&sKK[tri_tile(I, M)][m][4 * grp]);
-                const float* tb = &sT[tri_tile(M, J)][4 * grp][m];
-                mma16_f32(Y, a, make_float4(tb[0], tb[20], tb[40], tb[60]));
-            }
-            // (T_II Y)^T = Y^T T_II^T: A = Y in its C layout, B = T_II read by rows
-            const float4 d = *reinterpret_cast<const float4*>(&sT[tri_tile(I, I)][m][4 * grp]);
-            floatx4 R = {0.f, 0.f, 0.f, 0.f};
-            mma16_f32(R, make_float4(Y[0], Y[1], Y[2], Y[3]), d);
-            *reinterpret_cast<float4*>(&sT[tri_tile(I, J)][m][4 * grp]) =
-                make_float4(-R[0], -R[1], -R[2], -R[3]);
-        }
-    }
-    __syncthreads();
-
-    // ---- T' = T diag(beta) as operand fragments in LDS, converted once: lane (m, grp) of
-    //      tile (I, J) holds T'[16I + m][16J + 4grp + r] ----
-    for (int tile = wave; tile < 10; tile += 4) {
-        const int I = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
-        const int J = tile - I * (I + 1) / 2;
-        const float4 t = *reinterpret_cast<const float4*>(&sT[tile][m][4 * grp]);
-        const float4 bb = *reinterpret_cast<const float4*>(&sBeta[16 * J + 4 * grp]);
-        Frag4 f;
-        f.set(0, t.x * bb.x); f.set(1, t.y * bb.y); f.set(2, t.z * bb.z); f.set(3, t.w * bb.w);
-        sTp[tile][lane] = f;
-    }
-    __syncthreads();
-
-    // ---- W = T' (k exp G): W^T(channel half, I) = sum_{J <= I} (k exp G)_J^T T'_IJ^T; the
-    //      result lane (m = token, grp) holds W[16 I + m][4 channels]. The operand of block
-    //      J is built once and transposed for both 16-channel halves ----
-    if (cs) {
-        constexpr int NH = DK >= 32 ? 2 : 1;              // channel halves with data
-        floatx4 accW[2][4];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int I = 0; I < 4; ++I) accW[hh][I] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            float kJ[8], ceJ[8];
-            K.get8(J, kJ);
-            ce8(J > 0 ? J - 1 : 0, ceJ);
-            Frag kg;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float cj = J > 0 ? ceJ[e] : 0.f;
-                kg.set(e, kJ[e] * fast_exp2(cj + G[8 * J + e]));
-            }
-#pragma unroll
-            for (int hh = 0; hh < NH; ++hh) {
-                floatx4 t = {0.f, 0.f, 0.f, 0.f};
-                Pol::mma_exact(t, kg, Eid[hh]);           // lane (channel n, grp): tokens 4 grp + r
-                const Frag4 a = frag4_of<Pol>(t);
-#pragma unroll
-                for (int I = J; I < 4; ++I) Pol::mma16(accW[hh][I], a, sTp[tri_tile(I, J)][lane]);
+        __syncthreads();
+        // A and T are consumed (T' is in sTp): stage the next task's inputs into their region
+        staged = false;
+        if constexpr (Stg::kBytes > 0) {
+            const int nt = task + (int)gridDim.x;
+            if (nt < ntasks) {
+                int t0n, Ln;
+                chunk_of(nt / H, t0n, Ln);
+                if (Ln > 0) {
+                    stage(t0n, Ln, nt % H);
+                    staged = true;
+                }
             }
         }
+
+        // ---- W = T' (k exp G): W^T(channel half, I) = sum_{J <= I} (k exp G)_J^T T'_IJ^T; the
+        //      result lane (m = token, grp) holds W[16 I + m][4 channels]. The operand of block
+        //      J is built once and transposed for both 16-channel halves ----
+        if (cs) {
+            constexpr int NH = DK >= 32 ? 2 : 1;              // channel halves with data
+            floatx4 accW[2][4];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+            for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int I = 0; I < 4; ++I)
-                Pol::pair_store_quad(blk + Ly::W + (I * Ly::NP + (wave >> 1)) * Ly::PT,
-                                     m + 16 * (2 * hh + (grp >> 1)), wave & 1, grp & 1,
-                                     accW[hh][I][0], accW[hh][I][1], accW[hh][I][2], accW[hh][I][3]);
-    }
-    // ---- U = T' v: lane (m = value, grp) of tile (value tile, I) holds U[16 I + 4 grp + r][value] ----
-    if (wave < NVS) {
+                for (int I = 0; I < 4; ++I) accW[hh][I] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            if (32 * wave + 16 * hh < DV) {
-                floatx4 accU[4];
+            for (int J = 0; J < 4; ++J) {
+                float kJ[8], ceJ[8];
+                K.get8(J, kJ);
+                ce8(J > 0 ? J - 1 : 0, ceJ);
+                Frag kg;
 #pragma unroll
-                for (int I = 0; I < 4; ++I) accU[I] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int J = 0; J < 4; ++J) {
-                    Frag vb;
-                    V.frag(J, vb);
-                    floatx4 t = {0.f, 0.f, 0.f, 0.f};
-                    Pol::mma_copy(t, vb, Eid[hh]);        // lane (value n, grp): tokens 4 grp + r
-                    const Frag4 b = frag4_of<Pol>(t);
-#pragma unroll
-                    for (int I = J; I < 4; ++I) Pol::mma16_exact(accU[I], sTp[tri_tile(I, J)][lane], b);
+                for (int e = 0; e < 8; ++e) {
+                    const float cj = J > 0 ? ceJ[e] : 0.f;
+                    kg.set(e, kJ[e] * fast_exp2(cj + G[8 * J + e]));
                 }
 #pragma unroll
+                for (int hh = 0; hh < NH; ++hh) {
+                    floatx4 t = {0.f, 0.f, 0.f, 0.f};
+                    Pol::mma_exact(t, kg, Eid[hh]);           // lane (channel n, grp): tokens 4 grp + r
+                    const Frag4 a = frag4_of<Pol>(t);
+#pragma unroll
+                    for (int I = J; I < 4; ++I) Pol::mma16(accW[hh][I], a, sTp[tri_tile(I, J)][lane]);
+                }
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
                 for (int I = 0; I < 4; ++I)
-                    Pol::quad_store(blk + Ly::U + ((2 * wave + hh) * 4 + I) * Ly::QT, lane,
-                                    accU[I][0], accU[I][1], accU[I][2], accU[I][3]);
+                    Pol::pair_store_quad(blk + Ly::W + (I * Ly::NP + (wave >> 1)) * Ly::PT,
+                                         m + 16 * (2 * hh + (grp >> 1)), wave & 1, grp & 1,
+                                         accW[hh][I][0], accW[hh][I][1], accW[hh][I][2], accW[hh][I][3]);
+        }
+        // ---- U = T' v: lane (m = value, grp) of tile (value tile, I) holds U[16 I + 4 grp + r][value] ----
+        if (wave < NVS) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                if (32 * wave + 16 * hh < DV) {
+                    floatx4 accU[4];
+#pragma unroll
+                    for (int I = 0; I < 4; ++I) accU[I] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int J = 0; J < 4; ++J) {
+                        Frag vb;
+                        V.frag(J, vb);
+                        floatx4 t = {0.f, 0.f, 0.f, 0.f};
+                        Pol::mma_copy(t, vb, Eid[hh]);        // lane (value n, grp): tokens 4 grp + r
+                        const Frag4 b = frag4_of<Pol>(t);
+#pragma unroll
+                        for (int I = J; I < 4; ++I) Pol::mma16_exact(accU[I], sTp[tri_tile(I, J)][lane], b);
+                    }
+#pragma unroll
+                    for (int I = 0; I < 4; ++I)
+                        Pol::quad_store(blk + Ly::U + ((2 * wave + hh) * 4 + I) * Ly::QT, lane,
+                                        accU[I][0], accU[I][1], accU[I][2], accU[I][3]);
+                }
             }
         }
+        // this wave's staged loads have landed before it reads them in the next task
+        if (staged) wait_all_memory();
     }
 }
 
@@ -1019,15 +1135,34 @@ hipError_t launch_chunk_map(const int32_t* cu, int N, int T, int max_slots, void
     return hipGetLastError();
 }
 
+// compute units of the current device (the prep kernel keeps two workgroups on each)
+static hipError_t current_cu_count(int& n) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64 && (n = cache[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n <= 0) return hipErrorInvalidDevice;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return hipSuccess;
+}
+
 template <typename TI, typename TO, int DK, int DV>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const float* g,
                                    const void* beta, float scale, const float* h0, float* ht,
                                    void* o, const int32_t* cu, int T, const void* tab,
                                    const int32_t* seq_off, uint8_t* blocks, int N, int H,
                                    int max_slots, hipStream_t s) {
-    hipLaunchKernelGGL((prep_kernel<TI, DK, DV>), dim3(max_slots, H), dim3(256), 0, s,
+    int cu_count = 0;
+    hipError_t ec = current_cu_count(cu_count);
+    if (ec != hipSuccess) return ec;
+    const long long ntasks = (long long)max_slots * H;
+    const long long grid = ntasks < 2LL * cu_count ? ntasks : 2LL * cu_count;
+    hipLaunchKernelGGL((prep_kernel<TI, DK, DV>), dim3((unsigned)grid), dim3(256), 0, s,
                        (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
-                       (const int4*)tab, T, blocks, H);
+                       (const int4*)tab, T, max_slots, blocks, H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int BV = DV >= 32 ? 32 : DV;
