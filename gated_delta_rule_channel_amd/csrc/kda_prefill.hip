@@ -35,11 +35,12 @@
 // each bounded by 2^120 (in log2 units x = G log2 e), so nothing overflows or
 // loses the range of float32/bfloat16:
 //  * off-diagonal 16x16 blocks (row block I > column block J): exp(G_i - G_r)
-//    with r the end of block I-1 (<= 1) times exp(G_r - G_j) (<= 1), the
-//    latter split as exp(G_end(J) - G_j) * exp(G_r - G_end(J));
-//  * diagonal 16x16 blocks: exp(G_i - G_m) * exp(G_m - G_j) with m the 8th
-//    row of the block; if some |G_i - G_m| exceeds 120 (log2 units) in the
-//    block, that block is computed pairwise instead (exp2 of each difference).
+//    with r the last token before block I (<= 1) times exp(G_r - G_j) (<= 1);
+//  * diagonal 16x16 blocks: the same reference r when no channel decays by
+//    more than 2^120 inside the block (the column factor exp(G_r - G_j) is then
+//    at most 2^120); else the block's 8th row m, exp(G_i - G_m) exp(G_m - G_j),
+//    when every |G_i - G_m| is within 120; else pairwise (exp2 of each
+//    difference).
 // The in-chunk prefix sums are computed per 16-token block (log-space prefix
 // sums, as the page's "real Triton implementation" paragraph describes), and
 // cross-block factors come from block totals.
