@@ -23,6 +23,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -60,15 +61,23 @@ def prefill_flops(T, H, Dk, Dv, C=64):
     return per_chunk * H * (T // C)
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank space, so that comment edits keep the hash."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernels_source_hash():
-    """sha256 over the kernel sources and build script (counter figures are tied to it)."""
+    """sha256 over the kernel sources and build script, comments and spacing removed (the
+    counter figures are tied to the code they were taken on)."""
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "gated_delta_rule_channel_amd")
     files = sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, "r", encoding="utf-8", errors="replace") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
