@@ -205,21 +205,6 @@ struct PolF32 {
                                                            float b, float c, float d) {
         reinterpret_cast<float4*>(t)[64 * half + lane] = make_float4(a, b, c, d);
     }
-    // quad tiles (1 KB): four elements per lane, 16 B
-    __device__ static __forceinline__ void quad_store(void* t, int lane, float a, float b, float c,
-                                                      float d) {
-        reinterpret_cast<float4*>(t)[lane] = make_float4(a, b, c, d);
-    }
-    // 4 stored elements kept raw until use (prefetch buffers)
-    struct Raw4 { float4 v; };
-    __device__ static __forceinline__ void load4raw(Raw4& r, const Store* base, size_t i,
-                                                    size_t /*ps*/) {
-        r.v = *reinterpret_cast<const float4*>(base + i);
-    }
-    __device__ static __forceinline__ float4 raw4f(const Raw4& r) { return r.v; }
-    __device__ static __forceinline__ void quad_load(Raw4& r, const void* t, int lane) {
-        r.v = reinterpret_cast<const float4*>(t)[lane];
-    }
     // product with b exact in the leading part (same as mma16 in fp32)
     __device__ static __forceinline__ void mma16_exact(floatx4& acc, const Frag4& a, const Frag4& b) {
         mma16(acc, a, b);
@@ -352,15 +337,19 @@ struct PolSplit {
         r.hi = reinterpret_cast<const bf16x8*>(t)[lane];
         r.ext = reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(t) + 1024)[lane];
     }
-    // hi as stored; lo = (hi with its extension byte) - hi, exact in bfloat16
+    // hi as stored; lo = (hi with its extension byte) - hi, exact in bfloat16. The two
+    // 24-bit values of a word pair are assembled with one byte permute each (v_perm_b32:
+    // bytes 4..7 select from the hi word, 0..3 from the extension word, 0x0c gives zero).
     __device__ static __forceinline__ void tile_decode(Frag& f, const Tile& r) {
         f.hi = r.hi;
         const u32x4 w = __builtin_bit_cast(u32x4, r.hi);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const unsigned e = r.ext[p >> 1] >> (16 * (p & 1));
+            const unsigned e = r.ext[p >> 1];
+            const unsigned b = 2u * (p & 1);               // byte of element 2p in e
+            const unsigned x0 = __builtin_amdgcn_perm(w[p], e, 0x0504000cu | (b << 8));
+            const unsigned x1 = __builtin_amdgcn_perm(w[p], e, 0x0706000cu | ((b + 1) << 8));
             const unsigned h0 = w[p] << 16, h1 = w[p] & 0xffff0000u;
-            const unsigned x0 = h0 | ((e & 0xffu) << 8), x1 = h1 | (e & 0xff00u);
             f.lo[2 * p] = (bf16)(__uint_as_float(x0) - __uint_as_float(h0));
             f.lo[2 * p + 1] = (bf16)(__uint_as_float(x1) - __uint_as_float(h1));
         }
@@ -410,37 +399,6 @@ struct PolSplit {
         t.ext[0] = r.ext[2 * W];
         t.ext[1] = r.ext[2 * W + 1];
         tile_decode(f, t);
-    }
-    // quad tiles (1 KB): four elements per lane as hi (8 B) then lo (8 B)
-    __device__ static __forceinline__ void quad_store(void* t, int lane, float a, float b, float c,
-                                                      float d) {
-        bf16x4 h, l;
-        split4(h, l, a, b, c, d);
-        bf16x8 x;
-        x[0] = h[0]; x[1] = h[1]; x[2] = h[2]; x[3] = h[3];
-        x[4] = l[0]; x[5] = l[1]; x[6] = l[2]; x[7] = l[3];
-        reinterpret_cast<bf16x8*>(t)[lane] = x;
-    }
-    __device__ static __forceinline__ void split4(bf16x4& h, bf16x4& l, float a, float b, float c,
-                                                  float d) {
-        h[0] = (bf16)a; h[1] = (bf16)b; h[2] = (bf16)c; h[3] = (bf16)d;
-        l[0] = (bf16)(a - (float)h[0]); l[1] = (bf16)(b - (float)h[1]);
-        l[2] = (bf16)(c - (float)h[2]); l[3] = (bf16)(d - (float)h[3]);
-    }
-    struct Raw4 { bf16x4 h, l; };
-    __device__ static __forceinline__ void load4raw(Raw4& r, const Store* base, size_t i,
-                                                    size_t ps) {
-        r.h = *reinterpret_cast<const bf16x4*>(base + i);
-        r.l = *reinterpret_cast<const bf16x4*>(base + ps + i);
-    }
-    __device__ static __forceinline__ float4 raw4f(const Raw4& r) {
-        return make_float4((float)r.h[0] + (float)r.l[0], (float)r.h[1] + (float)r.l[1],
-                           (float)r.h[2] + (float)r.l[2], (float)r.h[3] + (float)r.l[3]);
-    }
-    __device__ static __forceinline__ void quad_load(Raw4& r, const void* t, int lane) {
-        const bf16x8 x = reinterpret_cast<const bf16x8*>(t)[lane];
-        r.h = __builtin_shufflevector(x, x, 0, 1, 2, 3);
-        r.l = __builtin_shufflevector(x, x, 4, 5, 6, 7);
     }
     // product with b exact in bfloat16 (b.lo == 0): two MFMAs
     __device__ static __forceinline__ void mma16_exact(floatx4& acc, const Frag4& a, const Frag4& b) {

@@ -58,13 +58,13 @@ namespace kda {
 // wave reads 1 KB of consecutive bytes (16 B per lane). Fragments (8 elements per lane) are
 // stored in pairs (a, b): PolSplit, 3 KB: the hi values of a, of b, then the extension bytes
 // of both (x rounded to 24 bits = bfloat16 hi + 1 byte, 16 significant bits); PolF32, 4 KB:
-// two fp32 tiles. Quad tiles (1 KB) hold 4 elements per lane as bf16 hi then lo (PolSplit)
-// or 4 floats. With lane l = m + 16 grp:
+// two fp32 tiles. U tiles (1 KB) hold 4 fp32 values per lane (U is an addend of E, not an
+// MFMA operand). With lane l = m + 16 grp:
 //  W, Qd  pairs [token tile tw][channel steps (2p, 2p+1)]: row 16 tw + m, channels
 //         32 kap + 8 grp + e (zero past Dk);
 //  Kd^T   pairs [channel tile ct][token halves (0, 1)]: channel 16 ct + m, tokens
 //         32 ks + 8 grp + e;
-//  U      quad tiles [value tile vt][token tile tw]: tokens 16 tw + 4 grp + r, value 16 vt + m;
+//  U      tiles [value tile vt][token tile tw]: tokens 16 tw + 4 grp + r, value 16 vt + m;
 //  A_qk   pairs [token tile tw][column halves (0, 1)]: row 16 tw + m, columns 32 s + 8 grp + e;
 //  exp(G_end) float [Dk].
 __host__ __device__ constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -83,7 +83,7 @@ struct WsLayout {
     static constexpr int NCT = DK / 16;                  // 16-channel tiles
     static constexpr int NVT = DV / 16;                  // 16-value tiles
     static constexpr size_t PT = PTB;                    // pair tile
-    static constexpr size_t QT = 1024;                   // quad tile
+    static constexpr size_t QT = 1024;                   // U tile
     static constexpr size_t W = 0;
     static constexpr size_t QD = W + 4 * NP * PT;
     static constexpr size_t KDT = QD + 4 * NP * PT;
@@ -764,8 +764,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                     }
 #pragma unroll
                     for (int I = 0; I < 4; ++I)
-                        Pol::quad_store(blk + Ly::U + ((2 * wave + hh) * 4 + I) * Ly::QT, lane,
-                                        accU[I][0], accU[I][1], accU[I][2], accU[I][3]);
+                        reinterpret_cast<float4*>(blk + Ly::U + ((2 * wave + hh) * 4 + I) * Ly::QT)[lane] =
+                            make_float4(accU[I][0], accU[I][1], accU[I][2], accU[I][3]);
                 }
             }
         }
@@ -895,7 +895,7 @@ __global__ __launch_bounds__(768) void state_kernel(
         //      (phase B). For O, lane (n = token, grp) holds values 16 vr + 4 grp + r ----
         struct Raw {
             Pair w[NP];
-            typename Pol::Raw4 u[NVT];
+            float4 u[NVT];
             Pair a;
         };
         Raw R0, R1;                                // raw operands of two later chunks
@@ -909,14 +909,14 @@ __global__ __launch_bounds__(768) void state_kernel(
                 Pol::pair_load(r.w[p], blk + Ly::W + (tw * NP + p) * Ly::PT, lane);
 #pragma unroll
             for (int vr = 0; vr < NVT; ++vr)
-                Pol::quad_load(r.u[vr], blk + Ly::U + ((v0 / 16 + vr) * 4 + tw) * Ly::QT, lane);
+                r.u[vr] = reinterpret_cast<const float4*>(blk + Ly::U + ((v0 / 16 + vr) * 4 + tw) * Ly::QT)[lane];
             Pol::pair_load(r.a, blk + Ly::AQ + tw * Ly::PT, lane);
             issue_fence();
         };
         auto decode = [&](const Raw& r) {
             decode_pairs<Pol, KS, NP>(wd, r.w);
 #pragma unroll
-            for (int vr = 0; vr < NVT; ++vr) ud[vr] = Pol::raw4f(r.u[vr]);
+            for (int vr = 0; vr < NVT; ++vr) ud[vr] = r.u[vr];
 #pragma unroll
             for (int kap = 0; kap < KS; ++kap) wd[kap].pin_regs();
 #pragma unroll
