@@ -780,10 +780,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
 // One workgroup of 12 waves per (sequence, head, 32-column value tile), in three roles of
 // four waves. Each chunk runs in two phases separated by workgroup barriers:
 //   phase A (S_c published): E role (token tile w)  E = U - W S_c      -> LDS
-//                            O role (token tile w)  Qd S_c             -> LDS
+//                            O role (token tile w)  Qd S_c             (registers)
 //   phase B (E published):   S role (channel tiles) S_{c+1} = Diag(exp G_end) S_c + Kd^T E
 //                                                   -> LDS operand copy, fp32 in registers
-//                            E role                 O = Qd S_c + A_qk E, write o
+//                            O role                 O = Qd S_c + A_qk E, write o
 // so the serial chain of a chunk is one product per phase, and every role decodes the next
 // chunk's operands and issues later chunks' loads while it is off the chain. The S role
 // keeps S in fp32 MFMA accumulators for the whole sequence. All reads of S_c and E happen
@@ -829,7 +829,6 @@ __global__ __launch_bounds__(768) void state_kernel(
     constexpr int P = Pol::kPlanes;
     __shared__ St SLs[P][BV][Sh::SST];     // operand copy of S [value][channel]
     __shared__ St ELs[P][BV][Sh::EST];     // E [value][token]
-    __shared__ float4 OLs[4][NVT][64];     // Qd S per token tile, in the O lane layout
     __shared__ float4 sGd[DK / 4];         // exp(G_end) of the chunk in phase B
     St* const SL = &SLs[0][0][0];
     St* const EL = &ELs[0][0][0];
@@ -891,17 +890,14 @@ __global__ __launch_bounds__(768) void state_kernel(
     if (c_beg >= c_end) {
         // empty sequence: the state passes through
     } else if (role == 0) {
-        // ---- E role: E = U - W S (phase A); O = (Qd S from LDS) + A_qk E and the output
-        //      (phase B). For O, lane (n = token, grp) holds values 16 vr + 4 grp + r ----
+        // ---- E role: E = U - W S (phase A); loads and decodes W and U (phase B) ----
         struct Raw {
             Pair w[NP];
             float4 u[NVT];
-            Pair a;
         };
         Raw R0, R1;                                // raw operands of two later chunks
         Frag wd[KS];                               // decoded W of the current chunk
         float4 ud[NVT];
-        const int nks = tw < 2 ? 1 : 2;            // nonzero column halves of A_qk rows
         auto issue = [&](Raw& r, int c) {
             const uint8_t* blk = block(c);
 #pragma unroll
@@ -910,7 +906,6 @@ __global__ __launch_bounds__(768) void state_kernel(
 #pragma unroll
             for (int vr = 0; vr < NVT; ++vr)
                 r.u[vr] = reinterpret_cast<const float4*>(blk + Ly::U + ((v0 / 16 + vr) * 4 + tw) * Ly::QT)[lane];
-            Pol::pair_load(r.a, blk + Ly::AQ + tw * Ly::PT, lane);
             issue_fence();
         };
         auto decode = [&](const Raw& r) {
@@ -922,8 +917,7 @@ __global__ __launch_bounds__(768) void state_kernel(
 #pragma unroll
             for (int vr = 0; vr < NVT; ++vr) pin(ud[vr]);
         };
-        // one chunk; `next` holds this chunk's raw operands (its A_qk is still read) and
-        // receives chunk c + 2's loads; `cur1` holds chunk c + 1's
+        // one chunk; `next` receives chunk c + 2's loads; `cur1` holds chunk c + 1's
         auto chunk = [&](int c, Raw& next, const Raw& cur1) {
             floatx4 acc[NVT];
 #pragma unroll
@@ -943,35 +937,7 @@ __global__ __launch_bounds__(768) void state_kernel(
                 Pol::store4(EL, (size_t)(16 * vr + m) * Sh::EST + 16 * tw + 4 * grp, psE,
                             ud[vr].x - acc[vr][0], ud[vr].y - acc[vr][1],
                             ud[vr].z - acc[vr][2], ud[vr].w - acc[vr][3]);
-            __syncthreads();                       // phase B: E and Qd S published
-#pragma unroll
-            for (int vr = 0; vr < NVT; ++vr) {
-                const float4 x = OLs[tw][vr][lane];
-                acc[vr] = floatx4{x.x, x.y, x.z, x.w};
-            }
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                if (s2 < nks) {
-                    Frag aq;
-                    if (s2) Pol::template pair_decode<1>(aq, next.a);
-                    else Pol::template pair_decode<0>(aq, next.a);
-#pragma unroll
-                    for (int vr = 0; vr < NVT; ++vr) {
-                        Frag bE;
-                        Pol::load(bE, EL, (size_t)(16 * vr + m) * Sh::EST + 32 * s2 + 8 * grp, psE);
-                        Pol::mma(acc[vr], bE, aq);
-                    }
-                }
-            }
-            const int t0 = s_beg + kChunk * (c - c_beg);
-            const int len = s_end - t0 < kChunk ? s_end - t0 : kChunk;
-            const int tok = 16 * tw + m;
-            if (tok < len) {
-                TO* orow = o + (size_t)(t0 + tok) * rowo + (size_t)h * DV + v0 + 4 * grp;
-#pragma unroll
-                for (int vr = 0; vr < NVT; ++vr)
-                    store4(orow + 16 * vr, acc[vr][0], acc[vr][1], acc[vr][2], acc[vr][3]);
-            }
+            __syncthreads();                       // phase B: E published
             issue(next, min(c + 2, last));
             decode(cur1);                          // chunk c + 1
             __syncthreads();                       // phase A: S_{c+1} published
@@ -1062,18 +1028,21 @@ __global__ __launch_bounds__(768) void state_kernel(
         }
         if (c < c_end) chunk(c, R0, R1);
     } else {
-        // ---- O role: Qd S_c (phase A) into LDS for the E role; lane (n = token, grp)
-        //      holds values 16 vr + 4 grp + r ----
+        // ---- O role: O = Qd S_c (phase A, kept in registers) + A_qk E (phase B), then the
+        //      output; lane (n = token, grp) holds values 16 vr + 4 grp + r ----
         struct Raw {
             Pair q[NP];
+            Pair a;
         };
-        Raw R0, R1;                                // raw Qd of two later chunks
-        Frag qd[KS];                               // decoded, current chunk
+        Raw R0, R1;                                // raw Qd and A_qk of two later chunks
+        Frag qd[KS];                               // decoded Qd, current chunk
+        const int nks = tw < 2 ? 1 : 2;            // nonzero column halves of A_qk rows
         auto issue = [&](Raw& r, int c) {
             const uint8_t* blk = block(c);
 #pragma unroll
             for (int p = 0; p < NP; ++p)
                 Pol::pair_load(r.q[p], blk + Ly::QD + (tw * NP + p) * Ly::PT, lane);
+            Pol::pair_load(r.a, blk + Ly::AQ + tw * Ly::PT, lane);
             issue_fence();
         };
         auto decode = [&](const Raw& r) {
@@ -1081,23 +1050,45 @@ __global__ __launch_bounds__(768) void state_kernel(
 #pragma unroll
             for (int kap = 0; kap < KS; ++kap) qd[kap].pin_regs();
         };
+        // one chunk; `next` holds this chunk's raw operands (its A_qk is still read) and
+        // receives chunk c + 2's loads; `cur1` holds chunk c + 1's
         auto chunk = [&](int c, Raw& next, const Raw& cur1) {
-            floatx4 accO[NVT];
+            floatx4 acc[NVT];
 #pragma unroll
-            for (int vr = 0; vr < NVT; ++vr) accO[vr] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int vr = 0; vr < NVT; ++vr) acc[vr] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kap = 0; kap < KS; ++kap) {
 #pragma unroll
                 for (int vr = 0; vr < NVT; ++vr) {
                     Frag bS;
                     Pol::load(bS, SL, (size_t)(16 * vr + m) * Sh::SST + 32 * kap + 8 * grp, psS);
-                    Pol::mma(accO[vr], bS, qd[kap]);
+                    Pol::mma(acc[vr], bS, qd[kap]);
                 }
             }
+            __syncthreads();                       // phase B: E published
 #pragma unroll
-            for (int vr = 0; vr < NVT; ++vr)
-                OLs[tw][vr][lane] = make_float4(accO[vr][0], accO[vr][1], accO[vr][2], accO[vr][3]);
-            __syncthreads();                       // phase B: E and Qd S published
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (s2 < nks) {
+                    Frag aq;
+                    if (s2) Pol::template pair_decode<1>(aq, next.a);
+                    else Pol::template pair_decode<0>(aq, next.a);
+#pragma unroll
+                    for (int vr = 0; vr < NVT; ++vr) {
+                        Frag bE;
+                        Pol::load(bE, EL, (size_t)(16 * vr + m) * Sh::EST + 32 * s2 + 8 * grp, psE);
+                        Pol::mma(acc[vr], bE, aq);
+                    }
+                }
+            }
+            const int t0 = s_beg + kChunk * (c - c_beg);
+            const int len = s_end - t0 < kChunk ? s_end - t0 : kChunk;
+            const int tok = 16 * tw + m;
+            if (tok < len) {
+                TO* orow = o + (size_t)(t0 + tok) * rowo + (size_t)h * DV + v0 + 4 * grp;
+#pragma unroll
+                for (int vr = 0; vr < NVT; ++vr)
+                    store4(orow + 16 * vr, acc[vr][0], acc[vr][1], acc[vr][2], acc[vr][3]);
+            }
             issue(next, min(c + 2, last));
             decode(cur1);                          // chunk c + 1
             __syncthreads();                       // phase A: S_{c+1} published
