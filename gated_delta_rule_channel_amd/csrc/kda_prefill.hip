@@ -1037,12 +1037,17 @@ __global__ __launch_bounds__(768) void state_kernel(
         Raw R0, R1;                                // raw Qd and A_qk of two later chunks
         Frag qd[KS];                               // decoded Qd, current chunk
         const int nks = tw < 2 ? 1 : 2;            // nonzero column halves of A_qk rows
-        auto issue = [&](Raw& r, int c) {
+        // Qd loads are issued in phase A (after Qd S), A_qk loads in phase B (after A_qk E),
+        // which spreads the workgroup's load issue over both phases
+        auto issue_q = [&](Raw& r, int c) {
             const uint8_t* blk = block(c);
 #pragma unroll
             for (int p = 0; p < NP; ++p)
                 Pol::pair_load(r.q[p], blk + Ly::QD + (tw * NP + p) * Ly::PT, lane);
-            Pol::pair_load(r.a, blk + Ly::AQ + tw * Ly::PT, lane);
+            issue_fence();
+        };
+        auto issue_a = [&](Raw& r, int c) {
+            Pol::pair_load(r.a, block(c) + Ly::AQ + tw * Ly::PT, lane);
             issue_fence();
         };
         auto decode = [&](const Raw& r) {
@@ -1065,6 +1070,7 @@ __global__ __launch_bounds__(768) void state_kernel(
                     Pol::mma(acc[vr], bS, qd[kap]);
                 }
             }
+            issue_q(next, min(c + 2, last));       // this chunk's Qd is decoded and used
             __syncthreads();                       // phase B: E published
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
@@ -1089,12 +1095,14 @@ __global__ __launch_bounds__(768) void state_kernel(
                 for (int vr = 0; vr < NVT; ++vr)
                     store4(orow + 16 * vr, acc[vr][0], acc[vr][1], acc[vr][2], acc[vr][3]);
             }
-            issue(next, min(c + 2, last));
+            issue_a(next, min(c + 2, last));
             decode(cur1);                          // chunk c + 1
             __syncthreads();                       // phase A: S_{c+1} published
         };
-        issue(R0, c_beg);
-        issue(R1, min(c_beg + 1, last));
+        issue_q(R0, c_beg);
+        issue_a(R0, c_beg);
+        issue_q(R1, min(c_beg + 1, last));
+        issue_a(R1, min(c_beg + 1, last));
         decode(R0);
         int c = c_beg;
 #pragma unroll 1
