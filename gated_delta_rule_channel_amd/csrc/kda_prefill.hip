@@ -643,19 +643,29 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             Pol::pair_store_vals(blk + Ly::AQ + wave * Ly::PT, lane, s, a);
         }
 
-        // ---- T = (I + A_kk)^-1: diagonal blocks by forward substitution (fp32) ----
-        if (lane < 16) {
-            const int I = wave, n = lane;
-            float x[16];
+        // ---- T = (I + A_kk)^-1: diagonal blocks by forward substitution (fp32). Wave I solves
+        //      block (I, I) with all 64 lanes: lane 4 j + q carries column j, and the dot
+        //      product of row i is split over the quad (lane q takes columns 4q .. 4q + 3 of A's
+        //      row, whose entries on and above the diagonal are zero) and summed with two quad
+        //      permutes, so a row costs four FMAs and two adds on the serial path ----
+        {
+            const int I = wave, j = lane >> 2, q = lane & 3;
+            const float* arow = &sKK[tri_tile(I, I)][0][4 * q];
+            float xs[4] = {0.f, 0.f, 0.f, 0.f};               // x[4 q + e], the quad's share
 #pragma unroll
-            for (int ii = 0; ii < 16; ++ii) {
-                float s = 0.f;
-#pragma unroll
-                for (int mm = 0; mm < ii; ++mm) s += sKK[tri_tile(I, I)][ii][mm] * x[mm];
-                x[ii] = (ii == n) ? 1.f : (ii > n ? -s : 0.f);
+            for (int i = 0; i < 16; ++i) {
+                const float4 a = *reinterpret_cast<const float4*>(arow + 20 * i);
+                float p = a.x * xs[0];
+                p = fmaf(a.y, xs[1], p);
+                p = fmaf(a.z, xs[2], p);
+                p = fmaf(a.w, xs[3], p);
+                p += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, p), 0xb1, 0xf, 0xf, false));
+                p += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, p), 0x4e, 0xf, 0xf, false));
+                const float xi = (i == j) ? 1.f : (i > j ? -p : 0.f);
+                if (q == (i >> 2)) xs[i & 3] = xi;
             }
 #pragma unroll
-            for (int ii = 0; ii < 16; ++ii) sT[tri_tile(I, I)][ii][n] = x[ii];
+            for (int e = 0; e < 4; ++e) sT[tri_tile(I, I)][4 * q + e][j] = xs[e];
         }
         __syncthreads();
         // off-diagonal blocks, column block J = wave: T_IJ = -T_II sum_{M=J}^{I-1} A_IM T_MJ
