@@ -236,10 +236,12 @@ template <> struct In32<float> {
 template <typename TI> struct PrepStage { static constexpr int kBytes = 0; };
 template <> struct PrepStage<bf16> {
     static constexpr int kBytes = 65536;
-    // byte offsets of wave w's 1 KB parts: g (block I, half), k (block I), q (block I)
-    __device__ static constexpr int g_off(int w, int I, int half) { return ((w * 4 + I) * 2 + half) * 1024; }
-    __device__ static constexpr int k_off(int w, int I) { return 32768 + (w * 4 + I) * 1024; }
-    __device__ static constexpr int q_off(int w, int I) { return 49152 + (w * 4 + I) * 1024; }
+    // byte offsets of wave w's 1 KB parts: q (block I) over T and the start of A_kk, which
+    // are free once T' is formed; g (block I, half) and k (block I) over the rest of A_kk and
+    // A_qk, free once the off-diagonal T blocks are formed
+    __device__ static constexpr int q_off(int w, int I) { return (w * 4 + I) * 1024; }
+    __device__ static constexpr int g_off(int w, int I, int half) { return 16384 + ((w * 4 + I) * 2 + half) * 1024; }
+    __device__ static constexpr int k_off(int w, int I) { return 49152 + (w * 4 + I) * 1024; }
 };
 typedef __attribute__((address_space(3))) void* lds_ptr;
 // 16 (or 4) bytes per lane from global memory to LDS at dst + 16 lane (4 lane); dst is
@@ -273,14 +275,14 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     constexpr int NSL = DK >= 32 ? DK / 32 : 1;          // channel slices (32 wide, padded)
     constexpr int NVS = DV >= 32 ? DV / 32 : 1;          // value slices
     // lower 16x16 blocks, rows padded to 20 floats so that 16 lanes reading 4 floats of
-    // 16 different rows hit distinct LDS banks: A_kk, A_qk and T = (I + A_kk)^-1. The same
-    // region receives the next task's staged inputs once T' is formed.
+    // 16 different rows hit distinct LDS banks: T = (I + A_kk)^-1, A_kk and A_qk. The same
+    // region receives the next task's staged inputs as its parts fall free.
     constexpr int kABytes = 3 * 10 * 16 * 20 * 4;
     constexpr int kRBytes = kABytes > Stg::kBytes ? kABytes : Stg::kBytes;
     __shared__ __attribute__((aligned(16))) float sR[kRBytes / 4];
-    float (*const sKK)[16][20] = reinterpret_cast<float (*)[16][20]>(sR);
-    float (*const sQK)[16][20] = reinterpret_cast<float (*)[16][20]>(sR + 10 * 16 * 20);
-    float (*const sT)[16][20] = reinterpret_cast<float (*)[16][20]>(sR + 2 * 10 * 16 * 20);
+    float (*const sT)[16][20] = reinterpret_cast<float (*)[16][20]>(sR);
+    float (*const sKK)[16][20] = reinterpret_cast<float (*)[16][20]>(sR + 10 * 16 * 20);
+    float (*const sQK)[16][20] = reinterpret_cast<float (*)[16][20]>(sR + 2 * 10 * 16 * 20);
     uint8_t* const sRb = reinterpret_cast<uint8_t*>(sR);
     __shared__ float sBeta[64];
     __shared__ unsigned sBetaRaw[64];                     // staged word holding beta of token t
@@ -308,21 +310,24 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             L = T - kChunk * c < kChunk ? T - kChunk * c : kChunk;
         }
     };
-    // issues the staged loads of a task (bf16 input only)
-    auto stage = [&](int t0, int L, int h) {
+    // issues the staged loads of a task (bf16 input only): part 0 = g, k and beta, part 1 = q
+    auto stage = [&](int t0, int L, int h, int part) {
         if constexpr (Stg::kBytes > 0) {
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 const int row = 16 * I + m;
                 if (cvalid && row < L) {
                     const size_t off = (size_t)(t0 + row) * rowq + (size_t)h * DK + c0;
-                    lds_load16(g + off, sRb + Stg::g_off(wave, I, 0));
-                    lds_load16(g + off + 4, sRb + Stg::g_off(wave, I, 1));
-                    lds_load16(k + off, sRb + Stg::k_off(wave, I));
-                    lds_load16(q + off, sRb + Stg::q_off(wave, I));
+                    if (part == 0) {
+                        lds_load16(g + off, sRb + Stg::g_off(wave, I, 0));
+                        lds_load16(g + off + 4, sRb + Stg::g_off(wave, I, 1));
+                        lds_load16(k + off, sRb + Stg::k_off(wave, I));
+                    } else {
+                        lds_load16(q + off, sRb + Stg::q_off(wave, I));
+                    }
                 }
             }
-            if (wave == 0 && lane < L) {
+            if (part == 0 && wave == 0 && lane < L) {
                 const size_t e = (size_t)(t0 + lane) * H + h;       // beta element index
                 lds_load4(reinterpret_cast<const unsigned*>(beta) + (e >> 1), sBetaRaw);
             }
@@ -353,7 +358,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         In32<TI> K, Q;
         if constexpr (Stg::kBytes > 0) {
             if (!staged) {
-                stage(t0, L, h);
+                stage(t0, L, h, 0);
+                stage(t0, L, h, 1);
                 wait_all_memory();
             }
 #pragma unroll
@@ -689,6 +695,20 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             }
         }
         __syncthreads();
+        // A_kk and A_qk are consumed: stage the next task's g, k and beta into their region
+        staged = false;
+        int t0n = 0, Ln = 0, hn = 0;
+        if constexpr (Stg::kBytes > 0) {
+            const int nt = task + (int)gridDim.x;
+            if (nt < ntasks) {
+                chunk_of(nt / H, t0n, Ln);
+                hn = nt % H;
+                if (Ln > 0) {
+                    stage(t0n, Ln, hn, 0);
+                    staged = true;
+                }
+            }
+        }
 
         // ---- T' = T diag(beta) as operand fragments in LDS, converted once: lane (m, grp) of
         //      tile (I, J) holds T'[16I + m][16J + 4grp + r] ----
@@ -702,19 +722,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             sTp[tile][lane] = f;
         }
         __syncthreads();
-        // A and T are consumed (T' is in sTp): stage the next task's inputs into their region
-        staged = false;
-        if constexpr (Stg::kBytes > 0) {
-            const int nt = task + (int)gridDim.x;
-            if (nt < ntasks) {
-                int t0n, Ln;
-                chunk_of(nt / H, t0n, Ln);
-                if (Ln > 0) {
-                    stage(t0n, Ln, nt % H);
-                    staged = true;
-                }
-            }
-        }
+        // T is consumed (T' is in sTp): stage the next task's q into its region
+        if (staged) stage(t0n, Ln, hn, 1);
 
         // ---- W = T' (k exp G): W^T(channel half, I) = sum_{J <= I} (k exp G)_J^T T'_IJ^T; the
         //      result lane (m = token, grp) holds W[16 I + m][4 channels]. The operand of block
