@@ -443,6 +443,14 @@ __device__ __forceinline__ float row_scan16(float x) {
     (void)v;
     return s;
 }
+// one step (row_shr by 1, 2, 4 or 8 lanes: CTRL 0x111, 0x112, 0x114, 0x118) of the
+// inclusive row prefix sum, applied to 32 independent values
+template <int CTRL>
+__device__ __forceinline__ void row_scan16_step(float (&v)[32]) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        v[i] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v[i]), CTRL, 0xf, 0xf, true));
+}
 // value of lane n (compile-time) of each row, broadcast to the row
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {

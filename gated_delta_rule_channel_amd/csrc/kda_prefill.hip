@@ -418,12 +418,24 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         float gtot[8];
         {
             float ce[4][8];
+            // the lane's 32 scans advance one shift at a time, so consecutive DPP adds are
+            // independent and need no hazard wait states (on a plain array: the same steps
+            // applied to the elements of the vector type through a reference compiled to
+            // wrong code with this toolchain)
+            float gs[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) gs[i] = G[i] * kLog2e;
+            row_scan16_step<0x111>(gs);
+            row_scan16_step<0x112>(gs);
+            row_scan16_step<0x114>(gs);
+            row_scan16_step<0x118>(gs);
+#pragma unroll
+            for (int i = 0; i < 32; ++i) G[i] = gs[i];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float acc = 0.f;
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
-                    G[8 * I + e] = row_scan16(G[8 * I + e] * kLog2e);
                     acc += row_bcast<15>(G[8 * I + e]);
                     ce[I][e] = acc;
                 }
