@@ -244,13 +244,18 @@ template <> struct PrepStage<bf16> {
     __device__ static constexpr int k_off(int w, int I) { return 49152 + (w * 4 + I) * 1024; }
 };
 typedef __attribute__((address_space(3))) void* lds_ptr;
+// LDS address of a pointer into a __shared__ array: the low 32 bits of its generic address
+// (an integer conversion, so no null test is emitted for the address-space cast)
+__device__ __forceinline__ lds_ptr lds_addr(void* p) {
+    return (lds_ptr)(uintptr_t)(uint32_t)(uintptr_t)p;
+}
 // 16 (or 4) bytes per lane from global memory to LDS at dst + 16 lane (4 lane); dst is
 // wave-uniform. Completion is counted by vmcnt.
 __device__ __forceinline__ void lds_load16(const void* src, void* dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, lds_addr(dst), 16, 0, 0);
 }
 __device__ __forceinline__ void lds_load4(const void* src, void* dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, lds_addr(dst), 4, 0, 0);
 }
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
