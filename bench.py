@@ -282,6 +282,21 @@ def main():
     mfma_busy = 3.0 * pf_flops / (BF16_PEAK_TFLOPS * 1e12) / tp_mean
     traffic_pf, traffic_dc = load_traffic()
 
+    # context for the decode figure: torch's device-to-device copy of 1 GiB (read + write)
+    xc = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    yc = torch.empty_like(xc)
+    yc.copy_(xc)
+    tc = []
+    for _ in range(5):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        yc.copy_(xc)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        tc.append(c0.elapsed_time(c1) * 1e-3)
+    copy_gbs = 2 * COPY_BYTES / float(np.median(tc)) / 1e9
+    del xc, yc
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(wp, args.cpu_seconds)
 
     out = {
@@ -309,7 +324,8 @@ def main():
                    "ms_min": float(td.min()) * 1e3,
                    "state_updates_per_s": wd.N * wd.H / td_mean, "tokens_per_s": wd.N / td_mean,
                    "compulsory_bytes": dc_bytes, "hbm_gbs": dc_gbs,
-                   "frac_of_peak": dc_gbs / HBM_PEAK_GBS},
+                   "frac_of_peak": dc_gbs / HBM_PEAK_GBS,
+                   "device_copy_gbs": copy_gbs, "frac_of_device_copy": dc_gbs / copy_gbs},
         "roofline": {"bound": "hbm", "achieved": pf_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": pf_gbs / HBM_PEAK_GBS, "traffic": traffic_pf,
                      "kernel": "kda_fwd_chunked call (prep_kernel + state_kernel; packed "
