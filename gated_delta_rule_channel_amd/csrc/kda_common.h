@@ -200,6 +200,17 @@ struct PolF32 {
     }
     template <int W>
     __device__ static __forceinline__ void pair_decode(Frag& f, const Pair& r) { f = r.f[W]; }
+    // ---- U tiles (1 KB): four fp32 values per lane ----
+    static constexpr int kUTileBytes = 1024;
+    using URaw = float4;
+    __device__ static __forceinline__ void utile_store(void* t, int lane, float a, float b,
+                                                       float c, float d) {
+        reinterpret_cast<float4*>(t)[lane] = make_float4(a, b, c, d);
+    }
+    __device__ static __forceinline__ void utile_load(URaw& r, const void* t, int lane) {
+        r = reinterpret_cast<const float4*>(t)[lane];
+    }
+    __device__ static __forceinline__ float4 utile_decode(const URaw& r) { return r; }
     // elements 4 half .. 4 half + 3 of a lane's fragment
     __device__ static __forceinline__ void tile_store_quad(void* t, int lane, int half, float a,
                                                            float b, float c, float d) {
@@ -399,6 +410,30 @@ struct PolSplit {
         t.ext[0] = r.ext[2 * W];
         t.ext[1] = r.ext[2 * W + 1];
         tile_decode(f, t);
+    }
+    // ---- U tiles (768 B): four values per lane in the 24-bit form, the hi halves (8 B per
+    // lane) then the extension bytes (4 B per lane); U is an addend, so a value is rebuilt
+    // as one float32 (one byte permute) ----
+    static constexpr int kUTileBytes = 768;
+    struct URaw { u32x2 h; unsigned e; };
+    __device__ static __forceinline__ void utile_store(void* t, int lane, float a, float b,
+                                                       float c, float d) {
+        const unsigned r0 = round24(a), r1 = round24(b), r2 = round24(c), r3 = round24(d);
+        u32x2 hw;
+        hw[0] = (r0 >> 16) | (r1 & 0xffff0000u);
+        hw[1] = (r2 >> 16) | (r3 & 0xffff0000u);
+        reinterpret_cast<u32x2*>(t)[lane] = hw;
+        reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(t) + 512)[lane] = ext4(r0, r1, r2, r3);
+    }
+    __device__ static __forceinline__ void utile_load(URaw& r, const void* t, int lane) {
+        r.h = reinterpret_cast<const u32x2*>(t)[lane];
+        r.e = reinterpret_cast<const unsigned*>(reinterpret_cast<const uint8_t*>(t) + 512)[lane];
+    }
+    __device__ static __forceinline__ float4 utile_decode(const URaw& r) {
+        return make_float4(__uint_as_float(__builtin_amdgcn_perm(r.h[0], r.e, 0x0504000cu)),
+                           __uint_as_float(__builtin_amdgcn_perm(r.h[0], r.e, 0x0706010cu)),
+                           __uint_as_float(__builtin_amdgcn_perm(r.h[1], r.e, 0x0504020cu)),
+                           __uint_as_float(__builtin_amdgcn_perm(r.h[1], r.e, 0x0706030cu)));
     }
     // product with b exact in bfloat16 (b.lo == 0): two MFMAs
     __device__ static __forceinline__ void mma16_exact(floatx4& acc, const Frag4& a, const Frag4& b) {

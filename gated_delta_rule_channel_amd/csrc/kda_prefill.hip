@@ -58,8 +58,8 @@ namespace kda {
 // wave reads 1 KB of consecutive bytes (16 B per lane). Fragments (8 elements per lane) are
 // stored in pairs (a, b): PolSplit, 3 KB: the hi values of a, of b, then the extension bytes
 // of both (x rounded to 24 bits = bfloat16 hi + 1 byte, 16 significant bits); PolF32, 4 KB:
-// two fp32 tiles. U tiles (1 KB) hold 4 fp32 values per lane (U is an addend of E, not an
-// MFMA operand). With lane l = m + 16 grp:
+// two fp32 tiles. U tiles hold 4 values per lane (U is an addend of E, not an MFMA
+// operand): PolSplit 768 B in the 24-bit form, PolF32 1 KB of fp32. With lane l = m + 16 grp:
 //  W, Qd  pairs [token tile tw][channel steps (2p, 2p+1)]: row 16 tw + m, channels
 //         32 kap + 8 grp + e (zero past Dk);
 //  Kd^T   pairs [channel tile ct][token halves (0, 1)]: channel 16 ct + m, tokens
@@ -69,21 +69,21 @@ namespace kda {
 //  exp(G_end) float [Dk].
 __host__ __device__ constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-__host__ __device__ constexpr size_t ws_block_bytes(int DK, int DV, size_t PT) {
+__host__ __device__ constexpr size_t ws_block_bytes(int DK, int DV, size_t PT, size_t UT) {
     return round_up((size_t)2 * 4 * (((DK >= 32 ? DK / 32 : 1) + 1) / 2) * PT +
-                        (size_t)(DK / 16) * PT + (size_t)(DV / 16) * 4 * 1024 + 4 * PT +
+                        (size_t)(DK / 16) * PT + (size_t)(DV / 16) * 4 * UT + 4 * PT +
                         (size_t)DK * 4,
                     256);
 }
 
-template <int PTB, int DK, int DV>
+template <int PTB, int UTB, int DK, int DV>
 struct WsLayout {
     static constexpr int KS = DK >= 32 ? DK / 32 : 1;   // 32-channel steps (padded)
     static constexpr int NP = (KS + 1) / 2;              // pairs of channel steps
     static constexpr int NCT = DK / 16;                  // 16-channel tiles
     static constexpr int NVT = DV / 16;                  // 16-value tiles
     static constexpr size_t PT = PTB;                    // pair tile
-    static constexpr size_t QT = 1024;                   // U tile
+    static constexpr size_t QT = UTB;                    // U tile
     static constexpr size_t W = 0;
     static constexpr size_t QD = W + 4 * NP * PT;
     static constexpr size_t KDT = QD + 4 * NP * PT;
@@ -91,11 +91,14 @@ struct WsLayout {
     static constexpr size_t AQ = U + NVT * 4 * QT;
     static constexpr size_t GEND = AQ + 4 * PT;
     static constexpr size_t BYTES = round_up(GEND + DK * sizeof(float), 256);
-    static_assert(BYTES == ws_block_bytes(DK, DV, PT), "workspace block size");
+    static_assert(BYTES == ws_block_bytes(DK, DV, PT, QT), "workspace block size");
 };
+template <typename Pol, int DK, int DV>
+using WsLayoutOf = WsLayout<Pol::kPairBytes, Pol::kUTileBytes, DK, DV>;
 
 size_t prefill_block_bytes(int Dk, int Dv, bool bf16_in) {
-    return ws_block_bytes(Dk, Dv, bf16_in ? PolSplit::kPairBytes : PolF32::kPairBytes);
+    return bf16_in ? ws_block_bytes(Dk, Dv, PolSplit::kPairBytes, PolSplit::kUTileBytes)
+                   : ws_block_bytes(Dk, Dv, PolF32::kPairBytes, PolF32::kUTileBytes);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
     using Pol = typename PolOf<TI>::type;
     using Frag = typename Pol::Frag;
     using Frag4 = typename Pol::Frag4;
-    using Ly = WsLayout<Pol::kPairBytes, DK, DV>;
+    using Ly = WsLayoutOf<Pol, DK, DV>;
     using Stg = PrepStage<TI>;
     constexpr int NSL = DK >= 32 ? DK / 32 : 1;          // channel slices (32 wide, padded)
     constexpr int NVS = DV >= 32 ? DV / 32 : 1;          // value slices
@@ -800,8 +803,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                     }
 #pragma unroll
                     for (int I = 0; I < 4; ++I)
-                        reinterpret_cast<float4*>(blk + Ly::U + ((2 * wave + hh) * 4 + I) * Ly::QT)[lane] =
-                            make_float4(accU[I][0], accU[I][1], accU[I][2], accU[I][3]);
+                        Pol::utile_store(blk + Ly::U + ((2 * wave + hh) * 4 + I) * Ly::QT, lane,
+                                         accU[I][0], accU[I][1], accU[I][2], accU[I][3]);
                 }
             }
         }
@@ -860,7 +863,7 @@ __global__ __launch_bounds__(768) void state_kernel(
     using Pair = typename Pol::Pair;
     using St = typename Pol::Store;
     using Sh = StateShape<DK, DV, BV>;
-    using Ly = WsLayout<Pol::kPairBytes, DK, DV>;
+    using Ly = WsLayoutOf<Pol, DK, DV>;
     constexpr int KS = Sh::KS, NP = Sh::NP, NVT = Sh::NVT, NCT = Sh::NCT, CTW = Sh::CTW;
     constexpr int P = Pol::kPlanes;
     __shared__ St SLs[P][BV][Sh::SST];     // operand copy of S [value][channel]
@@ -929,7 +932,7 @@ __global__ __launch_bounds__(768) void state_kernel(
         // ---- E role: E = U - W S (phase A); loads and decodes W and U (phase B) ----
         struct Raw {
             Pair w[NP];
-            float4 u[NVT];
+            typename Pol::URaw u[NVT];
         };
         Raw R0, R1;                                // raw operands of two later chunks
         Frag wd[KS];                               // decoded W of the current chunk
@@ -941,13 +944,13 @@ __global__ __launch_bounds__(768) void state_kernel(
                 Pol::pair_load(r.w[p], blk + Ly::W + (tw * NP + p) * Ly::PT, lane);
 #pragma unroll
             for (int vr = 0; vr < NVT; ++vr)
-                r.u[vr] = reinterpret_cast<const float4*>(blk + Ly::U + ((v0 / 16 + vr) * 4 + tw) * Ly::QT)[lane];
+                Pol::utile_load(r.u[vr], blk + Ly::U + ((v0 / 16 + vr) * 4 + tw) * Ly::QT, lane);
             issue_fence();
         };
         auto decode = [&](const Raw& r) {
             decode_pairs<Pol, KS, NP>(wd, r.w);
 #pragma unroll
-            for (int vr = 0; vr < NVT; ++vr) ud[vr] = r.u[vr];
+            for (int vr = 0; vr < NVT; ++vr) ud[vr] = Pol::utile_decode(r.u[vr]);
 #pragma unroll
             for (int kap = 0; kap < KS; ++kap) wd[kap].pin_regs();
 #pragma unroll
