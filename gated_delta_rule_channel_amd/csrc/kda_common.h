@@ -200,6 +200,22 @@ struct PolF32 {
     }
     template <int W>
     __device__ static __forceinline__ void pair_decode(Frag& f, const Pair& r) { f = r.f[W]; }
+    // narrower pairs of the bf16 path: full fp32 here
+    static constexpr int kPairNBytes = kPairBytes;
+    using PairN = Pair;
+    __device__ static __forceinline__ void pairn_store_vals(void* t, int lane, int which,
+                                                            const float* x) {
+        pair_store_vals(t, lane, which, x);
+    }
+    __device__ static __forceinline__ void pairn_store_quad(void* t, int lane, int which, int half,
+                                                            float a, float b, float c, float d) {
+        pair_store_quad(t, lane, which, half, a, b, c, d);
+    }
+    __device__ static __forceinline__ void pairn_load(PairN& r, const void* t, int lane) {
+        pair_load(r, t, lane);
+    }
+    template <int W>
+    __device__ static __forceinline__ void pairn_decode(Frag& f, const PairN& r) { f = r.f[W]; }
     // ---- U tiles (1 KB): four fp32 values per lane ----
     static constexpr int kUTileBytes = 1024;
     using URaw = float4;
@@ -410,6 +426,59 @@ struct PolSplit {
         t.ext[0] = r.ext[2 * W];
         t.ext[1] = r.ext[2 * W + 1];
         tile_decode(f, t);
+    }
+    // ---- 20-bit pair tiles (2.5 KB): x rounded to 20 bits of float32 (12 significant bits,
+    // half-way cases away from zero), kept as its bfloat16 hi plus a 4-bit nibble: the hi
+    // values of a, of b, then per lane the 8 nibbles of a (4 B) and of b (4 B). The state
+    // pass rebuilds lo = (hi with its nibble) - hi, exact in bfloat16 ----
+    static constexpr int kPairNBytes = 2560;
+    struct PairN { bf16x8 hi[2]; u32x2 nib; };
+    __device__ static __forceinline__ unsigned round20(float x) { return __float_as_uint(x) + 0x800u; }
+    __device__ static __forceinline__ void pairn_store_vals(void* t, int lane, int which,
+                                                            const float* x) {
+        unsigned r[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = round20(x[e]);
+        u32x4 hw;
+        unsigned nb = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) hw[p] = (r[2 * p] >> 16) | (r[2 * p + 1] & 0xffff0000u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) nb |= ((r[e] >> 12) & 0xfu) << (4 * e);
+        reinterpret_cast<u32x4*>(t)[64 * which + lane] = hw;
+        reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(t) + 2048)[2 * lane + which] = nb;
+    }
+    __device__ static __forceinline__ void pairn_store_quad(void* t, int lane, int which, int half,
+                                                            float a, float b, float c, float d) {
+        const unsigned r0 = round20(a), r1 = round20(b), r2 = round20(c), r3 = round20(d);
+        u32x2 hw;
+        hw[0] = (r0 >> 16) | (r1 & 0xffff0000u);
+        hw[1] = (r2 >> 16) | (r3 & 0xffff0000u);
+        const unsigned nb = ((r0 >> 12) & 0xfu) | (((r1 >> 12) & 0xfu) << 4) |
+                            (((r2 >> 12) & 0xfu) << 8) | (((r3 >> 12) & 0xfu) << 12);
+        reinterpret_cast<u32x2*>(t)[128 * which + 2 * lane + half] = hw;
+        reinterpret_cast<unsigned short*>(reinterpret_cast<uint8_t*>(t) + 2048)[4 * lane + 2 * which + half] =
+            (unsigned short)nb;
+    }
+    __device__ static __forceinline__ void pairn_load(PairN& r, const void* t, int lane) {
+        const bf16x8* p = reinterpret_cast<const bf16x8*>(t);
+        r.hi[0] = p[lane];
+        r.hi[1] = p[64 + lane];
+        r.nib = reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(t) + 2048)[lane];
+    }
+    template <int W>
+    __device__ static __forceinline__ void pairn_decode(Frag& f, const PairN& r) {
+        f.hi = r.hi[W];
+        const u32x4 w = __builtin_bit_cast(u32x4, r.hi[W]);
+        const unsigned n = r.nib[W];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const unsigned h0 = w[p] << 16, h1 = w[p] & 0xffff0000u;
+            const unsigned x0 = h0 | (__builtin_amdgcn_ubfe(n, 8 * p, 4) << 12);
+            const unsigned x1 = h1 | (__builtin_amdgcn_ubfe(n, 8 * p + 4, 4) << 12);
+            f.lo[2 * p] = (bf16)(__uint_as_float(x0) - __uint_as_float(h0));
+            f.lo[2 * p + 1] = (bf16)(__uint_as_float(x1) - __uint_as_float(h1));
+        }
     }
     // ---- U tiles (768 B): four values per lane in the 24-bit form, the hi halves (8 B per
     // lane) then the extension bytes (4 B per lane); U is an addend, so a value is rebuilt

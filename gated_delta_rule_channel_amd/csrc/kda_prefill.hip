@@ -56,27 +56,30 @@ namespace kda {
 // One block per (chunk slot, head). Every operand of the state pass is stored in the
 // register layout of the MFMA fragment that consumes it, so that one load instruction of a
 // wave reads 1 KB of consecutive bytes (16 B per lane). Fragments (8 elements per lane) are
-// stored in pairs (a, b): PolSplit, 3 KB: the hi values of a, of b, then the extension bytes
-// of both (x rounded to 24 bits = bfloat16 hi + 1 byte, 16 significant bits); PolF32, 4 KB:
-// two fp32 tiles. U tiles hold 4 values per lane (U is an addend of E, not an MFMA
-// operand): PolSplit 768 B in the 24-bit form, PolF32 1 KB of fp32. With lane l = m + 16 grp:
-//  W, Qd  pairs [token tile tw][channel steps (2p, 2p+1)]: row 16 tw + m, channels
+// stored in pairs (a, b). PolSplit: A_qk pairs (3 KB) hold the hi values of a, of b, then the
+// extension bytes of both (x rounded to 24 bits = bfloat16 hi + 1 byte, 16 significant
+// bits); W, Qd and Kd^T pairs (2.5 KB) hold x rounded to 20 bits (bfloat16 hi + a 4-bit
+// nibble). PolF32: 4 KB, two fp32 tiles. U tiles hold 4 values per lane (U is an addend of
+// E, not an MFMA operand): PolSplit 768 B in the 24-bit form, PolF32 1 KB of fp32. With
+// lane l = m + 16 grp:
+//  W, Qd  20-bit pairs [token tile tw][channel steps (2p, 2p+1)]: row 16 tw + m, channels
 //         32 kap + 8 grp + e (zero past Dk);
-//  Kd^T   pairs [channel tile ct][token halves (0, 1)]: channel 16 ct + m, tokens
+//  Kd^T   20-bit pairs [channel tile ct][token halves (0, 1)]: channel 16 ct + m, tokens
 //         32 ks + 8 grp + e;
 //  U      tiles [value tile vt][token tile tw]: tokens 16 tw + 4 grp + r, value 16 vt + m;
 //  A_qk   pairs [token tile tw][column halves (0, 1)]: row 16 tw + m, columns 32 s + 8 grp + e;
 //  exp(G_end) float [Dk].
 __host__ __device__ constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-__host__ __device__ constexpr size_t ws_block_bytes(int DK, int DV, size_t PT, size_t UT) {
-    return round_up((size_t)2 * 4 * (((DK >= 32 ? DK / 32 : 1) + 1) / 2) * PT +
-                        (size_t)(DK / 16) * PT + (size_t)(DV / 16) * 4 * UT + 4 * PT +
+__host__ __device__ constexpr size_t ws_block_bytes(int DK, int DV, size_t PT, size_t UT,
+                                                    size_t PN) {
+    return round_up((size_t)2 * 4 * (((DK >= 32 ? DK / 32 : 1) + 1) / 2) * PN +
+                        (size_t)(DK / 16) * PN + (size_t)(DV / 16) * 4 * UT + 4 * PT +
                         (size_t)DK * 4,
                     256);
 }
 
-template <int PTB, int UTB, int DK, int DV>
+template <int PTB, int UTB, int PNB, int DK, int DV>
 struct WsLayout {
     static constexpr int KS = DK >= 32 ? DK / 32 : 1;   // 32-channel steps (padded)
     static constexpr int NP = (KS + 1) / 2;              // pairs of channel steps
@@ -84,21 +87,24 @@ struct WsLayout {
     static constexpr int NVT = DV / 16;                  // 16-value tiles
     static constexpr size_t PT = PTB;                    // pair tile
     static constexpr size_t QT = UTB;                    // U tile
+    static constexpr size_t PN = PNB;                    // narrower pair tile (W, Qd, Kd^T)
     static constexpr size_t W = 0;
-    static constexpr size_t QD = W + 4 * NP * PT;
-    static constexpr size_t KDT = QD + 4 * NP * PT;
-    static constexpr size_t U = KDT + NCT * PT;
+    static constexpr size_t QD = W + 4 * NP * PN;
+    static constexpr size_t KDT = QD + 4 * NP * PN;
+    static constexpr size_t U = KDT + NCT * PN;
     static constexpr size_t AQ = U + NVT * 4 * QT;
     static constexpr size_t GEND = AQ + 4 * PT;
     static constexpr size_t BYTES = round_up(GEND + DK * sizeof(float), 256);
-    static_assert(BYTES == ws_block_bytes(DK, DV, PT, QT), "workspace block size");
+    static_assert(BYTES == ws_block_bytes(DK, DV, PT, QT, PN), "workspace block size");
 };
 template <typename Pol, int DK, int DV>
-using WsLayoutOf = WsLayout<Pol::kPairBytes, Pol::kUTileBytes, DK, DV>;
+using WsLayoutOf = WsLayout<Pol::kPairBytes, Pol::kUTileBytes, Pol::kPairNBytes, DK, DV>;
 
 size_t prefill_block_bytes(int Dk, int Dv, bool bf16_in) {
-    return bf16_in ? ws_block_bytes(Dk, Dv, PolSplit::kPairBytes, PolSplit::kUTileBytes)
-                   : ws_block_bytes(Dk, Dv, PolF32::kPairBytes, PolF32::kUTileBytes);
+    return bf16_in ? ws_block_bytes(Dk, Dv, PolSplit::kPairBytes, PolSplit::kUTileBytes,
+                                    PolSplit::kPairNBytes)
+                   : ws_block_bytes(Dk, Dv, PolF32::kPairBytes, PolF32::kUTileBytes,
+                                    PolF32::kPairNBytes);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -497,7 +503,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                         qdv[e] = scale * qq[e] * ec;
                         Kd.set(e, kk[e] * ed);
                     }
-                    Pol::pair_store_vals(blk + Ly::QD + (I * Ly::NP + (wave >> 1)) * Ly::PT, lane,
+                    Pol::pairn_store_vals(blk + Ly::QD + (I * Ly::NP + (wave >> 1)) * Ly::PN, lane,
                                          wave & 1, qdv);
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
@@ -505,7 +511,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                             floatx4 dk = {0.f, 0.f, 0.f, 0.f};
                             Pol::mma_exact(dk, Kd, Eid[hh]);  // lane (channel n, grp): tokens 4 grp + r
                             const int ct = 2 * wave + hh, ks = I >> 1;
-                            Pol::pair_store_quad(blk + Ly::KDT + ct * Ly::PT,
+                            Pol::pairn_store_quad(blk + Ly::KDT + ct * Ly::PN,
                                                  m + 16 * (2 * (I & 1) + (grp >> 1)), ks, grp & 1,
                                                  dk[0], dk[1], dk[2], dk[3]);
                         }
@@ -779,7 +785,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                 for (int I = 0; I < 4; ++I)
-                    Pol::pair_store_quad(blk + Ly::W + (I * Ly::NP + (wave >> 1)) * Ly::PT,
+                    Pol::pairn_store_quad(blk + Ly::W + (I * Ly::NP + (wave >> 1)) * Ly::PN,
                                          m + 16 * (2 * hh + (grp >> 1)), wave & 1, grp & 1,
                                          accW[hh][I][0], accW[hh][I][1], accW[hh][I][2], accW[hh][I][3]);
         }
@@ -845,11 +851,11 @@ struct StateShape {
 
 template <typename Pol, int KS, int NP>
 __device__ __forceinline__ void decode_pairs(typename Pol::Frag (&d)[KS],
-                                             const typename Pol::Pair (&r)[NP]) {
+                                             const typename Pol::PairN (&r)[NP]) {
 #pragma unroll
     for (int kap = 0; kap < KS; ++kap) {
-        if (kap & 1) Pol::template pair_decode<1>(d[kap], r[kap >> 1]);
-        else Pol::template pair_decode<0>(d[kap], r[kap >> 1]);
+        if (kap & 1) Pol::template pairn_decode<1>(d[kap], r[kap >> 1]);
+        else Pol::template pairn_decode<0>(d[kap], r[kap >> 1]);
     }
 }
 
@@ -931,7 +937,7 @@ __global__ __launch_bounds__(768) void state_kernel(
     } else if (role == 0) {
         // ---- E role: E = U - W S (phase A); loads and decodes W and U (phase B) ----
         struct Raw {
-            Pair w[NP];
+            typename Pol::PairN w[NP];
             typename Pol::URaw u[NVT];
         };
         Raw R0, R1;                                // raw operands of two later chunks
@@ -941,7 +947,7 @@ __global__ __launch_bounds__(768) void state_kernel(
             const uint8_t* blk = block(c);
 #pragma unroll
             for (int p = 0; p < NP; ++p)
-                Pol::pair_load(r.w[p], blk + Ly::W + (tw * NP + p) * Ly::PT, lane);
+                Pol::pairn_load(r.w[p], blk + Ly::W + (tw * NP + p) * Ly::PN, lane);
 #pragma unroll
             for (int vr = 0; vr < NVT; ++vr)
                 Pol::utile_load(r.u[vr], blk + Ly::U + ((v0 / 16 + vr) * 4 + tw) * Ly::QT, lane);
@@ -995,7 +1001,7 @@ __global__ __launch_bounds__(768) void state_kernel(
         // ---- S role: S' = Diag(exp G_end) S + Kd^T E. exp(G_end) (Dk floats) is fetched by
         //      the first S-role wave alone and shared through LDS ----
         struct Raw {
-            Pair k[CTW];
+            typename Pol::PairN k[CTW];
             float2 g;                              // exp(G_end)[2 lane, 2 lane + 1] (wave 4)
         };
         Raw R0, R1;                                // raw operands of two later chunks
@@ -1009,7 +1015,7 @@ __global__ __launch_bounds__(768) void state_kernel(
 #pragma unroll
                 for (int j = 0; j < CTW; ++j) {
                     const int ct = tw + 4 * j;
-                    Pol::pair_load(r.k[j], blk + Ly::KDT + ct * Ly::PT, lane);
+                    Pol::pairn_load(r.k[j], blk + Ly::KDT + ct * Ly::PN, lane);
                 }
                 issue_fence();
             }
@@ -1020,8 +1026,8 @@ __global__ __launch_bounds__(768) void state_kernel(
             if (owns) {
 #pragma unroll
                 for (int j = 0; j < CTW; ++j) {
-                    Pol::template pair_decode<0>(kd[j][0], r.k[j]);
-                    Pol::template pair_decode<1>(kd[j][1], r.k[j]);
+                    Pol::template pairn_decode<0>(kd[j][0], r.k[j]);
+                    Pol::template pairn_decode<1>(kd[j][1], r.k[j]);
                     kd[j][0].pin_regs();
                     kd[j][1].pin_regs();
                 }
@@ -1070,7 +1076,7 @@ __global__ __launch_bounds__(768) void state_kernel(
         // ---- O role: O = Qd S_c (phase A, kept in registers) + A_qk E (phase B), then the
         //      output; lane (n = token, grp) holds values 16 vr + 4 grp + r ----
         struct Raw {
-            Pair q[NP];
+            typename Pol::PairN q[NP];
             Pair a;
         };
         Raw R0, R1;                                // raw Qd and A_qk of two later chunks
@@ -1082,7 +1088,7 @@ __global__ __launch_bounds__(768) void state_kernel(
             const uint8_t* blk = block(c);
 #pragma unroll
             for (int p = 0; p < NP; ++p)
-                Pol::pair_load(r.q[p], blk + Ly::QD + (tw * NP + p) * Ly::PT, lane);
+                Pol::pairn_load(r.q[p], blk + Ly::QD + (tw * NP + p) * Ly::PN, lane);
             issue_fence();
         };
         auto issue_a = [&](Raw& r, int c) {

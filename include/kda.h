@@ -70,8 +70,9 @@ const char* kda_status_string(kda_status s);
  * call will pass cu_seqlens (then B must be 1 and num_seqs is the number of
  * packed sequences); the bound used is floor(T/64) + num_seqs chunks per head
  * for packed input and B * ceil(T/64) otherwise, so cu_seqlens is never read
- * on the host. The size depends on dtype: the per-chunk operands take 3 bytes
- * per element for bf16 input (16 significant bits) and 4 for fp32 input.
+ * on the host. The size depends on dtype: for bf16 input the per-chunk
+ * operands take 2.5 bytes per element (W, Qd, Kd^T: 12 significant bits) or 3
+ * (A_qk, U: 16 significant bits); for fp32 input every operand takes 4 bytes.
  * Errors: KDA_ERROR_INVALID_VALUE for a NULL `bytes`, a non-positive size,
  * or an unsupported head size. */
 kda_status kda_fwd_chunked_workspace_size(int B, int T, int H, int Dk, int Dv, int num_seqs,

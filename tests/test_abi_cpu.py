@@ -50,12 +50,12 @@ def test_status_strings(lib):
 
 def test_workspace_size(lib):
     # chunk slots: B * ceil(T/64) fixed-length, floor(T/64) + N packed
-    # per (chunk, head): W, Qd, KdT, A_qk and U at 3 bytes per element for bf16 input and 4
-    # for fp32 input, exp(G_end) in fp32
+    # per (chunk, head): W, Qd, KdT at 2.5 bytes per element and A_qk, U at 3 for bf16 input,
+    # everything at 4 for fp32 input; exp(G_end) in fp32
     slots = 128
     header = ((slots * 16 + 255) // 256) * 256 + 256
-    for dtype, eb in ((kda.KDA_DTYPE_BF16, 3), (kda.KDA_DTYPE_F32, 4)):
-        per_block = eb * (4 * 64 * 128 + 64 * 64) + 128 * 4
+    for dtype, nb, eb in ((kda.KDA_DTYPE_BF16, 2.5, 3), (kda.KDA_DTYPE_F32, 4, 4)):
+        per_block = int(nb * 3 * 64 * 128 + eb * (64 * 128 + 64 * 64)) + 128 * 4
         n = kda.workspace_size(1, 8192, 64, 128, 128, 1, False, dtype)
         assert n == header + slots * 64 * ((per_block + 255) // 256 * 256)
     n2 = kda.workspace_size(1, 105872, 64, 128, 128, 8, True, kda.KDA_DTYPE_BF16)
