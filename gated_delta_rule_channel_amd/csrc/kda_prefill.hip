@@ -45,6 +45,7 @@
 // sums, as the page's "real Triton implementation" paragraph describes), and
 // cross-block factors come from block totals.
 #include <atomic>
+#include <type_traits>
 
 #include "kda_common.h"
 
@@ -208,6 +209,16 @@ template <> struct In32<bf16> {
             o[2 * p + 1] = __uint_as_float(x & 0xffff0000u);
         }
     }
+    // get8 through an empty asm on each word: the result counts as computed where it is read
+    __device__ __forceinline__ void get8p(int I, float* o) const {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            unsigned x = w[4 * I + p];
+            asm volatile("" : "+v"(x));
+            o[2 * p] = __uint_as_float(x << 16);
+            o[2 * p + 1] = __uint_as_float(x & 0xffff0000u);
+        }
+    }
     // the 8 elements of block I as an exact operand fragment
     __device__ __forceinline__ void frag(int I, PolSplit::Frag& f) const {
         typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -233,6 +244,14 @@ template <> struct In32<float> {
     __device__ __forceinline__ void get8(int I, float* o) const {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = v[8 * I + e];
+    }
+    __device__ __forceinline__ void get8p(int I, float* o) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = v[8 * I + e];
+            asm volatile("" : "+v"(x));
+            o[e] = x;
+        }
     }
     __device__ __forceinline__ void frag(int I, PolF32::Frag& f) const {
 #pragma unroll
@@ -475,172 +494,185 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         }
         __syncthreads();                                    // A accumulators zeroed, beta in LDS
 
-        // ---- rotated pass over the row blocks: Qd, Kd^T, partial A blocks ----
+        // ---- rotated pass over the row blocks: Qd, Kd^T, partial A blocks. The row block of
+        //      a step depends on the wave; each row block is its own instance of the step, so
+        //      the register arrays are indexed with constants ----
+        auto row_step = [&](auto Ic) {
+            constexpr int I = decltype(Ic)::value;
+            constexpr int Ip = I > 0 ? I - 1 : 0;
+            // the step reads its inputs through empty asm statements, so that no part of it is
+            // computed ahead of the loop (that would keep every row block's operands live)
+            auto opq = [](float x) { asm volatile("" : "+v"(x)); return x; };
+            const int row = 16 * I + m;
+            const float bi = sBeta[row];
+            float Gl[8], kk[8], qq[8], pf[8];
+            K.get8p(I, kk);
+            Q.get8p(I, qq);
+            ce8(Ip, pf);                                  // cumulative value before block I
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                Gl[e] = opq(G[8 * I + e]);
+                if (I == 0) pf[e] = 0.f;
+            }
+            // (a) chunk-start / chunk-end references: Qd and Kd^T to the workspace
+            {
+                Frag Kd;
+                float qdv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float Gc = pf[e] + Gl[e];
+                    const float ec = fast_exp2(Gc), ed = fast_exp2(gtot[e] - Gc);
+                    qdv[e] = scale * qq[e] * ec;
+                    Kd.set(e, kk[e] * ed);
+                }
+                Pol::pairn_store_vals(blk + Ly::QD + (I * Ly::NP + (wave >> 1)) * Ly::PN, lane,
+                                     wave & 1, qdv);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    if (32 * wave + 16 * hh < DK) {
+                        floatx4 dk = {0.f, 0.f, 0.f, 0.f};
+                        Pol::mma_exact(dk, Kd, Eid[hh]);  // lane (channel n, grp): tokens 4 grp + r
+                        const int ct = 2 * wave + hh, ks = I >> 1;
+                        Pol::pairn_store_quad(blk + Ly::KDT + ct * Ly::PN,
+                                             m + 16 * (2 * (I & 1) + (grp >> 1)), ks, grp & 1,
+                                             dk[0], dk[1], dk[2], dk[3]);
+                    }
+                }
+            }
+            // row operands with the block-start reference, exp(G_i - G_r) <= 1 (r = end of
+            // block I - 1): shared by the diagonal and the off-diagonal blocks of row I
+            Frag KA, QA;
+            bool far = false;                             // block decays beyond 2^120
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float ea = fast_exp2(Gl[e]);
+                KA.set(e, bi * kk[e] * ea);
+                QA.set(e, scale * qq[e] * ea);
+                far |= Gl[e] < -120.f;
+            }
+            // (b) diagonal block: block-start reference (column factor exp(G_r - G_j) <= 2^120),
+            //     else the midpoint of the block, else pairwise
+            {
+                floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+                bool bad = false;
+                if (!__any(far)) {
+                    Frag KC;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) KC.set(e, kk[e] * fast_exp2(-Gl[e]));
+                    Pol::mma(akk, KC, KA);
+                    Pol::mma(aqk, KC, QA);
+                } else {
+                    Frag KE, QE, KR;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float x = Gl[e] - row_bcast<7>(Gl[e]);
+                        bad |= fabsf(x) > 120.f;
+                        const float e1 = fast_exp2(x), e2 = fast_exp2(-x);
+                        KE.set(e, bi * kk[e] * e1);
+                        QE.set(e, scale * qq[e] * e1);
+                        KR.set(e, kk[e] * e2);
+                    }
+                    if (!__any(bad)) {
+                        Pol::mma(akk, KR, KE);
+                        Pol::mma(aqk, KR, QE);
+                    }
+                }
+                if (__any(bad)) {
+                    // exact pairwise sums over this slice: entry (i = m, j = jj)
+#pragma unroll 1
+                    for (int jj = 0; jj < 16; ++jj) {
+                        float skk = 0.f, sqk = 0.f;
+                        const int src = (lane & 48) | jj;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float Gj = __shfl(Gl[e], src);
+                            const float kj = __shfl(kk[e], src);
+                            const float d = jj <= m ? fast_exp2(Gl[e] - Gj) : 0.f;
+                            skk += kk[e] * kj * d;
+                            sqk += scale * qq[e] * kj * d;
+                        }
+                        skk += __shfl_xor(skk, 16);
+                        skk += __shfl_xor(skk, 32);
+                        sqk += __shfl_xor(sqk, 16);
+                        sqk += __shfl_xor(sqk, 32);
+                        if ((jj >> 2) == grp) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (r == (jj & 3)) { akk[r] = bi * skk; aqk[r] = sqk; }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 4 * grp + r;
+                    if (!(j < m)) akk[r] = 0.f;
+                    if (!(j <= m)) aqk[r] = 0.f;
+                }
+                float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(I, I)][m][4 * grp]);
+                float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(I, I)][m][4 * grp]);
+                float4 a = *pk, c = *pq;
+                a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
+                c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
+                *pk = a;
+                *pq = c;
+            }
+            // (c) off-diagonal blocks J < I: reference at the end of block I - 1. The pair
+            //     (3, 0) is taken by the wave holding row block 0 in this step (that wave has
+            //     no other off-diagonal pair), which balances the steps; every pair still gets
+            //     one partial per wave and no two waves write one block in the same step.
+            // partial of pair (II, J) with row operands KA, QA of block II (pfI = cumulative
+            // value before block II)
+            auto offdiag = [&](int II, int J, const Frag& KA2, const Frag& QA2, const float* pfI) {
+                // k of block J decayed to the start of block II
+                const int Jp = J > 0 ? J - 1 : 0;
+                float kJ[8], ceJ[8];
+                K.get8p(J, kJ);
+                ce8(Jp, ceJ);
+                Frag b;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float cj = J > 0 ? ceJ[e] : 0.f;
+                    b.set(e, kJ[e] * fast_exp2(pfI[e] - cj - opq(G[8 * J + e])));
+                }
+                floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+                Pol::mma(akk, b, KA2);
+                Pol::mma(aqk, b, QA2);
+                float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(II, J)][m][4 * grp]);
+                float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(II, J)][m][4 * grp]);
+                float4 a = *pk, c = *pq;
+                a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
+                c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
+                *pk = a;
+                *pq = c;
+            };
+            if constexpr (I > 0) {
+#pragma unroll
+                for (int J = I == 3 ? 1 : 0; J < I; ++J) offdiag(I, J, KA, QA, pf);
+            } else {
+                // row block 3 of this slice (static registers)
+                float k3[8], q3[8], pf3[8];
+                K.get8p(3, k3);
+                Q.get8p(3, q3);
+                ce8(2, pf3);
+                const float b3 = sBeta[48 + m];
+                Frag KA3, QA3;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float ea = fast_exp2(opq(G[24 + e]));
+                    KA3.set(e, b3 * k3[e] * ea);
+                    QA3.set(e, scale * q3[e] * ea);
+                }
+                offdiag(3, 0, KA3, QA3, pf3);
+            }
+        };
 #pragma unroll 1
         for (int st = 0; st < 4; ++st) {
             if (cs) {
-                const int I = (wave + st) & 3;                // wave-uniform
-                const int Ip = __builtin_amdgcn_readfirstlane(I > 0 ? I - 1 : 0);
-                const int row = 16 * I + m;
-                const float bi = sBeta[row];
-                float Gl[8], kk[8], qq[8], pf[8];
-                K.get8(I, kk);
-                Q.get8(I, qq);
-                ce8(Ip, pf);                                  // cumulative value before block I
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    Gl[e] = G[8 * I + e];
-                    if (I == 0) pf[e] = 0.f;
-                }
-                // (a) chunk-start / chunk-end references: Qd and Kd^T to the workspace
-                {
-                    Frag Kd;
-                    float qdv[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float Gc = pf[e] + Gl[e];
-                        const float ec = fast_exp2(Gc), ed = fast_exp2(gtot[e] - Gc);
-                        qdv[e] = scale * qq[e] * ec;
-                        Kd.set(e, kk[e] * ed);
-                    }
-                    Pol::pairn_store_vals(blk + Ly::QD + (I * Ly::NP + (wave >> 1)) * Ly::PN, lane,
-                                         wave & 1, qdv);
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        if (32 * wave + 16 * hh < DK) {
-                            floatx4 dk = {0.f, 0.f, 0.f, 0.f};
-                            Pol::mma_exact(dk, Kd, Eid[hh]);  // lane (channel n, grp): tokens 4 grp + r
-                            const int ct = 2 * wave + hh, ks = I >> 1;
-                            Pol::pairn_store_quad(blk + Ly::KDT + ct * Ly::PN,
-                                                 m + 16 * (2 * (I & 1) + (grp >> 1)), ks, grp & 1,
-                                                 dk[0], dk[1], dk[2], dk[3]);
-                        }
-                    }
-                }
-                // row operands with the block-start reference, exp(G_i - G_r) <= 1 (r = end of
-                // block I - 1): shared by the diagonal and the off-diagonal blocks of row I
-                Frag KA, QA;
-                bool far = false;                             // block decays beyond 2^120
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float ea = fast_exp2(Gl[e]);
-                    KA.set(e, bi * kk[e] * ea);
-                    QA.set(e, scale * qq[e] * ea);
-                    far |= Gl[e] < -120.f;
-                }
-                // (b) diagonal block: block-start reference (column factor exp(G_r - G_j) <= 2^120),
-                //     else the midpoint of the block, else pairwise
-                {
-                    floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
-                    bool bad = false;
-                    if (!__any(far)) {
-                        Frag KC;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) KC.set(e, kk[e] * fast_exp2(-Gl[e]));
-                        Pol::mma(akk, KC, KA);
-                        Pol::mma(aqk, KC, QA);
-                    } else {
-                        Frag KE, QE, KR;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float x = Gl[e] - row_bcast<7>(Gl[e]);
-                            bad |= fabsf(x) > 120.f;
-                            const float e1 = fast_exp2(x), e2 = fast_exp2(-x);
-                            KE.set(e, bi * kk[e] * e1);
-                            QE.set(e, scale * qq[e] * e1);
-                            KR.set(e, kk[e] * e2);
-                        }
-                        if (!__any(bad)) {
-                            Pol::mma(akk, KR, KE);
-                            Pol::mma(aqk, KR, QE);
-                        }
-                    }
-                    if (__any(bad)) {
-                        // exact pairwise sums over this slice: entry (i = m, j = jj)
-#pragma unroll 1
-                        for (int jj = 0; jj < 16; ++jj) {
-                            float skk = 0.f, sqk = 0.f;
-                            const int src = (lane & 48) | jj;
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const float Gj = __shfl(Gl[e], src);
-                                const float kj = __shfl(kk[e], src);
-                                const float d = jj <= m ? fast_exp2(Gl[e] - Gj) : 0.f;
-                                skk += kk[e] * kj * d;
-                                sqk += scale * qq[e] * kj * d;
-                            }
-                            skk += __shfl_xor(skk, 16);
-                            skk += __shfl_xor(skk, 32);
-                            sqk += __shfl_xor(sqk, 16);
-                            sqk += __shfl_xor(sqk, 32);
-                            if ((jj >> 2) == grp) {
-#pragma unroll
-                                for (int r = 0; r < 4; ++r)
-                                    if (r == (jj & 3)) { akk[r] = bi * skk; aqk[r] = sqk; }
-                            }
-                        }
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = 4 * grp + r;
-                        if (!(j < m)) akk[r] = 0.f;
-                        if (!(j <= m)) aqk[r] = 0.f;
-                    }
-                    float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(I, I)][m][4 * grp]);
-                    float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(I, I)][m][4 * grp]);
-                    float4 a = *pk, c = *pq;
-                    a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
-                    c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
-                    *pk = a;
-                    *pq = c;
-                }
-                // (c) off-diagonal blocks J < I: reference at the end of block I - 1. The pair
-                //     (3, 0) is taken by the wave holding row block 0 in this step (that wave has
-                //     no other off-diagonal pair), which balances the steps; every pair still gets
-                //     one partial per wave and no two waves write one block in the same step.
-                // partial of pair (II, J) with row operands KA, QA of block II (pfI = cumulative
-                // value before block II)
-                auto offdiag = [&](int II, int J, const Frag& KA2, const Frag& QA2, const float* pfI) {
-                    // k of block J decayed to the start of block II
-                    const int Jp = __builtin_amdgcn_readfirstlane(J > 0 ? J - 1 : 0);
-                    float kJ[8], ceJ[8];
-                    K.get8(J, kJ);
-                    ce8(Jp, ceJ);
-                    Frag b;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float cj = J > 0 ? ceJ[e] : 0.f;
-                        b.set(e, kJ[e] * fast_exp2(pfI[e] - cj - G[8 * J + e]));
-                    }
-                    floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
-                    Pol::mma(akk, b, KA2);
-                    Pol::mma(aqk, b, QA2);
-                    float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(II, J)][m][4 * grp]);
-                    float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(II, J)][m][4 * grp]);
-                    float4 a = *pk, c = *pq;
-                    a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
-                    c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
-                    *pk = a;
-                    *pq = c;
-                };
-                if (I > 0) {
-#pragma unroll 1
-                    for (int J = I == 3 ? 1 : 0; J < I; ++J) offdiag(I, J, KA, QA, pf);
-                } else {
-                    // row block 3 of this slice (static registers)
-                    float k3[8], q3[8], pf3[8];
-                    K.get8(3, k3);
-                    Q.get8(3, q3);
-                    ce8(2, pf3);
-                    const float b3 = sBeta[48 + m];
-                    Frag KA3, QA3;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float ea = fast_exp2(G[24 + e]);
-                        KA3.set(e, b3 * k3[e] * ea);
-                        QA3.set(e, scale * q3[e] * ea);
-                    }
-                    offdiag(3, 0, KA3, QA3, pf3);
+                switch ((wave + st) & 3) {                    // wave-uniform
+                    case 0: row_step(std::integral_constant<int, 0>{}); break;
+                    case 1: row_step(std::integral_constant<int, 1>{}); break;
+                    case 2: row_step(std::integral_constant<int, 2>{}); break;
+                    default: row_step(std::integral_constant<int, 3>{}); break;
                 }
             }
             __syncthreads();
