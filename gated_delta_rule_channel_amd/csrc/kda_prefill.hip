@@ -264,9 +264,9 @@ template <> struct In32<float> {
 template <typename TI> struct PrepStage { static constexpr int kBytes = 0; };
 template <> struct PrepStage<bf16> {
     static constexpr int kBytes = 65536;
-    // byte offsets of wave w's 1 KB parts: q (block I) over T and the start of A_kk, which
-    // are free once T' is formed; g (block I, half) and k (block I) over the rest of A_kk and
-    // A_qk, free once the off-diagonal T blocks are formed
+    // byte offsets of wave w's 1 KB parts: q (block I) over T and the start of A_kk, g
+    // (block I, half) and k (block I) over the rest of A_kk and A_qk; all of it is free once
+    // T' is formed
     __device__ static constexpr int q_off(int w, int I) { return (w * 4 + I) * 1024; }
     __device__ static constexpr int g_off(int w, int I, int half) { return 16384 + ((w * 4 + I) * 2 + half) * 1024; }
     __device__ static constexpr int k_off(int w, int I) { return 49152 + (w * 4 + I) * 1024; }
@@ -753,21 +753,6 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             }
         }
         __syncthreads();
-        // A_kk and A_qk are consumed: stage the next task's g, k and beta into their region
-        staged = false;
-        int t0n = 0, Ln = 0, hn = 0;
-        if constexpr (Stg::kBytes > 0) {
-            const int nt = task + (int)gridDim.x;
-            if (nt < ntasks) {
-                chunk_of(nt / H, t0n, Ln);
-                hn = nt % H;
-                if (Ln > 0) {
-                    stage(t0n, Ln, hn, 0);
-                    staged = true;
-                }
-            }
-        }
-
         // ---- T' = T diag(beta) as operand fragments in LDS, converted once: lane (m, grp) of
         //      tile (I, J) holds T'[16I + m][16J + 4grp + r] ----
         for (int tile = wave; tile < 10; tile += 4) {
@@ -780,8 +765,23 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             sTp[tile][lane] = f;
         }
         __syncthreads();
-        // T is consumed (T' is in sTp): stage the next task's q into its region
-        if (staged) stage(t0n, Ln, hn, 1);
+        // A_kk, A_qk and T are consumed (T' is in sTp): stage the next task's g, k, beta and q
+        // into their regions. Issued after the last barrier of the task: a barrier waits for
+        // every load into LDS still in flight, so these land during W and U instead
+        staged = false;
+        if constexpr (Stg::kBytes > 0) {
+            const int nt = task + (int)gridDim.x;
+            if (nt < ntasks) {
+                int t0n, Ln;
+                chunk_of(nt / H, t0n, Ln);
+                const int hn = nt % H;
+                if (Ln > 0) {
+                    stage(t0n, Ln, hn, 0);
+                    stage(t0n, Ln, hn, 1);
+                    staged = true;
+                }
+            }
+        }
 
         // ---- W = T' (k exp G): W^T(channel half, I) = sum_{J <= I} (k exp G)_J^T T'_IJ^T; the
         //      result lane (m = token, grp) holds W[16 I + m][4 channels]. The operand of block
