@@ -343,24 +343,19 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             L = T - kChunk * c < kChunk ? T - kChunk * c : kChunk;
         }
     };
-    // issues the staged loads of a task (bf16 input only): part 0 = g, k and beta, part 1 = q
-    auto stage = [&](int t0, int L, int h, int part) {
+    // issues the staged loads of row block I of a task (bf16 input only): g, k and q of the
+    // block, and beta with block 0
+    auto stage = [&](int t0, int L, int h, int I) {
         if constexpr (Stg::kBytes > 0) {
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                const int row = 16 * I + m;
-                if (cvalid && row < L) {
-                    const size_t off = (size_t)(t0 + row) * rowq + (size_t)h * DK + c0;
-                    if (part == 0) {
-                        lds_load16(g + off, sRb + Stg::g_off(wave, I, 0));
-                        lds_load16(g + off + 4, sRb + Stg::g_off(wave, I, 1));
-                        lds_load16(k + off, sRb + Stg::k_off(wave, I));
-                    } else {
-                        lds_load16(q + off, sRb + Stg::q_off(wave, I));
-                    }
-                }
+            const int row = 16 * I + m;
+            if (cvalid && row < L) {
+                const size_t off = (size_t)(t0 + row) * rowq + (size_t)h * DK + c0;
+                lds_load16(g + off, sRb + Stg::g_off(wave, I, 0));
+                lds_load16(g + off + 4, sRb + Stg::g_off(wave, I, 1));
+                lds_load16(k + off, sRb + Stg::k_off(wave, I));
+                lds_load16(q + off, sRb + Stg::q_off(wave, I));
             }
-            if (part == 0 && wave == 0 && lane < L) {
+            if (I == 0 && wave == 0 && lane < L) {
                 const size_t e = (size_t)(t0 + lane) * H + h;       // beta element index
                 lds_load4(reinterpret_cast<const unsigned*>(beta) + (e >> 1), sBetaRaw);
             }
@@ -391,8 +386,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         In32<TI> K, Q;
         if constexpr (Stg::kBytes > 0) {
             if (!staged) {
-                stage(t0, L, h, 0);
-                stage(t0, L, h, 1);
+#pragma unroll
+                for (int I = 0; I < 4; ++I) stage(t0, L, h, I);
                 wait_all_memory();
             }
 #pragma unroll
@@ -765,23 +760,22 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             sTp[tile][lane] = f;
         }
         __syncthreads();
-        // A_kk, A_qk and T are consumed (T' is in sTp): stage the next task's g, k, beta and q
-        // into their regions. Issued after the last barrier of the task: a barrier waits for
-        // every load into LDS still in flight, so these land during W and U instead
-        staged = false;
+        // A_kk, A_qk and T are consumed (T' is in sTp): the next task's g, k, beta and q are
+        // staged into their regions, one row block before each block of W below. Issued after
+        // the last barrier of the task (a barrier waits for every load into LDS in flight) and
+        // spread out, because the issue of a load stalls while the memory system holds too
+        // many of them
+        bool stage_next = false;
+        int t0n = 0, Ln = 0, hn = 0;
         if constexpr (Stg::kBytes > 0) {
             const int nt = task + (int)gridDim.x;
             if (nt < ntasks) {
-                int t0n, Ln;
                 chunk_of(nt / H, t0n, Ln);
-                const int hn = nt % H;
-                if (Ln > 0) {
-                    stage(t0n, Ln, hn, 0);
-                    stage(t0n, Ln, hn, 1);
-                    staged = true;
-                }
+                hn = nt % H;
+                stage_next = Ln > 0;
             }
         }
+        staged = stage_next;
 
         // ---- W = T' (k exp G): W^T(channel half, I) = sum_{J <= I} (k exp G)_J^T T'_IJ^T; the
         //      result lane (m = token, grp) holds W[16 I + m][4 channels]. The operand of block
@@ -795,6 +789,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                 for (int I = 0; I < 4; ++I) accW[hh][I] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
+                if (stage_next) stage(t0n, Ln, hn, J);
                 float kJ[8], ceJ[8];
                 K.get8(J, kJ);
                 ce8(J > 0 ? J - 1 : 0, ceJ);
