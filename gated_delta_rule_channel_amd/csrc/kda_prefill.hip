@@ -265,8 +265,8 @@ template <typename TI> struct PrepStage { static constexpr int kBytes = 0; };
 template <> struct PrepStage<bf16> {
     static constexpr int kBytes = 65536;
     // byte offsets of wave w's 1 KB parts: q (block I) over T and the start of A_kk, g
-    // (block I, half) and k (block I) over the rest of A_kk and A_qk; all of it is free once
-    // T' is formed
+    // (block I, rows 8 half .. 8 half + 7) and k (block I) over the rest of A_kk and A_qk;
+    // all of it is free once T' is formed
     __device__ static constexpr int q_off(int w, int I) { return (w * 4 + I) * 1024; }
     __device__ static constexpr int g_off(int w, int I, int half) { return 16384 + ((w * 4 + I) * 2 + half) * 1024; }
     __device__ static constexpr int k_off(int w, int I) { return 49152 + (w * 4 + I) * 1024; }
@@ -350,10 +350,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             const int row = 16 * I + m;
             if (cvalid && row < L) {
                 const size_t off = (size_t)(t0 + row) * rowq + (size_t)h * DK + c0;
-                lds_load16(g + off, sRb + Stg::g_off(wave, I, 0));
-                lds_load16(g + off + 4, sRb + Stg::g_off(wave, I, 1));
                 lds_load16(k + off, sRb + Stg::k_off(wave, I));
                 lds_load16(q + off, sRb + Stg::q_off(wave, I));
+            }
+            // g (float32): eight lanes per row, so each load covers whole 128-byte rows of the
+            // slice (rows 8 hg .. 8 hg + 7 of the block)
+#pragma unroll
+            for (int hg = 0; hg < 2; ++hg) {
+                const int grow = 16 * I + 8 * hg + (lane >> 3), gc = 32 * wave + 4 * (lane & 7);
+                if (cs && gc < DK && grow < L)
+                    lds_load16(g + (size_t)(t0 + grow) * rowq + (size_t)h * DK + gc,
+                               sRb + Stg::g_off(wave, I, hg));
             }
             if (I == 0 && wave == 0 && lane < L) {
                 const size_t e = (size_t)(t0 + lane) * H + h;       // beta element index
@@ -394,8 +401,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             for (int I = 0; I < 4; ++I) {
                 const int row = 16 * I + m;
                 if (cvalid && row < L) {
-                    const floatx4 g0 = reinterpret_cast<const floatx4*>(sRb + Stg::g_off(wave, I, 0))[lane];
-                    const floatx4 g1 = reinterpret_cast<const floatx4*>(sRb + Stg::g_off(wave, I, 1))[lane];
+                    // row m of the block sits in part m / 8, its 8 channels at 16-byte slots
+                    // 8 (m % 8) + 2 grp and the next
+                    const floatx4* gp = reinterpret_cast<const floatx4*>(sRb + Stg::g_off(wave, I, m >> 3)) +
+                                        8 * (m & 7) + 2 * grp;
+                    const floatx4 g0 = gp[0], g1 = gp[1];
                     G[8 * I] = g0[0]; G[8 * I + 1] = g0[1]; G[8 * I + 2] = g0[2]; G[8 * I + 3] = g0[3];
                     G[8 * I + 4] = g1[0]; G[8 * I + 5] = g1[1]; G[8 * I + 6] = g1[2]; G[8 * I + 7] = g1[3];
                     K.set(I, reinterpret_cast<const u32x4*>(sRb + Stg::k_off(wave, I))[lane]);
