@@ -240,6 +240,15 @@ struct PolF32 {
     __device__ static __forceinline__ void mma_copy(floatx4& acc, const Frag& x, const Frag& e) {
         mma(acc, x, e);
     }
+    // x times a 0/1 selection matrix e (a transpose, exact) as a 16-wide K fragment
+    __device__ static __forceinline__ Frag4 transpose4(const Frag& x, const Frag& e) {
+        floatx4 t = {0.f, 0.f, 0.f, 0.f};
+        mma(t, x, e);
+        Frag4 f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f.v[r] = t[r];
+        return f;
+    }
 };
 
 struct PolSplit {
@@ -515,6 +524,20 @@ struct PolSplit {
     // x (exact in bfloat16, x.lo == 0) times an exact 0/1 matrix e: one MFMA
     __device__ static __forceinline__ void mma_copy(floatx4& acc, const Frag& x, const Frag& e) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.hi, e.hi, acc, 0, 0, 0);
+    }
+    // x times a 0/1 selection matrix e (a transpose) as a 16-wide K fragment: the hi and lo
+    // parts are moved by one MFMA each, so both come out exact and need no new split
+    __device__ static __forceinline__ Frag4 transpose4(const Frag& x, const Frag& e) {
+        floatx4 th = {0.f, 0.f, 0.f, 0.f}, tl = {0.f, 0.f, 0.f, 0.f};
+        th = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.hi, e.hi, th, 0, 0, 0);
+        tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.lo, e.hi, tl, 0, 0, 0);
+        Frag4 f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            f.hi[r] = (bf16)th[r];
+            f.lo[r] = (bf16)tl[r];
+        }
+        return f;
     }
 };
 

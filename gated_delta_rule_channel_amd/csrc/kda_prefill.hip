@@ -811,9 +811,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                 }
 #pragma unroll
                 for (int hh = 0; hh < NH; ++hh) {
-                    floatx4 t = {0.f, 0.f, 0.f, 0.f};
-                    Pol::mma_exact(t, kg, Eid[hh]);           // lane (channel n, grp): tokens 4 grp + r
-                    const Frag4 a = frag4_of<Pol>(t);
+                    // lane (channel n, grp): tokens 4 grp + r
+                    const Frag4 a = Pol::transpose4(kg, Eid[hh]);
 #pragma unroll
                     for (int I = J; I < 4; ++I) Pol::mma16(accW[hh][I], a, sTp[tri_tile(I, J)][lane]);
                 }
