@@ -40,6 +40,15 @@ int kda_oracle_num_threads(void) {
 #endif
 }
 
+/* threads of the following calls (timing only; results do not depend on it) */
+void kda_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* One (sequence, head) chain over tokens [t0, t1). S is Dk*Dv doubles,
  * updated in place; o gets the outputs of the chain's tokens. */
 static void chain(const float* q, const float* k, const float* v, const float* g,

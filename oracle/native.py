@@ -47,12 +47,19 @@ def _load():
                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.kda_oracle_decode.restype = ctypes.c_int
         lib.kda_oracle_num_threads.restype = ctypes.c_int
+        lib.kda_oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.kda_oracle_set_num_threads.restype = None
         _lib = lib
     return _lib
 
 
 def num_threads() -> int:
     return int(_load().kda_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads used by the following calls (timing only)."""
+    _load().kda_oracle_set_num_threads(int(n))
 
 
 def _f32(x) -> np.ndarray:
