@@ -117,7 +117,10 @@ def _short(name):
     return None
 
 
-def traffic_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv):
+def traffic_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, out_file=None):
+    """Per-kernel HBM bytes from two FETCH_SIZE / WRITE_SIZE passes, scaled by what the same
+    counters read for a 1 GiB copy; written to out_file (the profiles JSON by default)."""
+    out_file = out_file or TRAFFIC_FILE
     cf = max(v for v, _ in _pmc_per_kernel(cfetch_csv, "FETCH_SIZE").values())
     cw = max(v for v, _ in _pmc_per_kernel(cwrite_csv, "WRITE_SIZE").values())
     f_fac = COPY_BYTES / (cf * 1024.0)
@@ -145,19 +148,21 @@ def traffic_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv):
         "decode_bytes": (per["decode_kernel"]["fetch_bytes"] + per["decode_kernel"]["write_bytes"]
                          if "decode_kernel" in per else None),
     }
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as fh:
+    os.makedirs(os.path.dirname(out_file), exist_ok=True)
+    with open(out_file, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
+    return out
 
 
-def load_traffic():
+def load_traffic(path=None):
     """Measured HBM bytes per prefill call and per decode step, or None when the counters
     were taken on different kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = path or TRAFFIC_FILE
+    if not os.path.exists(path):
         return None, None
     try:
-        d = json.load(open(TRAFFIC_FILE))
+        d = json.load(open(path))
     except (OSError, ValueError):
         return None, None
     if d.get("kernels_source_sha256") != kernels_source_hash():
