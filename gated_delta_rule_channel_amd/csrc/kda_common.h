@@ -145,30 +145,18 @@ struct PolF32 {
     __device__ static __forceinline__ void put(Store* base, size_t i, size_t /*ps*/, float x) {
         base[i] = x;
     }
-    __device__ static __forceinline__ float get(const Store* base, size_t i, size_t /*ps*/) {
-        return base[i];
-    }
     // 8 consecutive stored elements (32-byte aligned) into a fragment
     __device__ static __forceinline__ void load(Frag& f, const Store* base, size_t i,
                                                 size_t /*ps*/) {
         load8f(f.v, base + i);
-    }
-    __device__ static __forceinline__ void store(Store* base, size_t i, size_t /*ps*/,
-                                                 const Frag& f) {
-        reinterpret_cast<float4*>(base + i)[0] = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
-        reinterpret_cast<float4*>(base + i)[1] = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
     }
     // 4 consecutive elements (16-byte aligned)
     __device__ static __forceinline__ void store4(Store* base, size_t i, size_t /*ps*/, float a,
                                                   float b, float c, float d) {
         *reinterpret_cast<float4*>(base + i) = make_float4(a, b, c, d);
     }
-    __device__ static __forceinline__ float4 load4f(const Store* base, size_t i, size_t /*ps*/) {
-        return *reinterpret_cast<const float4*>(base + i);
-    }
     // ---- fragment tiles in the workspace (two 1 KB parts, lane-contiguous 16 B each) ----
     // part 0 holds elements 0..3 of every lane, part 1 elements 4..7
-    static constexpr int kTileBytes = 2048;
     using Tile = Frag;                      // fp32 tiles are used as loaded
     __device__ static __forceinline__ void tile_store_vals(void* t, int lane, const float* x) {
         float4* p = reinterpret_cast<float4*>(t);
@@ -227,11 +215,6 @@ struct PolF32 {
         r = reinterpret_cast<const float4*>(t)[lane];
     }
     __device__ static __forceinline__ float4 utile_decode(const URaw& r) { return r; }
-    // elements 4 half .. 4 half + 3 of a lane's fragment
-    __device__ static __forceinline__ void tile_store_quad(void* t, int lane, int half, float a,
-                                                           float b, float c, float d) {
-        reinterpret_cast<float4*>(t)[64 * half + lane] = make_float4(a, b, c, d);
-    }
     // product with b exact in the leading part (same as mma16 in fp32)
     __device__ static __forceinline__ void mma16_exact(floatx4& acc, const Frag4& a, const Frag4& b) {
         mma16(acc, a, b);
@@ -303,17 +286,9 @@ struct PolSplit {
         base[i] = h;
         base[ps + i] = (bf16)(x - (float)h);
     }
-    __device__ static __forceinline__ float get(const Store* base, size_t i, size_t ps) {
-        return (float)base[i] + (float)base[ps + i];
-    }
     __device__ static __forceinline__ void load(Frag& f, const Store* base, size_t i, size_t ps) {
         f.hi = *reinterpret_cast<const bf16x8*>(base + i);
         f.lo = *reinterpret_cast<const bf16x8*>(base + ps + i);
-    }
-    __device__ static __forceinline__ void store(Store* base, size_t i, size_t ps,
-                                                 const Frag& f) {
-        *reinterpret_cast<bf16x8*>(base + i) = f.hi;
-        *reinterpret_cast<bf16x8*>(base + ps + i) = f.lo;
     }
     // 4 consecutive elements (8-byte aligned in each plane)
     __device__ static __forceinline__ void store4(Store* base, size_t i, size_t ps, float a,
@@ -325,15 +300,8 @@ struct PolSplit {
         *reinterpret_cast<bf16x4*>(base + i) = h;
         *reinterpret_cast<bf16x4*>(base + ps + i) = l;
     }
-    __device__ static __forceinline__ float4 load4f(const Store* base, size_t i, size_t ps) {
-        const bf16x4 h = *reinterpret_cast<const bf16x4*>(base + i);
-        const bf16x4 l = *reinterpret_cast<const bf16x4*>(base + ps + i);
-        return make_float4((float)h[0] + (float)l[0], (float)h[1] + (float)l[1],
-                           (float)h[2] + (float)l[2], (float)h[3] + (float)l[3]);
-    }
-    // ---- fragment tiles in the workspace (1.5 KB): part 0 (1 KB) holds the eight hi
-    // values of every lane (16 B), part 1 (512 B) their extension bytes (8 B) ----
-    static constexpr int kTileBytes = 1536;
+    // ---- 24-bit fragments: the eight hi values of a lane (16 B) and their extension bytes
+    // (8 B), as held in registers after a pair tile load ----
     struct Tile { bf16x8 hi; u32x2 ext; };
     // x rounded to 24 bits of float32 (16 significant bits), half-way cases away from zero;
     // the low byte is left as is (callers take bytes 1..3 only)
@@ -344,34 +312,6 @@ struct PolSplit {
                                                     unsigned d) {
         return ((a >> 8) & 0xffu) | (b & 0xff00u) | ((c << 8) & 0xff0000u) |
                ((d << 16) & 0xff000000u);
-    }
-    __device__ static __forceinline__ void tile_store_vals(void* t, int lane, const float* x) {
-        unsigned r[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = round24(x[e]);
-        u32x4 hw;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) hw[p] = (r[2 * p] >> 16) | (r[2 * p + 1] & 0xffff0000u);
-        u32x2 ew;
-        ew[0] = ext4(r[0], r[1], r[2], r[3]);
-        ew[1] = ext4(r[4], r[5], r[6], r[7]);
-        reinterpret_cast<u32x4*>(t)[lane] = hw;
-        reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(t) + 1024)[lane] = ew;
-    }
-    // elements 4 half .. 4 half + 3 of a lane's fragment
-    __device__ static __forceinline__ void tile_store_quad(void* t, int lane, int half, float a,
-                                                           float b, float c, float d) {
-        const unsigned r0 = round24(a), r1 = round24(b), r2 = round24(c), r3 = round24(d);
-        u32x2 hw;
-        hw[0] = (r0 >> 16) | (r1 & 0xffff0000u);
-        hw[1] = (r2 >> 16) | (r3 & 0xffff0000u);
-        reinterpret_cast<u32x2*>(t)[2 * lane + half] = hw;
-        reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(t) + 1024)[2 * lane + half] =
-            ext4(r0, r1, r2, r3);
-    }
-    __device__ static __forceinline__ void tile_load_raw(Tile& r, const void* t, int lane) {
-        r.hi = reinterpret_cast<const bf16x8*>(t)[lane];
-        r.ext = reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(t) + 1024)[lane];
     }
     // hi as stored; lo = (hi with its extension byte) - hi, exact in bfloat16. The two
     // 24-bit values of a word pair are assembled with one byte permute each (v_perm_b32:
@@ -409,18 +349,6 @@ struct PolSplit {
         reinterpret_cast<u32x4*>(t)[64 * which + lane] = hw;
         // half of every 16 B: the other wave of the pair writes the rest, merged in L2
         reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(t) + 2048)[2 * lane + which] = ew;
-    }
-    __device__ static __forceinline__ void pair_store_quad(void* t, int lane, int which, int half,
-                                                           float a, float b, float c, float d) {
-        const unsigned r0 = round24(a), r1 = round24(b), r2 = round24(c), r3 = round24(d);
-        u32x2 hw;
-        hw[0] = (r0 >> 16) | (r1 & 0xffff0000u);
-        hw[1] = (r2 >> 16) | (r3 & 0xffff0000u);
-        // partial 16-byte groups (the other halves come from other lanes or waves): plain
-        // stores, merged in L2
-        reinterpret_cast<u32x2*>(t)[128 * which + 2 * lane + half] = hw;
-        reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(t) + 2048)[4 * lane + 2 * which + half] =
-            ext4(r0, r1, r2, r3);
     }
     __device__ static __forceinline__ void pair_load(Pair& r, const void* t, int lane) {
         const bf16x8* p = reinterpret_cast<const bf16x8*>(t);
@@ -559,17 +487,6 @@ __device__ __forceinline__ void pin(float4& x) {
 }
 
 // ---- cross-lane helpers (a DPP row = 16 consecutive lanes = one value of grp) ------------
-// inclusive prefix sum over the 16 lanes of each row
-__device__ __forceinline__ float row_scan16(float x) {
-    int v = __builtin_bit_cast(int, x);
-    float s = x;
-    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x111, 0xf, 0xf, true));
-    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x112, 0xf, 0xf, true));
-    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x114, 0xf, 0xf, true));
-    s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x118, 0xf, 0xf, true));
-    (void)v;
-    return s;
-}
 // one step (row_shr by 1, 2, 4 or 8 lanes: CTRL 0x111, 0x112, 0x114, 0x118) of the
 // inclusive row prefix sum, applied to 32 independent values
 template <int CTRL>
