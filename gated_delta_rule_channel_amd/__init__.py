@@ -97,9 +97,23 @@ def workspace_size(B: int, T: int, H: int, Dk: int, Dv: int, num_seqs: int, varl
 
 
 def _check_gpu(*ts):
+    ts = [t for t in ts if t is not None]
     for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous GPU tensors")
+    if len({t.device for t in ts}) > 1:
+        raise ValueError("all tensors must be on the same device")
+
+
+def _check_shape(name, t, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_same_dtype(ref, **ts):
+    for name, t in ts.items():
+        if t.dtype != ref.dtype:
+            raise TypeError(f"{name} is {t.dtype}, q is {ref.dtype}: q, k, v and beta share one dtype")
 
 
 def fwd_chunked(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
@@ -111,18 +125,32 @@ def fwd_chunked(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
     Returns (o [B,T,H,Dv], ht [N,H,Dk,Dv] float32 or None)."""
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
-    _check_gpu(q, k, v, g, beta, initial_state, cu_seqlens, workspace, out, final_state)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, g must be [B,T,H,Dk] and v [B,T,H,Dv]")
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     code = _dtype_code(q)
+    _check_same_dtype(q, k=k, v=v, beta=beta)
     varlen = cu_seqlens is not None
     N = (cu_seqlens.numel() - 1) if varlen else B
+    _check_shape("k", k, (B, T, H, Dk))
+    _check_shape("g", g, (B, T, H, Dk))
+    _check_shape("v", v, (B, T, H, Dv))
+    _check_shape("beta", beta, (B, T, H))
+    _check_shape("initial_state", initial_state, (N, H, Dk, Dv))
+    _check_shape("out", out, (B, T, H, Dv))
+    _check_shape("final_state", final_state, (N, H, Dk, Dv))
     if g.dtype != torch.float32:
         raise TypeError("g must be float32")
     if initial_state is not None and initial_state.dtype != torch.float32:
         raise TypeError("initial_state must be float32")
-    if varlen and cu_seqlens.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
+    if final_state is not None and final_state.dtype != torch.float32:
+        raise TypeError("final_state must be float32")
+    if varlen and (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1):
+        raise TypeError("cu_seqlens must be a 1-D int32 tensor")
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
+    _check_gpu(q, k, v, g, beta, initial_state, cu_seqlens, workspace, out, final_state)
     nbytes = workspace_size(B, T, H, Dk, Dv, N, varlen, code)
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
@@ -146,12 +174,21 @@ def decode_step(q, k, v, g, beta, state, scale: float = 1.0, out=None, out_dtype
     state: [N,H,Dk,Dv] float32, updated in place. Returns o [N,H,Dv] (float32 by default)."""
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
-    _check_gpu(q, k, v, g, beta, state, out)
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, g must be [N,H,Dk] and v [N,H,Dv]")
     N, H, Dk = q.shape
     Dv = v.shape[-1]
     code = _dtype_code(q)
+    _check_same_dtype(q, k=k, v=v, beta=beta)
+    _check_shape("k", k, (N, H, Dk))
+    _check_shape("g", g, (N, H, Dk))
+    _check_shape("v", v, (N, H, Dv))
+    _check_shape("beta", beta, (N, H))
+    _check_shape("state", state, (N, H, Dk, Dv))
+    _check_shape("out", out, (N, H, Dv))
     if g.dtype != torch.float32 or state.dtype != torch.float32:
         raise TypeError("g and state must be float32")
+    _check_gpu(q, k, v, g, beta, state, out)
     o = out if out is not None else torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
     st = load_library().kda_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(state), _ptr(o),

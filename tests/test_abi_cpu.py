@@ -115,3 +115,33 @@ def test_decode_validation(lib):
     assert f(dtype=2) == E
     assert f(odtype=3) == E
     assert f(state=FAKE + 4) == E
+
+
+def test_binding_rejects_mismatched_arguments():
+    """The binding checks shapes and dtypes on the host before anything reaches the
+    library (a wrong shape would otherwise make a kernel read past a buffer)."""
+    import torch
+    kda = pytest.importorskip("gated_delta_rule_channel_amd")
+    B, T, H, D = 1, 64, 2, 16
+    q = torch.zeros(B, T, H, D, dtype=torch.bfloat16)
+    g = torch.zeros(B, T, H, D)
+    beta = torch.zeros(B, T, H, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="v has shape"):
+        kda.fwd_chunked(q, q, torch.zeros(B, T + 1, H, D, dtype=torch.bfloat16), g, beta)
+    with pytest.raises(TypeError, match="share one dtype"):
+        kda.fwd_chunked(q, q, torch.zeros(B, T, H, D), g, beta)
+    with pytest.raises(ValueError, match="beta has shape"):
+        kda.fwd_chunked(q, q, q, g, torch.zeros(B, T, H + 1, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="initial_state has shape"):
+        kda.fwd_chunked(q, q, q, g, beta, initial_state=torch.zeros(B, H, D, D + 1))
+    with pytest.raises(ValueError, match="contiguous GPU"):
+        kda.fwd_chunked(q, q, q, g, beta)                     # well formed, but on the CPU
+    N = 3
+    qd = torch.zeros(N, H, D)
+    st = torch.zeros(N, H, D, D)
+    with pytest.raises(ValueError, match="state has shape"):
+        kda.decode_step(qd, qd, qd, qd, torch.zeros(N, H), torch.zeros(N, H, D, 2 * D))
+    with pytest.raises(ValueError, match="g has shape"):
+        kda.decode_step(qd, qd, qd, torch.zeros(N, H, D + 16), torch.zeros(N, H), st)
+    with pytest.raises(ValueError, match="contiguous GPU"):
+        kda.decode_step(qd, qd, qd, qd, torch.zeros(N, H), st)
