@@ -444,12 +444,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             if (tid < 64) sBeta[tid] = tid < L ? to_f(beta[(size_t)(t0 + tid) * H + h]) : 0.f;
         }
         // every wave has its inputs (and is past the previous task's reads of sCE): the staging
-        // region becomes the A accumulators
+        // region becomes the A accumulators (the first partial of each block is stored, the
+        // others added, so they need no clearing)
         __syncthreads();
-        for (int idx = tid; idx < 10 * 16 * 20; idx += 256) {
-            (&sKK[0][0][0])[idx] = 0.f;
-            (&sQK[0][0][0])[idx] = 0.f;
-        }
 
         // ---- block-local prefix sums (log2 units); the cumulative value at each block end goes
         //      to LDS (all 16 lanes of a row hold it), the chunk total stays in registers ----
@@ -502,9 +499,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         // ---- rotated pass over the row blocks: Qd, Kd^T, partial A blocks. The row block of
         //      a step depends on the wave; each row block is its own instance of the step, so
         //      the register arrays are indexed with constants ----
-        auto row_step = [&](auto Ic) {
+        auto row_step = [&](auto Ic, int st) {
             constexpr int I = decltype(Ic)::value;
             constexpr int Ip = I > 0 ? I - 1 : 0;
+            // the blocks of row I (and the pair (3, 0) with row 0) get their first partial from
+            // the channel-slice wave that reaches row I first: wave min(I, NSL - 1), at this step
+            const bool first = st == I - (I < NSL - 1 ? I : NSL - 1);
             // the step reads its inputs through empty asm statements, so that no part of it is
             // computed ahead of the loop (that would keep every row block's operands live)
             auto opq = [](float x) { asm volatile("" : "+v"(x)); return x; };
@@ -615,7 +615,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                 }
                 float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(I, I)][m][4 * grp]);
                 float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(I, I)][m][4 * grp]);
-                float4 a = *pk, c = *pq;
+                float4 a = make_float4(0.f, 0.f, 0.f, 0.f), c = a;
+                if (!first) {
+                    a = *pk;
+                    c = *pq;
+                }
                 a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
                 c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
                 *pk = a;
@@ -644,7 +648,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                 Pol::mma(aqk, b, QA2);
                 float4* pk = reinterpret_cast<float4*>(&sKK[tri_tile(II, J)][m][4 * grp]);
                 float4* pq = reinterpret_cast<float4*>(&sQK[tri_tile(II, J)][m][4 * grp]);
-                float4 a = *pk, c = *pq;
+                float4 a = make_float4(0.f, 0.f, 0.f, 0.f), c = a;
+                if (!first) {
+                    a = *pk;
+                    c = *pq;
+                }
                 a.x += akk[0]; a.y += akk[1]; a.z += akk[2]; a.w += akk[3];
                 c.x += aqk[0]; c.y += aqk[1]; c.z += aqk[2]; c.w += aqk[3];
                 *pk = a;
@@ -674,10 +682,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         for (int st = 0; st < 4; ++st) {
             if (cs) {
                 switch ((wave + st) & 3) {                    // wave-uniform
-                    case 0: row_step(std::integral_constant<int, 0>{}); break;
-                    case 1: row_step(std::integral_constant<int, 1>{}); break;
-                    case 2: row_step(std::integral_constant<int, 2>{}); break;
-                    default: row_step(std::integral_constant<int, 3>{}); break;
+                    case 0: row_step(std::integral_constant<int, 0>{}, st); break;
+                    case 1: row_step(std::integral_constant<int, 1>{}, st); break;
+                    case 2: row_step(std::integral_constant<int, 2>{}, st); break;
+                    default: row_step(std::integral_constant<int, 3>{}, st); break;
                 }
             }
             __syncthreads();
