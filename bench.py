@@ -61,10 +61,13 @@ def prefill_flops(T, H, Dk, Dv, C=64):
     return per_chunk * H * (T // C)
 
 
-def _code_only(text: str) -> str:
+def _code_only(text: str, python: bool = False) -> str:
     """Source text without comments and blank space, so that comment edits keep the hash."""
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
+    if python:
+        text = re.sub(r"#[^\n]*", " ", text)
+    else:
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
     return " ".join(text.split())
 
 
@@ -77,7 +80,7 @@ def kernels_source_hash():
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "r", encoding="utf-8", errors="replace") as fh:
-            h.update(_code_only(fh.read()).encode())
+            h.update(_code_only(fh.read(), python=f.endswith(".py")).encode())
     return h.hexdigest()
 
 

@@ -94,3 +94,7 @@ def test_traffic_summary_calibration(tmp_path):
     d["kernels_source_sha256"] = "0" * 64
     json.dump(d, open(out_file, "w"))
     assert bench.load_traffic(out_file) == (None, None)
+
+
+def test_code_hash_ignores_python_comments():
+    assert bench._code_only("x = 1  # one\n# two\n", python=True) == bench._code_only("x = 1", python=True)
