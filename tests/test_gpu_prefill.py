@@ -59,6 +59,14 @@ def test_main_prefill_full():
     _compare(I.prefill_inputs(w), w.dtype)
 
 
+def test_batched_full_heads_with_ragged_tail():
+    """B2 T4100 H64 d128 bf16, the main workload's generators and launch shape with two
+    sequences of a partial last chunk: every head against the oracle."""
+    w = dataclasses.replace(I.WORKLOADS[2], B=2, T=4100)
+    print(f"[prefill] {w.name} B2 T4100", flush=True)
+    _compare(I.prefill_inputs(w), w.dtype)
+
+
 def test_varlen_long_context_full():
     """8 packed sequences (lengths ~U[1024, 32768]) with near-0 and near-1 decay channels.
 
