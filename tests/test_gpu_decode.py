@@ -74,3 +74,38 @@ def test_decode_bf16_output_is_rounded_fp32_output():
     torch.cuda.synchronize()
     assert torch.equal(o16, o32.to(torch.bfloat16))
     assert torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_gate_closed_is_pure_decay(dtype):
+    """beta = 0: S' = diag(exp(g)) S exactly as written, and o = scale q^T S'."""
+    import dataclasses
+    w = dataclasses.replace(I.WORKLOADS[3], H=4, N=9, dtype=dtype)
+    x = I.decode_inputs(w)
+    x.beta = torch.zeros_like(x.beta)
+    x.scale = 0.5
+    print(f"[decode] beta = 0 {dtype}", flush=True)
+    o_ref, S_ref = native.decode(x.q, x.k, x.v, x.g, x.beta, x.state, scale=0.5)
+    o, S = _run(x, dtype)
+    check("o", o, o_ref, dtype)
+    check("state", S, S_ref, dtype)
+    S_cf = np.exp(x.g.double().numpy())[..., None] * x.state.double().numpy()
+    o_cf = 0.5 * np.einsum("nhi,nhij->nhj", x.q.double().numpy(), S_cf)
+    check("state (closed form)", S, S_cf, "f32")
+    check("o (closed form)", o, o_cf, dtype)
+
+
+def test_decode_no_decay_unit_beta_stores_pair():
+    """g = 0, beta = 1 with unit-norm keys: after the step k^T S' = v for every request."""
+    import dataclasses
+    w = dataclasses.replace(I.WORKLOADS[3], H=4, N=9, dtype="f32")
+    x = I.decode_inputs(w)
+    x.g = torch.zeros_like(x.g)
+    x.beta = torch.ones_like(x.beta)
+    print("[decode] g = 0, beta = 1", flush=True)
+    o_ref, S_ref = native.decode(x.q, x.k, x.v, x.g, x.beta, x.state)
+    o, S = _run(x, "f32")
+    check("o", o, o_ref, "f32")
+    check("state", S, S_ref, "f32")
+    got = np.einsum("nhi,nhij->nhj", x.k.double().numpy(), S.astype(np.float64))
+    check("k^T S' vs v", got, x.v.double().numpy(), "f32")

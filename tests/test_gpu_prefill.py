@@ -160,6 +160,47 @@ def test_steep_decay_pairwise_path(dtype):
     _compare(x, dtype)
 
 
+def _mild_decay(x, seed):
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy(-rng.uniform(0.0, 0.02, size=tuple(x.g.shape))).float()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gate_closed_beta_is_pure_decay(dtype):
+    """beta = 0 writes nothing: the state only decays, S_t = diag(exp(g_t)) S_(t-1), and
+    o_t = scale q_t^T diag(exp(G_t)) h0 with G_t the running sum of g. Checked against that
+    closed form as well as the oracle, over three chunks and a ragged tail."""
+    w = dataclasses.replace(I.WORKLOADS[1], B=1, T=200, H=2, Dk=64, Dv=64, dtype=dtype)
+    x = I.prefill_inputs(w)
+    x.g = _mild_decay(x, 77)
+    x.beta = torch.zeros_like(x.beta)
+    print(f"[prefill] beta = 0 {dtype}", flush=True)
+    fo, fs = _compare(x, dtype)
+    o, ht = _gpu(x)
+    G = np.cumsum(x.g.double().numpy(), axis=1)                        # [1, T, H, Dk]
+    h0 = x.h0.double().numpy()[0]                                      # [H, Dk, Dv]
+    q = x.q.double().numpy()[0]                                        # [T, H, Dk]
+    o_cf = x.scale * np.einsum("thi,hij->thj", q * np.exp(G[0]), h0)[None]
+    ht_cf = (np.exp(G[0, -1])[:, :, None] * h0)[None]
+    check("o (closed form)", o, o_cf, dtype)
+    check("ht (closed form)", ht, ht_cf, dtype)
+
+
+def test_no_decay_unit_beta_stores_last_pair():
+    """g = 0, beta = 1 is the plain delta rule: with a unit-norm key the write overwrites the
+    value stored along k, so k_T^T S_T = v_T for the last token of every head."""
+    w = dataclasses.replace(I.WORKLOADS[1], B=1, T=200, H=3, Dk=64, Dv=64)
+    x = I.prefill_inputs(w)
+    x.g = torch.zeros_like(x.g)
+    x.beta = torch.ones_like(x.beta)
+    print("[prefill] g = 0, beta = 1", flush=True)
+    _compare(x, "f32")
+    _, ht = _gpu(x)
+    k_last = x.k.double().numpy()[0, -1]                               # [H, Dk]
+    got = np.einsum("hi,hij->hj", k_last, ht[0].astype(np.float64))
+    check("k_T^T S_T vs v_T", got, x.v.double().numpy()[0, -1], "f32")
+
+
 def test_resume_split_equals_one_pass():
     """[0, T1) then [T1, T) with ht -> h0 equals one pass; T1 is not a chunk multiple."""
     w = I.WORKLOADS[1]
