@@ -20,7 +20,11 @@ round-to-nearest-even; consumers that need float64 upcast the cast values):
 * the varlen workload picks, per head, 13 "fast" channels with
   g ~ -U(5, 10) and 13 disjoint "slow" channels with g ~ -U(0, 1e-4)
   (about 10 % of 128 each), per token;
-* initial states are 0.1 * N(0, 1) where a workload asks for one.
+* initial states are 0.1 * N(0, 1) where a workload asks for one;
+* Gated DeltaNet inputs (scalar gate) reuse q, k, v, beta and states of the
+  same workload and replace g by one log-decay per (token, head),
+  -softplus(N(0, 1)) times U(0.5, 2) where the workload scales g, from a
+  stream of its own.
 
 Shapes follow the library: q, k, g are [B, T, H, Dk], v is [B, T, H, Dv],
 beta is [B, T, H]; varlen packs sequences along T with B = 1 and int32
@@ -37,7 +41,7 @@ import numpy as np
 import torch
 
 # tensor ids of the per-head streams
-_Q, _K, _V, _BETA, _G, _GFAC, _CHAN, _STATE, _LEN = range(1, 10)
+_Q, _K, _V, _BETA, _G, _GFAC, _CHAN, _STATE, _LEN, _GSC = range(1, 11)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -247,3 +251,33 @@ def decode_inputs(w: Workload, heads: Optional[Sequence[int]] = None,
     with _cf.ThreadPoolExecutor(_n_threads()) as ex:
         list(ex.map(fill, list(enumerate(heads))))
     return DecodeInputs(q=q, k=k, v=v, g=g, beta=beta, state=state, heads=heads)
+
+
+def scalar_gate(w: Workload, heads: Sequence[int], ntok: int) -> torch.Tensor:
+    """Gated DeltaNet log-decay, one value per (token, head): float32 [ntok, len(heads)]."""
+    out = torch.empty((ntok, len(heads)), dtype=torch.float32)
+    for j, h in enumerate(heads):
+        rng = _rng(w.wid, _GSC, h)
+        gg = -_softplus(rng.standard_normal(ntok))
+        if w.g_factor:
+            gg = gg * rng.uniform(0.5, 2.0, size=ntok)
+        out[:, j] = _cast(gg, torch.float32)
+    return out
+
+
+def gdn_prefill_inputs(w: Workload, heads: Optional[Sequence[int]] = None,
+                       T: Optional[int] = None,
+                       lengths: Optional[Sequence[int]] = None) -> PrefillInputs:
+    """prefill_inputs with g replaced by a scalar gate g [B, T, H] (Gated DeltaNet)."""
+    x = prefill_inputs(w, heads=heads, T=T, lengths=lengths)
+    B, Tt, Hs = x.beta.shape
+    x.g = scalar_gate(w, x.heads, B * Tt).view(B, Tt, Hs)
+    return x
+
+
+def gdn_decode_inputs(w: Workload, heads: Optional[Sequence[int]] = None,
+                      N: Optional[int] = None) -> DecodeInputs:
+    """decode_inputs with g replaced by a scalar gate g [N, H] (Gated DeltaNet)."""
+    x = decode_inputs(w, heads=heads, N=N)
+    x.g = scalar_gate(w, x.heads, x.beta.shape[0])
+    return x

@@ -21,6 +21,10 @@
  * Layouts: q, k, g [Ttot, H, Dk]; v [Ttot, H, Dv]; beta [Ttot, H];
  * states [N, H, Dk, Dv] with row = key channel.
  *
+ * With a scalar gate (Gated DeltaNet: "Notes on Linear Attention",
+ * zhilingong.com, section 6) g is [Ttot, H] and step (1) scales every row of
+ * S by the same exp(g_t); the other steps are unchanged.
+ *
  * Parity pins: the Python test-suite checks this file against the numpy
  * oracle (same definition, written independently) on the small workloads.
  */
@@ -52,16 +56,16 @@ void kda_oracle_set_num_threads(int n) {
 /* One (sequence, head) chain over tokens [t0, t1). S is Dk*Dv doubles,
  * updated in place; o gets the outputs of the chain's tokens. */
 static void chain(const float* q, const float* k, const float* v, const float* g,
-                  const float* beta, double scale, int H, int Dk, int Dv, int h,
+                  int scalar_gate, const float* beta, double scale, int H, int Dk, int Dv, int h,
                   int64_t t0, int64_t t1, double* S, double* o,
                   double* vhat, double* err, double* dec) {
     for (int64_t t = t0; t < t1; ++t) {
         const float* qt = q + (t * H + h) * (int64_t)Dk;
         const float* kt = k + (t * H + h) * (int64_t)Dk;
         const float* vt = v + (t * H + h) * (int64_t)Dv;
-        const float* gt = g + (t * H + h) * (int64_t)Dk;
+        const float* gt = g + (t * H + h) * (int64_t)(scalar_gate ? 1 : Dk);
         const double b = (double)beta[t * H + h];
-        for (int c = 0; c < Dk; ++c) dec[c] = exp((double)gt[c]);
+        for (int c = 0; c < Dk; ++c) dec[c] = exp((double)gt[scalar_gate ? 0 : c]);
         /* (1) forget */
         for (int c = 0; c < Dk; ++c)
             for (int j = 0; j < Dv; ++j) S[c * Dv + j] *= dec[c];
@@ -90,10 +94,11 @@ static void chain(const float* q, const float* k, const float* v, const float* g
 
 /* Prefill over packed sequences. cu_seqlens is int32[num_seqs + 1] with
  * cu[0] = 0 (fixed-length batches pass n*T). h0 may be NULL (zero state).
+ * g is [Ttot, H, Dk], or [Ttot, H] when scalar_gate is non-zero.
  * o: double [Ttot, H, Dv]; ht: double [num_seqs, H, Dk, Dv] (may be NULL).
  * Returns 0, or -1 on allocation failure. */
 int kda_oracle_prefill(const float* q, const float* k, const float* v, const float* g,
-                       const float* beta, double scale, const float* h0,
+                       int scalar_gate, const float* beta, double scale, const float* h0,
                        const int32_t* cu_seqlens, int num_seqs, int H, int Dk, int Dv,
                        double* o, double* ht) {
     int failed = 0;
@@ -108,7 +113,8 @@ int kda_oracle_prefill(const float* q, const float* k, const float* v, const flo
         double* dec = err + Dv;
         const float* h0p = h0 ? h0 + ((int64_t)n * H + h) * (int64_t)Dk * Dv : NULL;
         for (int64_t i = 0; i < (int64_t)Dk * Dv; ++i) S[i] = h0p ? (double)h0p[i] : 0.0;
-        chain(q, k, v, g, beta, scale, H, Dk, Dv, h, cu_seqlens[n], cu_seqlens[n + 1], S, o,
+        chain(q, k, v, g, scalar_gate, beta, scale, H, Dk, Dv, h, cu_seqlens[n],
+              cu_seqlens[n + 1], S, o,
               vhat, err, dec);
         if (ht) memcpy(ht + ((int64_t)n * H + h) * (int64_t)Dk * Dv, S,
                        sizeof(double) * (size_t)Dk * Dv);
@@ -117,10 +123,11 @@ int kda_oracle_prefill(const float* q, const float* k, const float* v, const flo
     return failed ? -1 : 0;
 }
 
-/* One decode step: q, k, g [N, H, Dk]; v [N, H, Dv]; beta [N, H];
- * state double [N, H, Dk, Dv] updated in place; o double [N, H, Dv]. */
+/* One decode step: q, k [N, H, Dk]; g [N, H, Dk] ([N, H] with scalar_gate);
+ * v [N, H, Dv]; beta [N, H]; state double [N, H, Dk, Dv] updated in place;
+ * o double [N, H, Dv]. */
 int kda_oracle_decode(const float* q, const float* k, const float* v, const float* g,
-                      const float* beta, double scale, double* state, double* o,
+                      int scalar_gate, const float* beta, double scale, double* state, double* o,
                       int N, int H, int Dk, int Dv) {
     int failed = 0;
     const int64_t pairs = (int64_t)N * H;
@@ -131,7 +138,8 @@ int kda_oracle_decode(const float* q, const float* k, const float* v, const floa
         /* a decode step is one token of a chain whose "time" index is the pair */
         const int n = (int)(p / H), h = (int)(p % H);
         chain(q + (int64_t)n * H * Dk, k + (int64_t)n * H * Dk, v + (int64_t)n * H * Dv,
-              g + (int64_t)n * H * Dk, beta + (int64_t)n * H, scale, H, Dk, Dv, h, 0, 1,
+              g + (int64_t)n * H * (scalar_gate ? 1 : Dk), scalar_gate, beta + (int64_t)n * H,
+              scale, H, Dk, Dv, h, 0, 1,
               state + p * (int64_t)Dk * Dv, o + (int64_t)n * H * Dv, tmp, tmp + Dv,
               tmp + 2 * Dv);
         free(tmp);

@@ -23,10 +23,18 @@ Recurrence" (jared-hpc.com), section 2:
 Implementations keep g_t = log(alpha_t) <= 0 and decay by exp(g_t)
 (brain.bigb.es, "KDA: one gate per key channel").
 
+Gated DeltaNet (gdn_forward, gdn_decode) is the same recurrence with one
+scalar retention gate alpha_t = exp(g_t) per token and head instead of one
+per key channel: decay the whole state, then apply the delta rule to the
+decayed state ("Notes on Linear Attention", zhilingong.com, section 6;
+"From Fast Weight Programmers to KDA", section "Gated Delta Networks").
+
 Parity pins: every function here is pinned by tests/test_oracle_pins.py
 (worked example, read-back, locality, orthogonal-key example, additive
 brute force, DeltaNet and Gated DeltaNet reductions, operator order,
-stability, chunked mirror, resume/varlen/decode consistency).
+stability, chunked mirror, resume/varlen/decode consistency; for the scalar
+gate: the matrix form alpha (I - beta k k^T) S + beta k v^T, the pure-decay
+closed form at beta = 0, and the per-channel recurrence with an equal gate).
 """
 from __future__ import annotations
 
@@ -123,3 +131,53 @@ def kda_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta:
     S = S + k[..., :, None] * err[..., None, :]                         # (4)
     o = np.einsum("nhkv,nhk->nhv", S, scale * q)                        # (5)
     return o, S
+
+
+def gdn_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta: np.ndarray,
+                scale: float = 1.0, h0: Optional[np.ndarray] = None,
+                cu_seqlens: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Gated DeltaNet, token by token (float64 results).
+
+    q, k: [B, T, H, Dk]; v: [B, T, H, Dv]; g, beta: [B, T, H] (g = log alpha, one
+    scalar per token and head); h0, cu_seqlens and the returns as in kda_forward.
+    Per token, following zhilingong.com section 6: S_bar = alpha_t S, then the delta
+    rule on the decayed state, S = S_bar + k_t (beta_t (v_t - S_bar^T k_t))^T, and the
+    read o_t = S^T (scale q_t) of the updated state.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    qf, kf, vf = q.reshape(B * T, H, Dk), k.reshape(B * T, H, Dk), v.reshape(B * T, H, Dv)
+    af = np.exp(g.reshape(B * T, H))                                    # alpha_t per head
+    bf = beta.reshape(B * T, H)
+    segs = _segments(B * T, B, T, cu_seqlens)
+    o = np.zeros((B * T, H, Dv))
+    ht = np.zeros((len(segs), H, Dk, Dv))
+    for n, (s, e_) in enumerate(segs):
+        S = np.zeros((H, Dk, Dv)) if h0 is None else np.array(h0[n], dtype=np.float64)
+        for t in range(s, e_):
+            S_bar = af[t][:, None, None] * S                            # retention gate
+            err = bf[t][:, None] * (vf[t] - np.einsum("hkv,hk->hv", S_bar, kf[t]))
+            S = S_bar + kf[t][:, :, None] * err[:, None, :]             # delta rule
+            o[t] = np.einsum("hkv,hk->hv", S, scale * qf[t])            # read
+        ht[n] = S
+    return o.reshape(B, T, H, Dv), ht
+
+
+def gdn_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta: np.ndarray,
+               state: np.ndarray, scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+    """One Gated DeltaNet step per (request, head): q, k [N, H, Dk]; v [N, H, Dv];
+    g, beta [N, H]; state [N, H, Dk, Dv]. Returns (o [N, H, Dv], new state)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    S_bar = np.exp(np.asarray(g, dtype=np.float64))[..., None, None] * np.asarray(
+        state, dtype=np.float64)
+    err = beta[..., None] * (v - np.einsum("nhkv,nhk->nhv", S_bar, k))
+    S = S_bar + k[..., :, None] * err[..., None, :]
+    return np.einsum("nhkv,nhk->nhv", S, scale * q), S

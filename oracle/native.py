@@ -39,11 +39,11 @@ def _load():
         fp = ctypes.POINTER(ctypes.c_float)
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(ctypes.c_int32)
-        lib.kda_oracle_prefill.argtypes = [fp, fp, fp, fp, fp, ctypes.c_double, fp, ip,
+        lib.kda_oracle_prefill.argtypes = [fp, fp, fp, fp, ctypes.c_int, fp, ctypes.c_double, fp, ip,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            dp, dp]
         lib.kda_oracle_prefill.restype = ctypes.c_int
-        lib.kda_oracle_decode.argtypes = [fp, fp, fp, fp, fp, ctypes.c_double, dp, dp,
+        lib.kda_oracle_decode.argtypes = [fp, fp, fp, fp, ctypes.c_int, fp, ctypes.c_double, dp, dp,
                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.kda_oracle_decode.restype = ctypes.c_int
         lib.kda_oracle_num_threads.restype = ctypes.c_int
@@ -76,12 +76,12 @@ def _p(a: np.ndarray, t):
     return a.ctypes.data_as(ctypes.POINTER(t))
 
 
-def prefill(q, k, v, g, beta, scale: float = 1.0, h0=None,
-            cu_seqlens: Optional[Sequence[int]] = None):
-    """Recurrence over [B, T, H, D] inputs; returns float64 (o [B,T,H,Dv], ht [N,H,Dk,Dv])."""
+def _prefill(q, k, v, g, beta, scale, h0, cu_seqlens, scalar_gate):
     qf, kf, vf, gf, bf = (_f32(x) for x in (q, k, v, g, beta))
     B, T, H, Dk = qf.shape
     Dv = vf.shape[-1]
+    if gf.shape != ((B, T, H) if scalar_gate else (B, T, H, Dk)):
+        raise ValueError(f"g has shape {gf.shape}")
     if cu_seqlens is None:
         cu = (np.arange(B + 1, dtype=np.int64) * T).astype(np.int32)
     else:
@@ -92,7 +92,7 @@ def prefill(q, k, v, g, beta, scale: float = 1.0, h0=None,
     ht = np.zeros((N, H, Dk, Dv), dtype=np.float64)
     rc = _load().kda_oracle_prefill(
         _p(qf, ctypes.c_float), _p(kf, ctypes.c_float), _p(vf, ctypes.c_float),
-        _p(gf, ctypes.c_float), _p(bf, ctypes.c_float), float(scale),
+        _p(gf, ctypes.c_float), int(scalar_gate), _p(bf, ctypes.c_float), float(scale),
         None if h0f is None else _p(h0f, ctypes.c_float), _p(cu, ctypes.c_int32), N, H, Dk, Dv,
         _p(o, ctypes.c_double), _p(ht, ctypes.c_double))
     if rc != 0:
@@ -100,11 +100,24 @@ def prefill(q, k, v, g, beta, scale: float = 1.0, h0=None,
     return o, ht
 
 
-def decode(q, k, v, g, beta, state, scale: float = 1.0):
-    """One step; returns float64 (o [N,H,Dv], new state [N,H,Dk,Dv])."""
+def prefill(q, k, v, g, beta, scale: float = 1.0, h0=None,
+            cu_seqlens: Optional[Sequence[int]] = None):
+    """Recurrence over [B, T, H, D] inputs; returns float64 (o [B,T,H,Dv], ht [N,H,Dk,Dv])."""
+    return _prefill(q, k, v, g, beta, scale, h0, cu_seqlens, False)
+
+
+def gdn_prefill(q, k, v, g, beta, scale: float = 1.0, h0=None,
+                cu_seqlens: Optional[Sequence[int]] = None):
+    """Gated DeltaNet (scalar gate g [B, T, H]); returns float64 (o, ht) as prefill."""
+    return _prefill(q, k, v, g, beta, scale, h0, cu_seqlens, True)
+
+
+def _decode(q, k, v, g, beta, state, scale, scalar_gate):
     qf, kf, vf, gf, bf = (_f32(x) for x in (q, k, v, g, beta))
     N, H, Dk = qf.shape
     Dv = vf.shape[-1]
+    if gf.shape != ((N, H) if scalar_gate else (N, H, Dk)):
+        raise ValueError(f"g has shape {gf.shape}")
     try:
         import torch
         if isinstance(state, torch.Tensor):
@@ -115,8 +128,18 @@ def decode(q, k, v, g, beta, state, scale: float = 1.0):
     o = np.zeros((N, H, Dv), dtype=np.float64)
     rc = _load().kda_oracle_decode(
         _p(qf, ctypes.c_float), _p(kf, ctypes.c_float), _p(vf, ctypes.c_float),
-        _p(gf, ctypes.c_float), _p(bf, ctypes.c_float), float(scale), _p(S, ctypes.c_double),
-        _p(o, ctypes.c_double), N, H, Dk, Dv)
+        _p(gf, ctypes.c_float), int(scalar_gate), _p(bf, ctypes.c_float), float(scale),
+        _p(S, ctypes.c_double), _p(o, ctypes.c_double), N, H, Dk, Dv)
     if rc != 0:
         raise MemoryError("kda_oracle_decode failed")
     return o, S
+
+
+def decode(q, k, v, g, beta, state, scale: float = 1.0):
+    """One step; returns float64 (o [N,H,Dv], new state [N,H,Dk,Dv])."""
+    return _decode(q, k, v, g, beta, state, scale, False)
+
+
+def gdn_decode(q, k, v, g, beta, state, scale: float = 1.0):
+    """One Gated DeltaNet step (g [N, H]); returns float64 (o, new state)."""
+    return _decode(q, k, v, g, beta, state, scale, True)

@@ -356,3 +356,92 @@ def test_native_decode_matches_numpy():
     o_c, S_c = native.decode(x.q, x.k, x.v, x.g, x.beta, x.state)
     assert _rel(o_c, o_ref) <= 1e-12
     assert _rel(S_c, S_ref) <= 1e-12
+
+
+# --- Gated DeltaNet (scalar gate) -------------------------------------------------------------
+def test_gdn_matrix_form():
+    """The scalar-gate oracle (decay, then the delta rule on the decayed state) equals the
+    matrix form S_t = alpha_t (I - beta_t k_t k_t^T) S_(t-1) + beta_t k_t v_t^T, the second
+    form of zhilingong.com section 6 and the recurrence on jonahsamost.bearblog.dev,
+    "Gated Delta Networks" (transposed there: S_t^T in this layout), with o_t = S_t^T q_t."""
+    rng = np.random.default_rng(61)
+    T, Dk, Dv = 24, 6, 5
+    q, k, v, beta = _random_seq(rng, T, Dk, Dv)
+    alpha = rng.uniform(0.2, 1.0, T)
+    S0 = rng.standard_normal((Dk, Dv))
+    S = S0.copy()
+    ref = []
+    for t in range(T):
+        S = alpha[t] * (np.eye(Dk) - beta[t] * np.outer(k[t], k[t])) @ S + beta[t] * np.outer(
+            k[t], v[t])
+        ref.append(S.T @ q[t])
+    o, ht = kda_oracle.gdn_forward(q[None, :, None], k[None, :, None], v[None, :, None],
+                                   np.log(alpha)[None, :, None], beta[None, :, None],
+                                   h0=S0[None, None])
+    np.testing.assert_allclose(o[0, :, 0], np.array(ref), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ht[0, 0], S, rtol=1e-12, atol=1e-12)
+    # alpha = 1 leaves plain DeltaNet; a per-channel reading of alpha would differ here
+    o1, _ = kda_oracle.gdn_forward(q[None, :, None], k[None, :, None], v[None, :, None],
+                                   np.zeros((1, T, 1)), beta[None, :, None])
+    S = np.zeros((Dk, Dv))
+    for t in range(T):
+        S = S + beta[t] * np.outer(k[t], v[t] - k[t] @ S)
+    np.testing.assert_allclose(o1[0, -1, 0], S.T @ q[-1], rtol=1e-12, atol=1e-12)
+
+
+def test_gdn_beta_zero_is_pure_decay():
+    """beta = 0 writes nothing: S_t = (prod alpha) S_0 and o_t = exp(G_t) S_0^T q_t with G_t
+    the running sum of g (the retention gate alone, zhilingong.com section 6)."""
+    rng = np.random.default_rng(62)
+    T, H, Dk, Dv = 30, 2, 4, 3
+    q = rng.standard_normal((1, T, H, Dk))
+    k = rng.standard_normal((1, T, H, Dk))
+    v = rng.standard_normal((1, T, H, Dv))
+    g = -rng.uniform(0, 0.3, (1, T, H))
+    S0 = rng.standard_normal((1, H, Dk, Dv))
+    o, ht = kda_oracle.gdn_forward(q, k, v, g, np.zeros((1, T, H)), scale=0.5, h0=S0)
+    G = np.cumsum(g[0], axis=0)                                          # [T, H]
+    o_cf = 0.5 * np.exp(G)[:, :, None] * np.einsum("thi,hij->thj", q[0], S0[0])
+    np.testing.assert_allclose(o[0], o_cf, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(ht[0], np.exp(G[-1])[:, None, None] * S0[0], rtol=1e-12)
+
+
+def test_gdn_equals_per_channel_recurrence_with_equal_gate():
+    """Gated DeltaNet is KDA with the gate repeated over the key channels (the scalar gate is
+    the special case KDA refines, zhilingong.com section 7); two independently written
+    oracles, over several sequences and heads."""
+    x = I.gdn_prefill_inputs(I.WORKLOADS[4], heads=[1, 6], lengths=[70, 0, 33, 64])
+    q, k, v, _, beta, h0, cu = _prefill_np(x)
+    gs = x.g.double().numpy()
+    o, ht = kda_oracle.gdn_forward(q, k, v, gs, beta, cu_seqlens=cu)
+    gk = np.repeat(gs[..., None], q.shape[-1], axis=-1)
+    o2, ht2 = kda_oracle.kda_forward(q, k, v, gk, beta, cu_seqlens=cu)
+    assert _rel(o, o2) <= 1e-12
+    assert _rel(ht, ht2) <= 1e-12
+
+
+def test_native_gdn_matches_numpy():
+    for x in (I.gdn_prefill_inputs(I.WORKLOADS[1], heads=[0, 3], T=130),
+              I.gdn_prefill_inputs(I.WORKLOADS[4], heads=[2], lengths=[65, 0, 1, 40])):
+        q, k, v, g, beta, h0, cu = _prefill_np(x)
+        o_ref, ht_ref = kda_oracle.gdn_forward(q, k, v, g, beta, h0=h0, cu_seqlens=cu)
+        o_c, ht_c = native.gdn_prefill(x.q, x.k, x.v, x.g, x.beta, h0=x.h0, cu_seqlens=cu)
+        assert _rel(o_c, o_ref) <= 1e-12
+        assert _rel(ht_c, ht_ref) <= 1e-12
+    y = I.gdn_decode_inputs(I.WORKLOADS[3], heads=[0, 9], N=4)
+    args = [t.double().numpy() for t in (y.q, y.k, y.v, y.g, y.beta, y.state)]
+    o_ref, S_ref = kda_oracle.gdn_decode(*args, scale=0.7)
+    o_c, S_c = native.gdn_decode(y.q, y.k, y.v, y.g, y.beta, y.state, scale=0.7)
+    assert _rel(o_c, o_ref) <= 1e-12
+    assert _rel(S_c, S_ref) <= 1e-12
+
+
+def test_gdn_decode_steps_equal_forward():
+    x = I.gdn_prefill_inputs(I.WORKLOADS[1], heads=[1], T=20)
+    q, k, v, g, beta, h0, _ = _prefill_np(x)
+    o, ht = kda_oracle.gdn_forward(q, k, v, g, beta, h0=h0)
+    S = h0
+    for t in range(q.shape[1]):
+        od, S = kda_oracle.gdn_decode(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], S)
+        np.testing.assert_allclose(od, o[:, t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S, ht, rtol=1e-12, atol=1e-12)
