@@ -9,6 +9,9 @@ raise.
     o, ht = fwd_chunked(q, k, v, g, beta, scale=1.0, initial_state=None,
                         output_final_state=True, cu_seqlens=None)
     o = decode_step(q, k, v, g, beta, state, scale=1.0)     # state updated in place
+
+Gated DeltaNet (one scalar gate per token and head, g [B,T,H] / [N,H]) has
+the same calls under the names gdn_fwd_chunked and gdn_decode_step.
 """
 from __future__ import annotations
 
@@ -28,7 +31,7 @@ KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 
 EXPORTED = ("kda_status_string", "kda_fwd_chunked_workspace_size", "kda_fwd_chunked",
-            "kda_decode_step")
+            "kda_decode_step", "kda_gdn_fwd_chunked", "kda_gdn_decode_step")
 
 
 class KDAError(RuntimeError):
@@ -54,11 +57,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_fwd_chunked_workspace_size.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
     lib.kda_fwd_chunked_workspace_size.restype = i
-    lib.kda_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
-                                    vp, sz, vp]
-    lib.kda_fwd_chunked.restype = i
-    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, i, i, i, i, i, i, vp]
-    lib.kda_decode_step.restype = i
+    for name in ("kda_fwd_chunked", "kda_gdn_fwd_chunked"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
+        fn.restype = i
+    for name in ("kda_decode_step", "kda_gdn_decode_step"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, i, i, i, i, i, i, vp]
+        fn.restype = i
     if path is None:
         _lib_handle = lib
     return lib
@@ -123,6 +129,20 @@ def fwd_chunked(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
     initial_state: [N,H,Dk,Dv] float32 or None; cu_seqlens: int32 [N+1] (B == 1) or None.
     out_dtype: torch.float32 (default) or torch.bfloat16.
     Returns (o [B,T,H,Dv], ht [N,H,Dk,Dv] float32 or None)."""
+    return _fwd_chunked(False, q, k, v, g, beta, scale, initial_state, output_final_state,
+                        cu_seqlens, workspace, out, final_state, out_dtype)
+
+
+def gdn_fwd_chunked(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
+                    output_final_state: bool = True, cu_seqlens=None, workspace=None,
+                    out=None, final_state=None, out_dtype=None):
+    """Gated DeltaNet chunked prefill: as fwd_chunked with g [B,T,H] float32."""
+    return _fwd_chunked(True, q, k, v, g, beta, scale, initial_state, output_final_state,
+                        cu_seqlens, workspace, out, final_state, out_dtype)
+
+
+def _fwd_chunked(scalar_gate, q, k, v, g, beta, scale, initial_state, output_final_state,
+                 cu_seqlens, workspace, out, final_state, out_dtype):
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if q.dim() != 4 or v.dim() != 4:
@@ -134,7 +154,7 @@ def fwd_chunked(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
     varlen = cu_seqlens is not None
     N = (cu_seqlens.numel() - 1) if varlen else B
     _check_shape("k", k, (B, T, H, Dk))
-    _check_shape("g", g, (B, T, H, Dk))
+    _check_shape("g", g, (B, T, H) if scalar_gate else (B, T, H, Dk))
     _check_shape("v", v, (B, T, H, Dv))
     _check_shape("beta", beta, (B, T, H))
     _check_shape("initial_state", initial_state, (N, H, Dk, Dv))
@@ -160,18 +180,28 @@ def fwd_chunked(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
     if output_final_state:
         ht = final_state if final_state is not None else torch.empty(
             (N, H, Dk, Dv), dtype=torch.float32, device=q.device)
-    st = load_library().kda_fwd_chunked(
+    name = "kda_gdn_fwd_chunked" if scalar_gate else "kda_fwd_chunked"
+    st = getattr(load_library(), name)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(initial_state),
         _ptr(ht), _ptr(o), _ptr(cu_seqlens), int(N), int(B), int(T), int(H), int(Dk), int(Dv),
         code, ocode, _ptr(workspace), nbytes, _stream(q.device))
     if st != KDA_SUCCESS:
-        raise KDAError(st, "kda_fwd_chunked")
+        raise KDAError(st, name)
     return o, ht
 
 
 def decode_step(q, k, v, g, beta, state, scale: float = 1.0, out=None, out_dtype=None):
     """One decode step. q, k, g: [N,H,Dk]; v: [N,H,Dv]; beta: [N,H];
     state: [N,H,Dk,Dv] float32, updated in place. Returns o [N,H,Dv] (float32 by default)."""
+    return _decode_step(False, q, k, v, g, beta, state, scale, out, out_dtype)
+
+
+def gdn_decode_step(q, k, v, g, beta, state, scale: float = 1.0, out=None, out_dtype=None):
+    """One Gated DeltaNet decode step: as decode_step with g [N,H] float32."""
+    return _decode_step(True, q, k, v, g, beta, state, scale, out, out_dtype)
+
+
+def _decode_step(scalar_gate, q, k, v, g, beta, state, scale, out, out_dtype):
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if q.dim() != 3 or v.dim() != 3:
@@ -181,7 +211,7 @@ def decode_step(q, k, v, g, beta, state, scale: float = 1.0, out=None, out_dtype
     code = _dtype_code(q)
     _check_same_dtype(q, k=k, v=v, beta=beta)
     _check_shape("k", k, (N, H, Dk))
-    _check_shape("g", g, (N, H, Dk))
+    _check_shape("g", g, (N, H) if scalar_gate else (N, H, Dk))
     _check_shape("v", v, (N, H, Dv))
     _check_shape("beta", beta, (N, H))
     _check_shape("state", state, (N, H, Dk, Dv))
@@ -190,9 +220,10 @@ def decode_step(q, k, v, g, beta, state, scale: float = 1.0, out=None, out_dtype
         raise TypeError("g and state must be float32")
     _check_gpu(q, k, v, g, beta, state, out)
     o = out if out is not None else torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
-    st = load_library().kda_decode_step(
+    name = "kda_gdn_decode_step" if scalar_gate else "kda_decode_step"
+    st = getattr(load_library(), name)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(state), _ptr(o),
         int(N), int(H), int(Dk), int(Dv), code, _dtype_code(o), _stream(q.device))
     if st != KDA_SUCCESS:
-        raise KDAError(st, "kda_decode_step")
+        raise KDAError(st, name)
     return o

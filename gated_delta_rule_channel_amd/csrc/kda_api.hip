@@ -7,12 +7,12 @@
 #include "../../include/kda.h"
 
 namespace kda {
-hipError_t launch_decode(bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
+hipError_t launch_decode(bool sg, bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
                          const void* k, const void* v, const float* g, const void* beta,
                          float scale, float* state, void* o, int N, int H, hipStream_t s);
 hipError_t launch_chunk_map(const int32_t* cu, int N, int T, int max_slots, void* tab,
                             int32_t* seq_off, hipStream_t s);
-hipError_t launch_prefill(bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
+hipError_t launch_prefill(bool sg, bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
                           const void* k, const void* v, const float* g, const void* beta,
                           float scale, const float* h0, float* ht, void* o, const int32_t* cu,
                           int T, const void* tab, const int32_t* seq_off, uint8_t* blocks, int N,
@@ -52,6 +52,58 @@ kda_status plan_prefill(int B, int T, int H, int Dk, int Dv, int num_seqs, bool 
     return KDA_SUCCESS;
 }
 
+// sg: scalar gate (Gated DeltaNet), g holds one value per token and head
+kda_status fwd_chunked(bool sg, const void* q, const void* k, const void* v, const float* g,
+                       const void* beta, float scale, const float* h0, float* ht, void* o,
+                       const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int Dk,
+                       int Dv, kda_dtype dtype, kda_dtype o_dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !g || !beta || !o) return KDA_ERROR_INVALID_VALUE;
+    if (!dtype_ok(o_dtype)) return KDA_ERROR_INVALID_VALUE;
+    PrefillPlan p;
+    const kda_status st = plan_prefill(B, T, H, Dk, Dv, num_seqs, cu_seqlens != nullptr, dtype, &p);
+    if (st != KDA_SUCCESS) return st;
+    const void* ptrs[] = {q, k, v, g, beta, o, h0, ht};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned(ptr, 16)) return KDA_ERROR_INVALID_VALUE;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERROR_INVALID_VALUE;
+    if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256))
+        return KDA_ERROR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    void* tab = nullptr;
+    int32_t* seq_off = nullptr;
+    if (cu_seqlens) {                          // packed sequences: chunk table on the device
+        tab = ws + p.tab_off;
+        seq_off = reinterpret_cast<int32_t*>(ws + p.seq_off);
+        if (kda::launch_chunk_map(cu_seqlens, p.nseq, T, (int)p.max_slots, tab, seq_off, s) !=
+            hipSuccess)
+            return KDA_ERROR_LAUNCH;
+    }
+    if (kda::launch_prefill(sg, dtype == KDA_DTYPE_BF16, o_dtype == KDA_DTYPE_BF16, Dk, Dv, q, k,
+                            v, g, beta, scale, h0, ht, o, cu_seqlens, T, tab, seq_off,
+                            ws + p.blocks_off, p.nseq, H, (int)p.max_slots, s) != hipSuccess)
+        return KDA_ERROR_LAUNCH;
+    return KDA_SUCCESS;
+}
+
+kda_status decode_step(bool sg, const void* q, const void* k, const void* v, const float* g,
+                       const void* beta, float scale, float* state, void* o, int N, int H,
+                       int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype, void* stream) {
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERROR_INVALID_VALUE;
+    if (N <= 0 || H <= 0 || !head_ok(Dk) || !head_ok(Dv)) return KDA_ERROR_INVALID_VALUE;
+    if (!dtype_ok(dtype) || !dtype_ok(o_dtype)) return KDA_ERROR_INVALID_VALUE;
+    if ((long long)N * H > (1LL << 31) - 1) return KDA_ERROR_NOT_SUPPORTED;
+    const void* ptrs[] = {q, k, v, g, beta, state, o};
+    for (const void* ptr : ptrs)
+        if (!aligned(ptr, 16)) return KDA_ERROR_INVALID_VALUE;
+    if (kda::launch_decode(sg, dtype == KDA_DTYPE_BF16, o_dtype == KDA_DTYPE_BF16, Dk, Dv, q, k, v,
+                           g, beta, scale, state, o, N, H,
+                           reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return KDA_ERROR_LAUNCH;
+    return KDA_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,50 +134,32 @@ kda_status kda_fwd_chunked(const void* q, const void* k, const void* v, const fl
                            const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int Dk,
                            int Dv, kda_dtype dtype, kda_dtype o_dtype, void* workspace,
                            size_t workspace_bytes, void* stream) {
-    if (!q || !k || !v || !g || !beta || !o) return KDA_ERROR_INVALID_VALUE;
-    if (!dtype_ok(o_dtype)) return KDA_ERROR_INVALID_VALUE;
-    PrefillPlan p;
-    const kda_status st = plan_prefill(B, T, H, Dk, Dv, num_seqs, cu_seqlens != nullptr, dtype, &p);
-    if (st != KDA_SUCCESS) return st;
-    const void* ptrs[] = {q, k, v, g, beta, o, h0, ht};
-    for (const void* ptr : ptrs)
-        if (ptr && !aligned(ptr, 16)) return KDA_ERROR_INVALID_VALUE;
-    if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERROR_INVALID_VALUE;
-    if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256))
-        return KDA_ERROR_WORKSPACE;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    void* tab = nullptr;
-    int32_t* seq_off = nullptr;
-    if (cu_seqlens) {                          // packed sequences: chunk table on the device
-        tab = ws + p.tab_off;
-        seq_off = reinterpret_cast<int32_t*>(ws + p.seq_off);
-        if (kda::launch_chunk_map(cu_seqlens, p.nseq, T, (int)p.max_slots, tab, seq_off, s) !=
-            hipSuccess)
-            return KDA_ERROR_LAUNCH;
-    }
-    if (kda::launch_prefill(dtype == KDA_DTYPE_BF16, o_dtype == KDA_DTYPE_BF16, Dk, Dv, q, k, v,
-                            g, beta, scale, h0, ht, o, cu_seqlens, T, tab, seq_off,
-                            ws + p.blocks_off, p.nseq, H, (int)p.max_slots, s) != hipSuccess)
-        return KDA_ERROR_LAUNCH;
-    return KDA_SUCCESS;
+    return fwd_chunked(false, q, k, v, g, beta, scale, h0, ht, o, cu_seqlens, num_seqs, B, T, H,
+                       Dk, Dv, dtype, o_dtype, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_gdn_fwd_chunked(const void* q, const void* k, const void* v, const float* g,
+                               const void* beta, float scale, const float* h0, float* ht,
+                               void* o, const int32_t* cu_seqlens, int num_seqs, int B, int T,
+                               int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    return fwd_chunked(true, q, k, v, g, beta, scale, h0, ht, o, cu_seqlens, num_seqs, B, T, H,
+                       Dk, Dv, dtype, o_dtype, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
                            const void* beta, float scale, float* state, void* o, int N, int H,
                            int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype, void* stream) {
-    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERROR_INVALID_VALUE;
-    if (N <= 0 || H <= 0 || !head_ok(Dk) || !head_ok(Dv)) return KDA_ERROR_INVALID_VALUE;
-    if (!dtype_ok(dtype) || !dtype_ok(o_dtype)) return KDA_ERROR_INVALID_VALUE;
-    if ((long long)N * H > (1LL << 31) - 1) return KDA_ERROR_NOT_SUPPORTED;
-    const void* ptrs[] = {q, k, v, g, beta, state, o};
-    for (const void* ptr : ptrs)
-        if (!aligned(ptr, 16)) return KDA_ERROR_INVALID_VALUE;
-    if (kda::launch_decode(dtype == KDA_DTYPE_BF16, o_dtype == KDA_DTYPE_BF16, Dk, Dv, q, k, v, g,
-                           beta, scale, state, o, N, H,
-                           reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
-        return KDA_ERROR_LAUNCH;
-    return KDA_SUCCESS;
+    return decode_step(false, q, k, v, g, beta, scale, state, o, N, H, Dk, Dv, dtype, o_dtype,
+                       stream);
+}
+
+kda_status kda_gdn_decode_step(const void* q, const void* k, const void* v, const float* g,
+                               const void* beta, float scale, float* state, void* o, int N,
+                               int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
+                               void* stream) {
+    return decode_step(true, q, k, v, g, beta, scale, state, o, N, H, Dk, Dv, dtype, o_dtype,
+                       stream);
 }
 
 }  // extern "C"

@@ -17,6 +17,10 @@
 // wavefront and through LDS across wavefronts. State stores are nontemporal
 // (each state is written once per step); plain loads measured faster than
 // nontemporal ones.
+//
+// SG selects the scalar gate of Gated DeltaNet ("Notes on Linear Attention",
+// section 6): g holds one log-decay per (request, head) and every row of S
+// decays by the same factor.
 #include "kda_common.h"
 
 namespace kda {
@@ -34,7 +38,7 @@ struct DecodeShape {
     static_assert(NT % CG == 0 && DK % RS == 0 && RPT >= 1, "decode tiling");
 };
 
-template <typename TI, typename TO, int DK, int DV>
+template <typename TI, typename TO, int DK, int DV, bool SG>
 __global__ __launch_bounds__(1024) void decode_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
     const float* __restrict__ g, const TI* __restrict__ beta, float scale,
@@ -55,7 +59,7 @@ __global__ __launch_bounds__(1024) void decode_kernel(
     float* S = state + (size_t)head * DK * DV;
     const TI* qh = q + (size_t)head * DK;
     const TI* kh = k + (size_t)head * DK;
-    const float* gh = g + (size_t)head * DK;
+    const float* gh = g + (size_t)head * (SG ? 1 : DK);
 
     float4 s[RPT];
     float kr[RPT];
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(1024) void decode_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rs + RS * i;
-        const float a = fast_exp2(gh[r] * kLog2e);
+        const float a = fast_exp2(gh[SG ? 0 : r] * kLog2e);
         const float kk = to_f(kh[r]);
         const float qq = scale * to_f(qh[r]);
         kr[i] = kk;
@@ -127,24 +131,30 @@ __global__ __launch_bounds__(1024) void decode_kernel(
 }
 
 template <typename TI, typename TO, int DK, int DV>
-static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
-                                  const void* beta, float scale, float* state, void* o, int N,
-                                  int H, hipStream_t stream) {
+static hipError_t launch_decode_t(bool sg, const void* q, const void* k, const void* v,
+                                  const float* g, const void* beta, float scale, float* state,
+                                  void* o, int N, int H, hipStream_t stream) {
     const dim3 grid((unsigned)((long long)N * H));
     const dim3 block(DecodeShape<DK, DV>::NT);
-    hipLaunchKernelGGL((decode_kernel<TI, TO, DK, DV>), grid, block, 0, stream,
-                       (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
-                       state, (TO*)o);
+    if (sg)
+        hipLaunchKernelGGL((decode_kernel<TI, TO, DK, DV, true>), grid, block, 0, stream,
+                           (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
+                           state, (TO*)o);
+    else
+        hipLaunchKernelGGL((decode_kernel<TI, TO, DK, DV, false>), grid, block, 0, stream,
+                           (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
+                           state, (TO*)o);
     return hipGetLastError();
 }
 
 template <typename TI, typename TO>
-static hipError_t dispatch_decode(int Dk, int Dv, const void* q, const void* k, const void* v,
-                                  const float* g, const void* beta, float scale, float* state,
-                                  void* o, int N, int H, hipStream_t s) {
+static hipError_t dispatch_decode(bool sg, int Dk, int Dv, const void* q, const void* k,
+                                  const void* v, const float* g, const void* beta, float scale,
+                                  float* state, void* o, int N, int H, hipStream_t s) {
 #define KDA_DEC(DKV, DVV)                                                                   \
     if (Dk == DKV && Dv == DVV)                                                             \
-        return launch_decode_t<TI, TO, DKV, DVV>(q, k, v, g, beta, scale, state, o, N, H, s);
+        return launch_decode_t<TI, TO, DKV, DVV>(sg, q, k, v, g, beta, scale, state, o, N, H,  \
+                                                 s);
     KDA_DEC(16, 16) KDA_DEC(16, 32) KDA_DEC(16, 64) KDA_DEC(16, 128)
     KDA_DEC(32, 16) KDA_DEC(32, 32) KDA_DEC(32, 64) KDA_DEC(32, 128)
     KDA_DEC(64, 16) KDA_DEC(64, 32) KDA_DEC(64, 64) KDA_DEC(64, 128)
@@ -153,17 +163,18 @@ static hipError_t dispatch_decode(int Dk, int Dv, const void* q, const void* k, 
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
-                         const void* k, const void* v, const float* g, const void* beta,
-                         float scale, float* state, void* o, int N, int H, hipStream_t s) {
+hipError_t launch_decode(bool sg, bool bf16_in, bool bf16_out, int Dk, int Dv,
+                         const void* q, const void* k, const void* v, const float* g,
+                         const void* beta, float scale, float* state, void* o, int N, int H,
+                         hipStream_t s) {
     if (bf16_in) {
         if (bf16_out)
-            return dispatch_decode<bf16, bf16>(Dk, Dv, q, k, v, g, beta, scale, state, o, N, H, s);
-        return dispatch_decode<bf16, float>(Dk, Dv, q, k, v, g, beta, scale, state, o, N, H, s);
+            return dispatch_decode<bf16, bf16>(sg, Dk, Dv, q, k, v, g, beta, scale, state, o, N, H, s);
+        return dispatch_decode<bf16, float>(sg, Dk, Dv, q, k, v, g, beta, scale, state, o, N, H, s);
     }
     if (bf16_out)
-        return dispatch_decode<float, bf16>(Dk, Dv, q, k, v, g, beta, scale, state, o, N, H, s);
-    return dispatch_decode<float, float>(Dk, Dv, q, k, v, g, beta, scale, state, o, N, H, s);
+        return dispatch_decode<float, bf16>(sg, Dk, Dv, q, k, v, g, beta, scale, state, o, N, H, s);
+    return dispatch_decode<float, float>(sg, Dk, Dv, q, k, v, g, beta, scale, state, o, N, H, s);
 }
 
 }  // namespace kda

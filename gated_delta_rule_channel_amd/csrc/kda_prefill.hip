@@ -295,7 +295,7 @@ __device__ __forceinline__ typename Pol::Frag4 frag4_of(const floatx4& d) {
     return f;
 }
 
-template <typename TI, int DK, int DV>
+template <typename TI, int DK, int DV, bool SG>
 __global__ __launch_bounds__(256, 2) void prep_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
     const float* __restrict__ g, const TI* __restrict__ beta, float scale,
@@ -353,14 +353,20 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                 lds_load16(k + off, sRb + Stg::k_off(wave, I));
                 lds_load16(q + off, sRb + Stg::q_off(wave, I));
             }
-            // g (float32): eight lanes per row, so each load covers whole 128-byte rows of the
-            // slice (rows 8 hg .. 8 hg + 7 of the block)
+            if constexpr (SG) {
+                // scalar gate: the block's 16 values, one per lane, to the start of the part
+                if (cs && lane < 16 && 16 * I + lane < L)
+                    lds_load4(g + (size_t)(t0 + 16 * I + lane) * H + h, sRb + Stg::g_off(wave, I, 0));
+            } else {
+                // g (float32): eight lanes per row, so each load covers whole 128-byte rows of
+                // the slice (rows 8 hg .. 8 hg + 7 of the block)
 #pragma unroll
-            for (int hg = 0; hg < 2; ++hg) {
-                const int grow = 16 * I + 8 * hg + (lane >> 3), gc = 32 * wave + 4 * (lane & 7);
-                if (cs && gc < DK && grow < L)
-                    lds_load16(g + (size_t)(t0 + grow) * rowq + (size_t)h * DK + gc,
-                               sRb + Stg::g_off(wave, I, hg));
+                for (int hg = 0; hg < 2; ++hg) {
+                    const int grow = 16 * I + 8 * hg + (lane >> 3), gc = 32 * wave + 4 * (lane & 7);
+                    if (cs && gc < DK && grow < L)
+                        lds_load16(g + (size_t)(t0 + grow) * rowq + (size_t)h * DK + gc,
+                                   sRb + Stg::g_off(wave, I, hg));
+                }
             }
             if (I == 0 && wave == 0 && lane < L) {
                 const size_t e = (size_t)(t0 + lane) * H + h;       // beta element index
@@ -401,13 +407,20 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             for (int I = 0; I < 4; ++I) {
                 const int row = 16 * I + m;
                 if (cvalid && row < L) {
-                    // row m of the block sits in part m / 8, its 8 channels at 16-byte slots
-                    // 8 (m % 8) + 2 grp and the next
-                    const floatx4* gp = reinterpret_cast<const floatx4*>(sRb + Stg::g_off(wave, I, m >> 3)) +
-                                        8 * (m & 7) + 2 * grp;
-                    const floatx4 g0 = gp[0], g1 = gp[1];
-                    G[8 * I] = g0[0]; G[8 * I + 1] = g0[1]; G[8 * I + 2] = g0[2]; G[8 * I + 3] = g0[3];
-                    G[8 * I + 4] = g1[0]; G[8 * I + 5] = g1[1]; G[8 * I + 6] = g1[2]; G[8 * I + 7] = g1[3];
+                    if constexpr (SG) {
+                        const float gs = reinterpret_cast<const float*>(sRb + Stg::g_off(wave, I, 0))[m];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) G[8 * I + e] = gs;
+                    } else {
+                        // row m of the block sits in part m / 8, its 8 channels at 16-byte
+                        // slots 8 (m % 8) + 2 grp and the next
+                        const floatx4* gp =
+                            reinterpret_cast<const floatx4*>(sRb + Stg::g_off(wave, I, m >> 3)) +
+                            8 * (m & 7) + 2 * grp;
+                        const floatx4 g0 = gp[0], g1 = gp[1];
+                        G[8 * I] = g0[0]; G[8 * I + 1] = g0[1]; G[8 * I + 2] = g0[2]; G[8 * I + 3] = g0[3];
+                        G[8 * I + 4] = g1[0]; G[8 * I + 5] = g1[1]; G[8 * I + 6] = g1[2]; G[8 * I + 7] = g1[3];
+                    }
                     K.set(I, reinterpret_cast<const u32x4*>(sRb + Stg::k_off(wave, I))[lane]);
                     Q.set(I, reinterpret_cast<const u32x4*>(sRb + Stg::q_off(wave, I))[lane]);
                 } else {
@@ -428,10 +441,16 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                 const int row = 16 * I + m;
                 if (cvalid && row < L) {
                     const size_t off = (size_t)(t0 + row) * rowq + (size_t)h * DK + c0;
-                    const floatx4 g0 = reinterpret_cast<const floatx4*>(g + off)[0];
-                    const floatx4 g1 = reinterpret_cast<const floatx4*>(g + off)[1];
-                    G[8 * I] = g0[0]; G[8 * I + 1] = g0[1]; G[8 * I + 2] = g0[2]; G[8 * I + 3] = g0[3];
-                    G[8 * I + 4] = g1[0]; G[8 * I + 5] = g1[1]; G[8 * I + 6] = g1[2]; G[8 * I + 7] = g1[3];
+                    if constexpr (SG) {
+                        const float gs = g[(size_t)(t0 + row) * H + h];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) G[8 * I + e] = gs;
+                    } else {
+                        const floatx4 g0 = reinterpret_cast<const floatx4*>(g + off)[0];
+                        const floatx4 g1 = reinterpret_cast<const floatx4*>(g + off)[1];
+                        G[8 * I] = g0[0]; G[8 * I + 1] = g0[1]; G[8 * I + 2] = g0[2]; G[8 * I + 3] = g0[3];
+                        G[8 * I + 4] = g1[0]; G[8 * I + 5] = g1[1]; G[8 * I + 6] = g1[2]; G[8 * I + 7] = g1[3];
+                    }
                     K.load(I, k + off);
                     Q.load(I, q + off);
                 } else {
@@ -1239,7 +1258,7 @@ static hipError_t current_cu_count(int& n) {
 }
 
 template <typename TI, typename TO, int DK, int DV>
-static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const float* g,
+static hipError_t launch_prefill_t(bool sg, const void* q, const void* k, const void* v, const float* g,
                                    const void* beta, float scale, const float* h0, float* ht,
                                    void* o, const int32_t* cu, int T, const void* tab,
                                    const int32_t* seq_off, uint8_t* blocks, int N, int H,
@@ -1249,9 +1268,14 @@ static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, 
     if (ec != hipSuccess) return ec;
     const long long ntasks = (long long)max_slots * H;
     const long long grid = ntasks < 2LL * cu_count ? ntasks : 2LL * cu_count;
-    hipLaunchKernelGGL((prep_kernel<TI, DK, DV>), dim3((unsigned)grid), dim3(256), 0, s,
-                       (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
-                       (const int4*)tab, T, max_slots, blocks, H);
+    if (sg)
+        hipLaunchKernelGGL((prep_kernel<TI, DK, DV, true>), dim3((unsigned)grid), dim3(256), 0, s,
+                           (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
+                           (const int4*)tab, T, max_slots, blocks, H);
+    else
+        hipLaunchKernelGGL((prep_kernel<TI, DK, DV, false>), dim3((unsigned)grid), dim3(256), 0, s,
+                           (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
+                           (const int4*)tab, T, max_slots, blocks, H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int BV = DV >= 32 ? 32 : DV;
@@ -1264,14 +1288,14 @@ static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, 
 }
 
 template <typename TI, typename TO>
-static hipError_t dispatch_prefill(int Dk, int Dv, const void* q, const void* k, const void* v,
+static hipError_t dispatch_prefill(bool sg, int Dk, int Dv, const void* q, const void* k, const void* v,
                                    const float* g, const void* beta, float scale,
                                    const float* h0, float* ht, void* o, const int32_t* cu, int T,
                                    const void* tab, const int32_t* seq_off, uint8_t* blocks,
                                    int N, int H, int max_slots, hipStream_t s) {
 #define KDA_PF(DKV, DVV)                                                                    \
     if (Dk == DKV && Dv == DVV)                                                             \
-        return launch_prefill_t<TI, TO, DKV, DVV>(q, k, v, g, beta, scale, h0, ht, o, cu, T,\
+        return launch_prefill_t<TI, TO, DKV, DVV>(sg, q, k, v, g, beta, scale, h0, ht, o, cu, T,\
                                                   tab, seq_off, blocks, N, H, max_slots, s);
     KDA_PF(16, 16) KDA_PF(16, 32) KDA_PF(16, 64) KDA_PF(16, 128)
     KDA_PF(32, 16) KDA_PF(32, 32) KDA_PF(32, 64) KDA_PF(32, 128)
@@ -1281,22 +1305,22 @@ static hipError_t dispatch_prefill(int Dk, int Dv, const void* q, const void* k,
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill(bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
+hipError_t launch_prefill(bool sg, bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
                           const void* k, const void* v, const float* g, const void* beta,
                           float scale, const float* h0, float* ht, void* o, const int32_t* cu,
                           int T, const void* tab, const int32_t* seq_off, uint8_t* blocks, int N,
                           int H, int max_slots, hipStream_t s) {
     if (bf16_in) {
         if (bf16_out)
-            return dispatch_prefill<bf16, bf16>(Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T,
+            return dispatch_prefill<bf16, bf16>(sg, Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T,
                                                 tab, seq_off, blocks, N, H, max_slots, s);
-        return dispatch_prefill<bf16, float>(Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T,
+        return dispatch_prefill<bf16, float>(sg, Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T,
                                              tab, seq_off, blocks, N, H, max_slots, s);
     }
     if (bf16_out)
-        return dispatch_prefill<float, bf16>(Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T,
+        return dispatch_prefill<float, bf16>(sg, Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T,
                                              tab, seq_off, blocks, N, H, max_slots, s);
-    return dispatch_prefill<float, float>(Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T, tab,
+    return dispatch_prefill<float, float>(sg, Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T, tab,
                                           seq_off, blocks, N, H, max_slots, s);
 }
 

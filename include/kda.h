@@ -128,6 +128,35 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
                            const void* beta, float scale, float* state, void* o, int N, int H,
                            int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype, void* stream);
 
+/* Gated DeltaNet: the same recurrence with one scalar retention gate per
+ * token and head instead of one per key channel. Step (1) becomes
+ * S~ = exp(g_t) S, every row decaying alike; steps (2)-(5) are unchanged.
+ * This is the gated delta rule of "Notes on Linear Attention"
+ * (zhilingong.com), section 6 (decay first, then the delta rule on the
+ * decayed state), and of "From Fast Weight Programmers to KDA"
+ * (jonahsamost.bearblog.dev), section "Gated Delta Networks" (written there
+ * for the transposed state). It equals kda_fwd_chunked with g repeated over
+ * the Dk channels; the kernels read the one value per token instead.
+ *
+ *  g      [B, T, H]      float32       log-decay, one per token and head
+ *
+ * Every other argument, the workspace (sized by
+ * kda_fwd_chunked_workspace_size), the aliasing rules and the errors are
+ * those of kda_fwd_chunked. */
+kda_status kda_gdn_fwd_chunked(const void* q, const void* k, const void* v, const float* g,
+                               const void* beta, float scale, const float* h0, float* ht,
+                               void* o, const int32_t* cu_seqlens, int num_seqs, int B, int T,
+                               int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* One Gated DeltaNet decode step: as kda_decode_step with g [N, H] float32,
+ * one log-decay per request and head applied to every row of its state.
+ * Arguments and errors are those of kda_decode_step. */
+kda_status kda_gdn_decode_step(const void* q, const void* k, const void* v, const float* g,
+                               const void* beta, float scale, float* state, void* o, int N,
+                               int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -145,3 +145,44 @@ def test_binding_rejects_mismatched_arguments():
         kda.decode_step(qd, qd, qd, torch.zeros(N, H, D + 16), torch.zeros(N, H), st)
     with pytest.raises(ValueError, match="contiguous GPU"):
         kda.decode_step(qd, qd, qd, qd, torch.zeros(N, H), st)
+
+
+def test_binding_gdn_takes_one_gate_per_token():
+    """The Gated DeltaNet calls take g [B,T,H] (prefill) and [N,H] (decode) and refuse the
+    per-channel shape; the KDA calls refuse the scalar one."""
+    import torch
+    kda = pytest.importorskip("gated_delta_rule_channel_amd")
+    B, T, H, D = 1, 64, 2, 16
+    q = torch.zeros(B, T, H, D)
+    beta = torch.zeros(B, T, H)
+    with pytest.raises(ValueError, match="g has shape"):
+        kda.gdn_fwd_chunked(q, q, q, torch.zeros(B, T, H, D), beta)
+    with pytest.raises(ValueError, match="g has shape"):
+        kda.fwd_chunked(q, q, q, torch.zeros(B, T, H), beta)
+    with pytest.raises(ValueError, match="contiguous GPU"):
+        kda.gdn_fwd_chunked(q, q, q, torch.zeros(B, T, H), beta)    # well formed, on the CPU
+    N = 3
+    qd = torch.zeros(N, H, D)
+    st = torch.zeros(N, H, D, D)
+    with pytest.raises(ValueError, match="g has shape"):
+        kda.gdn_decode_step(qd, qd, qd, qd, torch.zeros(N, H), st)
+    with pytest.raises(ValueError, match="contiguous GPU"):
+        kda.gdn_decode_step(qd, qd, qd, torch.zeros(N, H), torch.zeros(N, H), st)
+
+
+def test_gdn_entry_points_validate_like_kda(lib):
+    """The scalar-gate entry points run the same host checks before any launch."""
+    E = kda.KDA_ERROR_INVALID_VALUE
+    g = lambda **o: lib.kda_gdn_fwd_chunked(
+        o.get("q", FAKE), FAKE, FAKE, o.get("g", FAKE), FAKE, 1.0, None, None, FAKE, None, 1, 1,
+        64, 1, o.get("Dk", 64), 64, 0, 0, o.get("ws", None), o.get("wsb", 0), None)
+    assert g(q=None) == E
+    assert g(g=None) == E
+    assert g(Dk=48) == E
+    assert g(g=FAKE + 4) == E
+    assert g() == kda.KDA_ERROR_WORKSPACE
+    d = lambda **o: lib.kda_gdn_decode_step(FAKE, FAKE, FAKE, o.get("g", FAKE), FAKE, 1.0, FAKE,
+                                            FAKE, o.get("N", 4), 2, 64, 64, 1, 0, None)
+    assert d(g=None) == E
+    assert d(N=0) == E
+    assert d(g=FAKE + 8) == E
