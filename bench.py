@@ -5,7 +5,9 @@ One step = one chunked prefill over the main prefill workload (B1 T8192 H64
 d128, bf16 q/k/v/beta, fp32 g and state, fp32 output) plus one decode step
 over the decode workload (256 requests x 64 heads, 128x128 fp32 states
 updated in place). Inputs are synthetic (seeded generators) and resident in
-HBM before timing starts. Prints one JSON line.
+HBM before timing starts. Prints one JSON line. Besides the step figures it
+reports the decode step repeated back to back (the sustained rate) and the
+same step for Gated DeltaNet (one scalar gate per token and head).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
   python bench.py --copy-calibration          # 1 GiB device copy (counter calibration)
@@ -114,6 +116,11 @@ def _pmc_per_kernel(path, counter):
 
 
 def _short(name):
+    """Kernel of the KDA path a counter row belongs to; the scalar-gate (Gated DeltaNet)
+    instantiations, whose last template argument is true ("Lb1EE" in a mangled name), are
+    not counted."""
+    if re.search(r"\btrue\s*>|Lb1EE", name):
+        return None
     for key in ("prep_kernel", "state_kernel", "chunk_map_kernel", "decode_kernel"):
         if key in name:
             return key
@@ -308,6 +315,45 @@ def main():
     mfma_busy = 3.0 * pf_flops / (BF16_PEAK_TFLOPS * 1e12) / tp_mean
     traffic_pf, traffic_dc = load_traffic()
 
+    # the same decode step repeated with nothing between the calls: the Infinity Cache holds
+    # the tail of each step's state writes, which then reach HBM inside the next step rather
+    # than under the following prefill, so this is the sustained decode rate
+    eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eb0.record(stream)
+    for _ in range(args.steps):
+        decode()
+    eb1.record(stream)
+    torch.cuda.synchronize()
+    td_b2b = eb0.elapsed_time(eb1) * 1e-3 / args.steps
+    dc_gbs_b2b = dc_bytes / td_b2b / 1e9
+
+    # Gated DeltaNet (scalar gate per token and head) on the same q, k, v, beta and state
+    # shapes, timed the same way (one prefill + one decode step per step)
+    gs = I.scalar_gate(wp, list(range(H)), B * T).view(B, T, H).to(dev)
+    gds = I.scalar_gate(wd, list(range(wd.H)), wd.N).to(dev)
+
+    def gdn_prefill():
+        kda.gdn_fwd_chunked(q, k, v, gs, b, scale=1.0, workspace=ws, out=o, final_state=ht)
+
+    def gdn_decode():
+        kda.gdn_decode_step(dq, dk, dv, gds, db, state, scale=1.0, out=od)
+
+    for _ in range(args.warmup):
+        gdn_prefill()
+        gdn_decode()
+    torch.cuda.synchronize()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        gdn_prefill()
+        e1.record(stream)
+        gdn_decode()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    tgp = np.array([a.elapsed_time(bb) for a, bb, _ in ev]) * 1e-3
+    tgd = np.array([bb.elapsed_time(c) for _, bb, c in ev]) * 1e-3
+    gdn_pf_bytes = pf_bytes - B * T * H * Dk * 4 + B * T * H * 4       # g is one float per token-head
+    gdn_dc_bytes = dc_bytes - wd.N * wd.H * wd.Dk * 4 + wd.N * wd.H * 4
+
     # context for the decode figure: torch's device-to-device copy of 1 GiB (read + write)
     xc = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     yc = torch.empty_like(xc)
@@ -351,7 +397,16 @@ def main():
                    "state_updates_per_s": wd.N * wd.H / td_mean, "tokens_per_s": wd.N / td_mean,
                    "compulsory_bytes": dc_bytes, "hbm_gbs": dc_gbs,
                    "frac_of_peak": dc_gbs / HBM_PEAK_GBS,
-                   "device_copy_gbs": copy_gbs, "frac_of_device_copy": dc_gbs / copy_gbs},
+                   "device_copy_gbs": copy_gbs, "frac_of_device_copy": dc_gbs / copy_gbs,
+                   "ms_back_to_back": td_b2b * 1e3, "hbm_gbs_back_to_back": dc_gbs_b2b,
+                   "frac_of_peak_back_to_back": dc_gbs_b2b / HBM_PEAK_GBS},
+        "gated_deltanet": {"prefill_ms": float(tgp.mean()) * 1e3,
+                           "prefill_tokens_per_s": tokens / float(tgp.mean()),
+                           "prefill_hbm_gbs": gdn_pf_bytes / float(tgp.mean()) / 1e9,
+                           "decode_ms": float(tgd.mean()) * 1e3,
+                           "decode_hbm_gbs": gdn_dc_bytes / float(tgd.mean()) / 1e9,
+                           "decode_frac_of_peak": gdn_dc_bytes / float(tgd.mean()) / 1e9
+                           / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": pf_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": pf_gbs / HBM_PEAK_GBS, "traffic": traffic_pf,
                      "kernel": "kda_fwd_chunked call (prep_kernel + state_kernel; packed "

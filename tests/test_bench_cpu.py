@@ -72,6 +72,11 @@ def test_traffic_summary_calibration(tmp_path):
               "Counter_Value": 3000.0} for d in (1, 2)]
     write += [{"Dispatch_Id": 3, "Kernel_Name": "kda::state_kernel<...>",
                "Counter_Name": "WRITE_SIZE", "Counter_Value": 100.0}]
+    # a scalar-gate (Gated DeltaNet) prep dispatch is not part of the KDA figures
+    fetch += [{"Dispatch_Id": 4, "Kernel_Name": "void kda::prep_kernel<__hip_bfloat16, 128, 128, true>(...)",
+               "Counter_Name": "FETCH_SIZE", "Counter_Value": 9.0e6},
+              {"Dispatch_Id": 5, "Kernel_Name": "_ZN3kda11prep_kernelIDF16bLi128ELi128ELb1EEEvPKT_",
+               "Counter_Name": "FETCH_SIZE", "Counter_Value": 7.0e6}]
     _write_csv(tmp_path / "f.csv", fetch)
     _write_csv(tmp_path / "w.csv", write)
     out_file = str(tmp_path / "traffic.json")
