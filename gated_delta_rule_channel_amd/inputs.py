@@ -24,7 +24,11 @@ round-to-nearest-even; consumers that need float64 upcast the cast values):
 * Gated DeltaNet inputs (scalar gate) reuse q, k, v, beta and states of the
   same workload and replace g by one log-decay per (token, head),
   -softplus(N(0, 1)) times U(0.5, 2) where the workload scales g, from a
-  stream of its own.
+  stream of its own;
+* Gated DeltaNet-2 inputs reuse q, k, v, g and states of the workload and draw an
+  erase gate b = sigmoid(N(0, 1)) per (token, head, key channel) and a write gate
+  w = sigmoid(N(0, 1)) per (token, head, value channel), each from its own stream,
+  cast to the workload dtype like beta.
 
 Shapes follow the library: q, k, g are [B, T, H, Dk], v is [B, T, H, Dv],
 beta is [B, T, H]; varlen packs sequences along T with B = 1 and int32
@@ -41,7 +45,7 @@ import numpy as np
 import torch
 
 # tensor ids of the per-head streams
-_Q, _K, _V, _BETA, _G, _GFAC, _CHAN, _STATE, _LEN, _GSC = range(1, 11)
+_Q, _K, _V, _BETA, _G, _GFAC, _CHAN, _STATE, _LEN, _GSC, _EB, _EW = range(1, 13)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -281,3 +285,33 @@ def gdn_decode_inputs(w: Workload, heads: Optional[Sequence[int]] = None,
     x = decode_inputs(w, heads=heads, N=N)
     x.g = scalar_gate(w, x.heads, x.beta.shape[0])
     return x
+
+
+def erase_write_gates(w: Workload, heads: Sequence[int], ntok: int):
+    """Gated DeltaNet-2 gates: b [ntok, len(heads), Dk] and w [ntok, len(heads), Dv] in the
+    workload dtype, sigmoid(N(0, 1)) per element."""
+    dt = w.torch_dtype
+    b = torch.empty((ntok, len(heads), w.Dk), dtype=dt)
+    wr = torch.empty((ntok, len(heads), w.Dv), dtype=dt)
+    for j, h in enumerate(heads):
+        b[:, j] = _cast(_sigmoid(_rng(w.wid, _EB, h).standard_normal((ntok, w.Dk))), dt)
+        wr[:, j] = _cast(_sigmoid(_rng(w.wid, _EW, h).standard_normal((ntok, w.Dv))), dt)
+    return b, wr
+
+
+def gdn2_prefill_inputs(w: Workload, heads: Optional[Sequence[int]] = None,
+                        T: Optional[int] = None, lengths: Optional[Sequence[int]] = None):
+    """prefill_inputs plus the Gated DeltaNet-2 gates; returns (inputs, b [B,T,H,Dk],
+    w [B,T,H,Dv]). inputs.beta is left in place and unused by Gated DeltaNet-2."""
+    x = prefill_inputs(w, heads=heads, T=T, lengths=lengths)
+    B, Tt, Hs = x.beta.shape
+    b, wr = erase_write_gates(w, x.heads, B * Tt)
+    return x, b.view(B, Tt, Hs, w.Dk), wr.view(B, Tt, Hs, w.Dv)
+
+
+def gdn2_decode_inputs(w: Workload, heads: Optional[Sequence[int]] = None,
+                       N: Optional[int] = None):
+    """decode_inputs plus the Gated DeltaNet-2 gates b [N,H,Dk] and w [N,H,Dv]."""
+    x = decode_inputs(w, heads=heads, N=N)
+    b, wr = erase_write_gates(w, x.heads, x.beta.shape[0])
+    return x, b, wr

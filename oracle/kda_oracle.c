@@ -25,6 +25,11 @@
  * zhilingong.com, section 6) g is [Ttot, H] and step (1) scales every row of
  * S by the same exp(g_t); the other steps are unchanged.
  *
+ * With erase and write gates (Gated DeltaNet-2: "From Fast Weight Programmers
+ * to KDA", section "Gated DeltaNet-2") beta is replaced by b [Ttot, H, Dk] and
+ * w [Ttot, H, Dv]: (2) predicts through the gated key, v^ = S~^T (b_t * k_t),
+ * and (3) becomes e = w_t * v_t - v^.
+ *
  * Parity pins: the Python test-suite checks this file against the numpy
  * oracle (same definition, written independently) on the small workloads.
  */
@@ -56,7 +61,8 @@ void kda_oracle_set_num_threads(int n) {
 /* One (sequence, head) chain over tokens [t0, t1). S is Dk*Dv doubles,
  * updated in place; o gets the outputs of the chain's tokens. */
 static void chain(const float* q, const float* k, const float* v, const float* g,
-                  int scalar_gate, const float* beta, double scale, int H, int Dk, int Dv, int h,
+                  int scalar_gate, const float* beta, const float* eb, const float* ew,
+                  double scale, int H, int Dk, int Dv, int h,
                   int64_t t0, int64_t t1, double* S, double* o,
                   double* vhat, double* err, double* dec) {
     for (int64_t t = t0; t < t1; ++t) {
@@ -64,7 +70,9 @@ static void chain(const float* q, const float* k, const float* v, const float* g
         const float* kt = k + (t * H + h) * (int64_t)Dk;
         const float* vt = v + (t * H + h) * (int64_t)Dv;
         const float* gt = g + (t * H + h) * (int64_t)(scalar_gate ? 1 : Dk);
-        const double b = (double)beta[t * H + h];
+        const double b = eb ? 0.0 : (double)beta[t * H + h];
+        const float* bt = eb ? eb + (t * H + h) * (int64_t)Dk : NULL;
+        const float* wt = ew ? ew + (t * H + h) * (int64_t)Dv : NULL;
         for (int c = 0; c < Dk; ++c) dec[c] = exp((double)gt[scalar_gate ? 0 : c]);
         /* (1) forget */
         for (int c = 0; c < Dk; ++c)
@@ -72,11 +80,14 @@ static void chain(const float* q, const float* k, const float* v, const float* g
         /* (2) predict: v^ = S~^T k */
         for (int j = 0; j < Dv; ++j) vhat[j] = 0.0;
         for (int c = 0; c < Dk; ++c) {
-            const double kc = (double)kt[c];
+            const double kc = (double)kt[c] * (bt ? (double)bt[c] : 1.0);
             for (int j = 0; j < Dv; ++j) vhat[j] += S[c * Dv + j] * kc;
         }
         /* (3) correct */
-        for (int j = 0; j < Dv; ++j) err[j] = b * ((double)vt[j] - vhat[j]);
+        if (bt)
+            for (int j = 0; j < Dv; ++j) err[j] = (double)wt[j] * (double)vt[j] - vhat[j];
+        else
+            for (int j = 0; j < Dv; ++j) err[j] = b * ((double)vt[j] - vhat[j]);
         /* (4) write */
         for (int c = 0; c < Dk; ++c) {
             const double kc = (double)kt[c];
@@ -97,10 +108,10 @@ static void chain(const float* q, const float* k, const float* v, const float* g
  * g is [Ttot, H, Dk], or [Ttot, H] when scalar_gate is non-zero.
  * o: double [Ttot, H, Dv]; ht: double [num_seqs, H, Dk, Dv] (may be NULL).
  * Returns 0, or -1 on allocation failure. */
-int kda_oracle_prefill(const float* q, const float* k, const float* v, const float* g,
-                       int scalar_gate, const float* beta, double scale, const float* h0,
-                       const int32_t* cu_seqlens, int num_seqs, int H, int Dk, int Dv,
-                       double* o, double* ht) {
+static int prefill_impl(const float* q, const float* k, const float* v, const float* g,
+                        int scalar_gate, const float* beta, const float* eb, const float* ew,
+                        double scale, const float* h0, const int32_t* cu_seqlens, int num_seqs,
+                        int H, int Dk, int Dv, double* o, double* ht) {
     int failed = 0;
     const int64_t pairs = (int64_t)num_seqs * H;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
@@ -113,12 +124,52 @@ int kda_oracle_prefill(const float* q, const float* k, const float* v, const flo
         double* dec = err + Dv;
         const float* h0p = h0 ? h0 + ((int64_t)n * H + h) * (int64_t)Dk * Dv : NULL;
         for (int64_t i = 0; i < (int64_t)Dk * Dv; ++i) S[i] = h0p ? (double)h0p[i] : 0.0;
-        chain(q, k, v, g, scalar_gate, beta, scale, H, Dk, Dv, h, cu_seqlens[n],
+        chain(q, k, v, g, scalar_gate, beta, eb, ew, scale, H, Dk, Dv, h, cu_seqlens[n],
               cu_seqlens[n + 1], S, o,
               vhat, err, dec);
         if (ht) memcpy(ht + ((int64_t)n * H + h) * (int64_t)Dk * Dv, S,
                        sizeof(double) * (size_t)Dk * Dv);
         free(S);
+    }
+    return failed ? -1 : 0;
+}
+
+int kda_oracle_prefill(const float* q, const float* k, const float* v, const float* g,
+                       int scalar_gate, const float* beta, double scale, const float* h0,
+                       const int32_t* cu_seqlens, int num_seqs, int H, int Dk, int Dv,
+                       double* o, double* ht) {
+    return prefill_impl(q, k, v, g, scalar_gate, beta, NULL, NULL, scale, h0, cu_seqlens,
+                        num_seqs, H, Dk, Dv, o, ht);
+}
+
+/* Gated DeltaNet-2 prefill: g, b [Ttot, H, Dk]; w [Ttot, H, Dv]; the rest as
+ * kda_oracle_prefill. */
+int kda_oracle_gdn2_prefill(const float* q, const float* k, const float* v, const float* g,
+                            const float* b, const float* w, double scale, const float* h0,
+                            const int32_t* cu_seqlens, int num_seqs, int H, int Dk, int Dv,
+                            double* o, double* ht) {
+    return prefill_impl(q, k, v, g, 0, NULL, b, w, scale, h0, cu_seqlens, num_seqs, H, Dk, Dv,
+                        o, ht);
+}
+
+static int decode_impl(const float* q, const float* k, const float* v, const float* g,
+                       int scalar_gate, const float* beta, const float* eb, const float* ew,
+                       double scale, double* state, double* o, int N, int H, int Dk, int Dv) {
+    int failed = 0;
+    const int64_t pairs = (int64_t)N * H;
+#pragma omp parallel for schedule(static) reduction(| : failed)
+    for (int64_t p = 0; p < pairs; ++p) {
+        double* tmp = (double*)malloc(sizeof(double) * (2 * (size_t)Dv + Dk));
+        if (!tmp) { failed = 1; continue; }
+        /* a decode step is one token of a chain whose "time" index is the pair */
+        const int n = (int)(p / H), h = (int)(p % H);
+        chain(q + (int64_t)n * H * Dk, k + (int64_t)n * H * Dk, v + (int64_t)n * H * Dv,
+              g + (int64_t)n * H * (scalar_gate ? 1 : Dk), scalar_gate,
+              beta ? beta + (int64_t)n * H : NULL, eb ? eb + (int64_t)n * H * Dk : NULL,
+              ew ? ew + (int64_t)n * H * Dv : NULL, scale, H, Dk, Dv, h, 0, 1,
+              state + p * (int64_t)Dk * Dv, o + (int64_t)n * H * Dv, tmp, tmp + Dv,
+              tmp + 2 * Dv);
+        free(tmp);
     }
     return failed ? -1 : 0;
 }
@@ -129,20 +180,13 @@ int kda_oracle_prefill(const float* q, const float* k, const float* v, const flo
 int kda_oracle_decode(const float* q, const float* k, const float* v, const float* g,
                       int scalar_gate, const float* beta, double scale, double* state, double* o,
                       int N, int H, int Dk, int Dv) {
-    int failed = 0;
-    const int64_t pairs = (int64_t)N * H;
-#pragma omp parallel for schedule(static) reduction(| : failed)
-    for (int64_t p = 0; p < pairs; ++p) {
-        double* tmp = (double*)malloc(sizeof(double) * (2 * (size_t)Dv + Dk));
-        if (!tmp) { failed = 1; continue; }
-        /* a decode step is one token of a chain whose "time" index is the pair */
-        const int n = (int)(p / H), h = (int)(p % H);
-        chain(q + (int64_t)n * H * Dk, k + (int64_t)n * H * Dk, v + (int64_t)n * H * Dv,
-              g + (int64_t)n * H * (scalar_gate ? 1 : Dk), scalar_gate, beta + (int64_t)n * H,
-              scale, H, Dk, Dv, h, 0, 1,
-              state + p * (int64_t)Dk * Dv, o + (int64_t)n * H * Dv, tmp, tmp + Dv,
-              tmp + 2 * Dv);
-        free(tmp);
-    }
-    return failed ? -1 : 0;
+    return decode_impl(q, k, v, g, scalar_gate, beta, NULL, NULL, scale, state, o, N, H, Dk, Dv);
+}
+
+/* One Gated DeltaNet-2 decode step: g, b [N, H, Dk]; w [N, H, Dv]; the rest as
+ * kda_oracle_decode. */
+int kda_oracle_gdn2_decode(const float* q, const float* k, const float* v, const float* g,
+                           const float* b, const float* w, double scale, double* state,
+                           double* o, int N, int H, int Dk, int Dv) {
+    return decode_impl(q, k, v, g, 0, NULL, b, w, scale, state, o, N, H, Dk, Dv);
 }

@@ -29,12 +29,21 @@ per key channel: decay the whole state, then apply the delta rule to the
 decayed state ("Notes on Linear Attention", zhilingong.com, section 6;
 "From Fast Weight Programmers to KDA", section "Gated Delta Networks").
 
+Gated DeltaNet-2 (gdn2_forward, gdn2_decode) keeps KDA's per-channel decay and
+replaces beta by a per-key-channel erase gate b_t and a per-value-channel write
+gate w_t: decay, retrieve the old value through the gated key b_t * k_t, then
+write the residual w_t * v_t - v^ at the original key ("From Fast Weight
+Programmers to KDA", section "Gated DeltaNet-2", written there for the
+transposed state).
+
 Parity pins: every function here is pinned by tests/test_oracle_pins.py
 (worked example, read-back, locality, orthogonal-key example, additive
 brute force, DeltaNet and Gated DeltaNet reductions, operator order,
 stability, chunked mirror, resume/varlen/decode consistency; for the scalar
 gate: the matrix form alpha (I - beta k k^T) S + beta k v^T, the pure-decay
-closed form at beta = 0, and the per-channel recurrence with an equal gate).
+closed form at beta = 0, and the per-channel recurrence with an equal gate; for
+the erase/write gates: the matrix form, the collapse to KDA at b = beta 1,
+w = beta 1, and the additive closed form at b = 0).
 """
 from __future__ import annotations
 
@@ -180,4 +189,47 @@ def gdn_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta:
         state, dtype=np.float64)
     err = beta[..., None] * (v - np.einsum("nhkv,nhk->nhv", S_bar, k))
     S = S_bar + k[..., :, None] * err[..., None, :]
+    return np.einsum("nhkv,nhk->nhv", S, scale * q), S
+
+
+def gdn2_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, b: np.ndarray,
+                 w: np.ndarray, scale: float = 1.0, h0: Optional[np.ndarray] = None,
+                 cu_seqlens: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Gated DeltaNet-2, token by token (float64 results).
+
+    q, k, g, b: [B, T, H, Dk] (b = erase gate per key channel); v, w: [B, T, H, Dv]
+    (w = write gate per value channel); h0, cu_seqlens and the returns as in kda_forward.
+    Per token, following jonahsamost.bearblog.dev, "Gated DeltaNet-2" (in the d_k x d_v
+    layout): S_bar = Diag(exp g_t) S; v^ = S_bar^T (b_t * k_t); S = S_bar + k_t (w_t * v_t - v^)^T;
+    then the read o_t = S^T (scale q_t) of the updated state.
+    """
+    q, k, v, g, b, w = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, b, w))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    fl = lambda a, d: a.reshape(B * T, H, d)
+    qf, kf, gf, bf = fl(q, Dk), fl(k, Dk), fl(g, Dk), fl(b, Dk)
+    vf, wf = fl(v, Dv), fl(w, Dv)
+    segs = _segments(B * T, B, T, cu_seqlens)
+    o = np.zeros((B * T, H, Dv))
+    ht = np.zeros((len(segs), H, Dk, Dv))
+    for n, (s, e_) in enumerate(segs):
+        S = np.zeros((H, Dk, Dv)) if h0 is None else np.array(h0[n], dtype=np.float64)
+        for t in range(s, e_):
+            S_bar = np.exp(gf[t])[:, :, None] * S                          # decay
+            v_hat = np.einsum("hkv,hk->hv", S_bar, bf[t] * kf[t])          # gated-key read
+            S = S_bar + kf[t][:, :, None] * (wf[t] * vf[t] - v_hat)[:, None, :]
+            o[t] = np.einsum("hkv,hk->hv", S, scale * qf[t])               # read
+        ht[n] = S
+    return o.reshape(B, T, H, Dv), ht
+
+
+def gdn2_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, b: np.ndarray,
+                w: np.ndarray, state: np.ndarray,
+                scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+    """One Gated DeltaNet-2 step per (request, head): q, k, g, b [N, H, Dk]; v, w [N, H, Dv];
+    state [N, H, Dk, Dv]. Returns (o [N, H, Dv], new state)."""
+    q, k, v, g, b, w = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, b, w))
+    S_bar = np.exp(g)[..., :, None] * np.asarray(state, dtype=np.float64)
+    v_hat = np.einsum("nhkv,nhk->nhv", S_bar, b * k)
+    S = S_bar + k[..., :, None] * (w * v - v_hat)[..., None, :]
     return np.einsum("nhkv,nhk->nhv", S, scale * q), S

@@ -46,6 +46,14 @@ def _load():
         lib.kda_oracle_decode.argtypes = [fp, fp, fp, fp, ctypes.c_int, fp, ctypes.c_double, dp, dp,
                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.kda_oracle_decode.restype = ctypes.c_int
+        lib.kda_oracle_gdn2_prefill.argtypes = [fp, fp, fp, fp, fp, fp, ctypes.c_double, fp, ip,
+                                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, dp, dp]
+        lib.kda_oracle_gdn2_prefill.restype = ctypes.c_int
+        lib.kda_oracle_gdn2_decode.argtypes = [fp, fp, fp, fp, fp, fp, ctypes.c_double, dp, dp,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int]
+        lib.kda_oracle_gdn2_decode.restype = ctypes.c_int
         lib.kda_oracle_num_threads.restype = ctypes.c_int
         lib.kda_oracle_set_num_threads.argtypes = [ctypes.c_int]
         lib.kda_oracle_set_num_threads.restype = None
@@ -143,3 +151,54 @@ def decode(q, k, v, g, beta, state, scale: float = 1.0):
 def gdn_decode(q, k, v, g, beta, state, scale: float = 1.0):
     """One Gated DeltaNet step (g [N, H]); returns float64 (o, new state)."""
     return _decode(q, k, v, g, beta, state, scale, True)
+
+
+def gdn2_prefill(q, k, v, g, b, w, scale: float = 1.0, h0=None,
+                 cu_seqlens: Optional[Sequence[int]] = None):
+    """Gated DeltaNet-2 (erase gate b [B,T,H,Dk], write gate w [B,T,H,Dv]); returns float64
+    (o, ht) as prefill."""
+    qf, kf, vf, gf, bf, wf = (_f32(x) for x in (q, k, v, g, b, w))
+    B, T, H, Dk = qf.shape
+    Dv = vf.shape[-1]
+    if gf.shape != qf.shape or bf.shape != qf.shape or wf.shape != vf.shape:
+        raise ValueError("g and b must match q, w must match v")
+    if cu_seqlens is None:
+        cu = (np.arange(B + 1, dtype=np.int64) * T).astype(np.int32)
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    N = len(cu) - 1
+    h0f = None if h0 is None else _f32(h0)
+    o = np.zeros((B, T, H, Dv), dtype=np.float64)
+    ht = np.zeros((N, H, Dk, Dv), dtype=np.float64)
+    fp = ctypes.c_float
+    rc = _load().kda_oracle_gdn2_prefill(
+        _p(qf, fp), _p(kf, fp), _p(vf, fp), _p(gf, fp), _p(bf, fp), _p(wf, fp), float(scale),
+        None if h0f is None else _p(h0f, fp), _p(cu, ctypes.c_int32), N, H, Dk, Dv,
+        _p(o, ctypes.c_double), _p(ht, ctypes.c_double))
+    if rc != 0:
+        raise MemoryError("kda_oracle_gdn2_prefill failed")
+    return o, ht
+
+
+def gdn2_decode(q, k, v, g, b, w, state, scale: float = 1.0):
+    """One Gated DeltaNet-2 step (b [N,H,Dk], w [N,H,Dv]); returns float64 (o, new state)."""
+    qf, kf, vf, gf, bf, wf = (_f32(x) for x in (q, k, v, g, b, w))
+    N, H, Dk = qf.shape
+    Dv = vf.shape[-1]
+    if gf.shape != qf.shape or bf.shape != qf.shape or wf.shape != vf.shape:
+        raise ValueError("g and b must match q, w must match v")
+    try:
+        import torch
+        if isinstance(state, torch.Tensor):
+            state = state.detach().to("cpu").numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    S = np.array(state, dtype=np.float64, order="C", copy=True)
+    o = np.zeros((N, H, Dv), dtype=np.float64)
+    fp = ctypes.c_float
+    rc = _load().kda_oracle_gdn2_decode(
+        _p(qf, fp), _p(kf, fp), _p(vf, fp), _p(gf, fp), _p(bf, fp), _p(wf, fp), float(scale),
+        _p(S, ctypes.c_double), _p(o, ctypes.c_double), N, H, Dk, Dv)
+    if rc != 0:
+        raise MemoryError("kda_oracle_gdn2_decode failed")
+    return o, S

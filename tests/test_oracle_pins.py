@@ -445,3 +445,93 @@ def test_gdn_decode_steps_equal_forward():
         od, S = kda_oracle.gdn_decode(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], S)
         np.testing.assert_allclose(od, o[:, t], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(S, ht, rtol=1e-12, atol=1e-12)
+
+
+# --- Gated DeltaNet-2 (erase gate b, write gate w) --------------------------------------------
+def test_gdn2_matrix_form():
+    """The oracle (decay, read through the gated key, write the residual at k) equals the
+    one-line update of jonahsamost.bearblog.dev, "Gated DeltaNet-2",
+    S_t = S_(t-1) D_t (I - (b_t * k_t) k_t^T) + (w_t * v_t) k_t^T for the d_v x d_k state,
+    taken here in that orientation and transposed back."""
+    rng = np.random.default_rng(71)
+    T, Dk, Dv = 22, 6, 5
+    q, k, v, _ = _random_seq(rng, T, Dk, Dv)
+    g = -rng.uniform(0, 1, (T, Dk))
+    b = rng.uniform(0, 1, (T, Dk))
+    w = rng.uniform(0, 1, (T, Dv))
+    S0 = rng.standard_normal((Dk, Dv))
+    P = S0.T.copy()                                   # d_v x d_k, the page's orientation
+    outs = []
+    for t in range(T):
+        P = P @ np.diag(np.exp(g[t])) @ (np.eye(Dk) - np.outer(b[t] * k[t], k[t])) \
+            + np.outer(w[t] * v[t], k[t])
+        outs.append(P @ q[t])
+    o, ht = kda_oracle.gdn2_forward(q[None, :, None], k[None, :, None], v[None, :, None],
+                                    g[None, :, None], b[None, :, None], w[None, :, None],
+                                    h0=S0[None, None])
+    np.testing.assert_allclose(o[0, :, 0], np.array(outs), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ht[0, 0], P.T, rtol=1e-12, atol=1e-12)
+
+
+def test_gdn2_collapses_to_kda():
+    """b = beta 1 and w = beta 1 give KDA (jonahsamost.bearblog.dev, "Gated DeltaNet-2"); two
+    independently written oracles, packed sequences with an empty one and h0."""
+    w_ = I.WORKLOADS[4]
+    x = I.prefill_inputs(w_, heads=[3], lengths=[40, 0, 70])
+    q, k, v, g, beta, _, cu = _prefill_np(x)
+    rng = np.random.default_rng(72)
+    h0 = rng.standard_normal((3, 1, q.shape[-1], v.shape[-1]))
+    bb = np.repeat(beta[..., None], q.shape[-1], axis=-1)
+    ww = np.repeat(beta[..., None], v.shape[-1], axis=-1)
+    o, ht = kda_oracle.gdn2_forward(q, k, v, g, bb, ww, h0=h0, cu_seqlens=cu)
+    o2, ht2 = kda_oracle.kda_forward(q, k, v, g, beta, h0=h0, cu_seqlens=cu)
+    assert _rel(o, o2) <= 1e-12
+    assert _rel(ht, ht2) <= 1e-12
+
+
+def test_gdn2_zero_erase_is_gated_linear_attention():
+    """b = 0 erases nothing: S_t = Diag(exp g_t) S_(t-1) + k_t (w_t * v_t)^T, so with S_0 = 0
+    o_t = sum_(j <= t) (q_t * exp(G_t - G_j)) . k_j (w_j * v_j), brute force over pairs."""
+    rng = np.random.default_rng(73)
+    T, Dk, Dv = 18, 4, 3
+    q = rng.standard_normal((T, Dk))
+    k = rng.standard_normal((T, Dk))
+    v = rng.standard_normal((T, Dv))
+    g = -rng.uniform(0, 0.5, (T, Dk))
+    w = rng.uniform(0, 1, (T, Dv))
+    G = np.cumsum(g, axis=0)
+    ref = np.zeros((T, Dv))
+    for t in range(T):
+        for j in range(t + 1):
+            ref[t] += np.sum(q[t] * np.exp(G[t] - G[j]) * k[j]) * (w[j] * v[j])
+    o, _ = kda_oracle.gdn2_forward(q[None, :, None], k[None, :, None], v[None, :, None],
+                                   g[None, :, None], np.zeros((1, T, 1, Dk)), w[None, :, None])
+    np.testing.assert_allclose(o[0, :, 0], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_native_gdn2_matches_numpy():
+    for x, b, w in (I.gdn2_prefill_inputs(I.WORKLOADS[1], heads=[0, 3], T=130),
+                    I.gdn2_prefill_inputs(I.WORKLOADS[4], heads=[2], lengths=[65, 0, 1, 40])):
+        q, k, v, g, _, h0, cu = _prefill_np(x)
+        o_ref, ht_ref = kda_oracle.gdn2_forward(q, k, v, g, _np(b), _np(w), h0=h0, cu_seqlens=cu)
+        o_c, ht_c = native.gdn2_prefill(x.q, x.k, x.v, x.g, b, w, h0=x.h0, cu_seqlens=cu)
+        assert _rel(o_c, o_ref) <= 1e-12
+        assert _rel(ht_c, ht_ref) <= 1e-12
+    y, b, w = I.gdn2_decode_inputs(I.WORKLOADS[3], heads=[0, 9], N=4)
+    args = [t.double().numpy() for t in (y.q, y.k, y.v, y.g, b, w, y.state)]
+    o_ref, S_ref = kda_oracle.gdn2_decode(*args, scale=0.7)
+    o_c, S_c = native.gdn2_decode(y.q, y.k, y.v, y.g, b, w, y.state, scale=0.7)
+    assert _rel(o_c, o_ref) <= 1e-12
+    assert _rel(S_c, S_ref) <= 1e-12
+
+
+def test_gdn2_decode_steps_equal_forward():
+    x, b, w = I.gdn2_prefill_inputs(I.WORKLOADS[1], heads=[1], T=20)
+    q, k, v, g, _, h0, _ = _prefill_np(x)
+    bn, wn = _np(b), _np(w)
+    o, ht = kda_oracle.gdn2_forward(q, k, v, g, bn, wn, h0=h0)
+    S = h0
+    for t in range(q.shape[1]):
+        od, S = kda_oracle.gdn2_decode(q[:, t], k[:, t], v[:, t], g[:, t], bn[:, t], wn[:, t], S)
+        np.testing.assert_allclose(od, o[:, t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S, ht, rtol=1e-12, atol=1e-12)
