@@ -11,7 +11,10 @@ raise.
     o = decode_step(q, k, v, g, beta, state, scale=1.0)     # state updated in place
 
 Gated DeltaNet (one scalar gate per token and head, g [B,T,H] / [N,H]) has
-the same calls under the names gdn_fwd_chunked and gdn_decode_step.
+the same calls under the names gdn_fwd_chunked and gdn_decode_step; Gated
+DeltaNet-2 (erase gate b per key channel and write gate w per value channel in
+place of beta) under gdn2_fwd_chunked(q, k, v, g, b, w, ...) and
+gdn2_decode_step(q, k, v, g, b, w, state, ...).
 """
 from __future__ import annotations
 
@@ -31,7 +34,8 @@ KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 
 EXPORTED = ("kda_status_string", "kda_fwd_chunked_workspace_size", "kda_fwd_chunked",
-            "kda_decode_step", "kda_gdn_fwd_chunked", "kda_gdn_decode_step")
+            "kda_decode_step", "kda_gdn_fwd_chunked", "kda_gdn_decode_step",
+            "kda_gdn2_fwd_chunked", "kda_gdn2_decode_step")
 
 
 class KDAError(RuntimeError):
@@ -65,6 +69,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, i, i, i, i, i, i, vp]
         fn.restype = i
+    lib.kda_gdn2_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, vp, f, vp, vp, vp, vp, i, i, i, i, i,
+                                         i, i, i, vp, sz, vp]
+    lib.kda_gdn2_fwd_chunked.restype = i
+    lib.kda_gdn2_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, f, vp, vp, i, i, i, i, i, i, vp]
+    lib.kda_gdn2_decode_step.restype = i
     if path is None:
         _lib_handle = lib
     return lib
@@ -119,7 +128,8 @@ def _check_shape(name, t, shape):
 def _check_same_dtype(ref, **ts):
     for name, t in ts.items():
         if t.dtype != ref.dtype:
-            raise TypeError(f"{name} is {t.dtype}, q is {ref.dtype}: q, k, v and beta share one dtype")
+            raise TypeError(f"{name} is {t.dtype}, q is {ref.dtype}: q, k, v and beta (or b, w) "
+                            "share one dtype")
 
 
 def fwd_chunked(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
@@ -141,8 +151,17 @@ def gdn_fwd_chunked(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
                         cu_seqlens, workspace, out, final_state, out_dtype)
 
 
+def gdn2_fwd_chunked(q, k, v, g, b, w, scale: float = 1.0, initial_state=None,
+                     output_final_state: bool = True, cu_seqlens=None, workspace=None,
+                     out=None, final_state=None, out_dtype=None):
+    """Gated DeltaNet-2 chunked prefill: as fwd_chunked with the erase gate b [B,T,H,Dk] and
+    the write gate w [B,T,H,Dv] (dtype of q) in place of beta."""
+    return _fwd_chunked(False, q, k, v, g, None, scale, initial_state, output_final_state,
+                        cu_seqlens, workspace, out, final_state, out_dtype, gates=(b, w))
+
+
 def _fwd_chunked(scalar_gate, q, k, v, g, beta, scale, initial_state, output_final_state,
-                 cu_seqlens, workspace, out, final_state, out_dtype):
+                 cu_seqlens, workspace, out, final_state, out_dtype, gates=None):
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if q.dim() != 4 or v.dim() != 4:
@@ -150,13 +169,21 @@ def _fwd_chunked(scalar_gate, q, k, v, g, beta, scale, initial_state, output_fin
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     code = _dtype_code(q)
-    _check_same_dtype(q, k=k, v=v, beta=beta)
+    if gates is None:
+        _check_same_dtype(q, k=k, v=v, beta=beta)
+        _check_shape("beta", beta, (B, T, H))
+        extra = (beta,)
+    else:
+        eb, ew = gates
+        _check_same_dtype(q, k=k, v=v, b=eb, w=ew)
+        _check_shape("b", eb, (B, T, H, Dk))
+        _check_shape("w", ew, (B, T, H, Dv))
+        extra = (eb, ew)
     varlen = cu_seqlens is not None
     N = (cu_seqlens.numel() - 1) if varlen else B
     _check_shape("k", k, (B, T, H, Dk))
     _check_shape("g", g, (B, T, H) if scalar_gate else (B, T, H, Dk))
     _check_shape("v", v, (B, T, H, Dv))
-    _check_shape("beta", beta, (B, T, H))
     _check_shape("initial_state", initial_state, (N, H, Dk, Dv))
     _check_shape("out", out, (B, T, H, Dv))
     _check_shape("final_state", final_state, (N, H, Dk, Dv))
@@ -170,7 +197,7 @@ def _fwd_chunked(scalar_gate, q, k, v, g, beta, scale, initial_state, output_fin
         raise TypeError("cu_seqlens must be a 1-D int32 tensor")
     if workspace is not None and workspace.dtype != torch.uint8:
         raise TypeError("workspace must be a uint8 tensor")
-    _check_gpu(q, k, v, g, beta, initial_state, cu_seqlens, workspace, out, final_state)
+    _check_gpu(q, k, v, g, *extra, initial_state, cu_seqlens, workspace, out, final_state)
     nbytes = workspace_size(B, T, H, Dk, Dv, N, varlen, code)
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
@@ -180,9 +207,11 @@ def _fwd_chunked(scalar_gate, q, k, v, g, beta, scale, initial_state, output_fin
     if output_final_state:
         ht = final_state if final_state is not None else torch.empty(
             (N, H, Dk, Dv), dtype=torch.float32, device=q.device)
-    name = "kda_gdn_fwd_chunked" if scalar_gate else "kda_fwd_chunked"
+    name = ("kda_gdn2_fwd_chunked" if gates is not None else
+            "kda_gdn_fwd_chunked" if scalar_gate else "kda_fwd_chunked")
     st = getattr(load_library(), name)(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(initial_state),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), *(_ptr(t) for t in extra), float(scale),
+        _ptr(initial_state),
         _ptr(ht), _ptr(o), _ptr(cu_seqlens), int(N), int(B), int(T), int(H), int(Dk), int(Dv),
         code, ocode, _ptr(workspace), nbytes, _stream(q.device))
     if st != KDA_SUCCESS:
@@ -201,7 +230,12 @@ def gdn_decode_step(q, k, v, g, beta, state, scale: float = 1.0, out=None, out_d
     return _decode_step(True, q, k, v, g, beta, state, scale, out, out_dtype)
 
 
-def _decode_step(scalar_gate, q, k, v, g, beta, state, scale, out, out_dtype):
+def gdn2_decode_step(q, k, v, g, b, w, state, scale: float = 1.0, out=None, out_dtype=None):
+    """One Gated DeltaNet-2 decode step: as decode_step with b [N,H,Dk] and w [N,H,Dv]."""
+    return _decode_step(False, q, k, v, g, None, state, scale, out, out_dtype, gates=(b, w))
+
+
+def _decode_step(scalar_gate, q, k, v, g, beta, state, scale, out, out_dtype, gates=None):
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if q.dim() != 3 or v.dim() != 3:
@@ -209,21 +243,31 @@ def _decode_step(scalar_gate, q, k, v, g, beta, state, scale, out, out_dtype):
     N, H, Dk = q.shape
     Dv = v.shape[-1]
     code = _dtype_code(q)
-    _check_same_dtype(q, k=k, v=v, beta=beta)
+    if gates is None:
+        _check_same_dtype(q, k=k, v=v, beta=beta)
+        _check_shape("beta", beta, (N, H))
+        extra = (beta,)
+    else:
+        eb, ew = gates
+        _check_same_dtype(q, k=k, v=v, b=eb, w=ew)
+        _check_shape("b", eb, (N, H, Dk))
+        _check_shape("w", ew, (N, H, Dv))
+        extra = (eb, ew)
     _check_shape("k", k, (N, H, Dk))
     _check_shape("g", g, (N, H) if scalar_gate else (N, H, Dk))
     _check_shape("v", v, (N, H, Dv))
-    _check_shape("beta", beta, (N, H))
     _check_shape("state", state, (N, H, Dk, Dv))
     _check_shape("out", out, (N, H, Dv))
     if g.dtype != torch.float32 or state.dtype != torch.float32:
         raise TypeError("g and state must be float32")
-    _check_gpu(q, k, v, g, beta, state, out)
+    _check_gpu(q, k, v, g, *extra, state, out)
     o = out if out is not None else torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
-    name = "kda_gdn_decode_step" if scalar_gate else "kda_decode_step"
+    name = ("kda_gdn2_decode_step" if gates is not None else
+            "kda_gdn_decode_step" if scalar_gate else "kda_decode_step")
     st = getattr(load_library(), name)(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(state), _ptr(o),
-        int(N), int(H), int(Dk), int(Dv), code, _dtype_code(o), _stream(q.device))
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), *(_ptr(t) for t in extra), float(scale),
+        _ptr(state), _ptr(o), int(N), int(H), int(Dk), int(Dv), code, _dtype_code(o),
+        _stream(q.device))
     if st != KDA_SUCCESS:
         raise KDAError(st, name)
     return o

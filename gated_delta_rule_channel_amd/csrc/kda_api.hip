@@ -9,14 +9,16 @@
 namespace kda {
 hipError_t launch_decode(bool sg, bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
                          const void* k, const void* v, const float* g, const void* beta,
-                         float scale, float* state, void* o, int N, int H, hipStream_t s);
+                         const void* eb, const void* ew, float scale, float* state, void* o,
+                         int N, int H, hipStream_t s);
 hipError_t launch_chunk_map(const int32_t* cu, int N, int T, int max_slots, void* tab,
                             int32_t* seq_off, hipStream_t s);
 hipError_t launch_prefill(bool sg, bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
                           const void* k, const void* v, const float* g, const void* beta,
-                          float scale, const float* h0, float* ht, void* o, const int32_t* cu,
-                          int T, const void* tab, const int32_t* seq_off, uint8_t* blocks, int N,
-                          int H, int max_slots, hipStream_t s);
+                          const void* eb, const void* ew, float scale, const float* h0,
+                          float* ht, void* o, const int32_t* cu, int T, const void* tab,
+                          const int32_t* seq_off, uint8_t* blocks, int N, int H, int max_slots,
+                          hipStream_t s);
 size_t prefill_block_bytes(int Dk, int Dv, bool bf16_in);
 }  // namespace kda
 
@@ -52,18 +54,20 @@ kda_status plan_prefill(int B, int T, int H, int Dk, int Dv, int num_seqs, bool 
     return KDA_SUCCESS;
 }
 
-// sg: scalar gate (Gated DeltaNet), g holds one value per token and head
+// sg: scalar gate (Gated DeltaNet), g holds one value per token and head; eb, ew: the erase
+// and write gates of Gated DeltaNet-2, given together in place of beta
 kda_status fwd_chunked(bool sg, const void* q, const void* k, const void* v, const float* g,
-                       const void* beta, float scale, const float* h0, float* ht, void* o,
-                       const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int Dk,
-                       int Dv, kda_dtype dtype, kda_dtype o_dtype, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-    if (!q || !k || !v || !g || !beta || !o) return KDA_ERROR_INVALID_VALUE;
+                       const void* beta, const void* eb, const void* ew, float scale,
+                       const float* h0, float* ht, void* o, const int32_t* cu_seqlens,
+                       int num_seqs, int B, int T, int H, int Dk, int Dv, kda_dtype dtype,
+                       kda_dtype o_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !g || !o) return KDA_ERROR_INVALID_VALUE;
+    if (eb || ew ? !(eb && ew) : !beta) return KDA_ERROR_INVALID_VALUE;
     if (!dtype_ok(o_dtype)) return KDA_ERROR_INVALID_VALUE;
     PrefillPlan p;
     const kda_status st = plan_prefill(B, T, H, Dk, Dv, num_seqs, cu_seqlens != nullptr, dtype, &p);
     if (st != KDA_SUCCESS) return st;
-    const void* ptrs[] = {q, k, v, g, beta, o, h0, ht};
+    const void* ptrs[] = {q, k, v, g, beta, eb, ew, o, h0, ht};
     for (const void* ptr : ptrs)
         if (ptr && !aligned(ptr, 16)) return KDA_ERROR_INVALID_VALUE;
     if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERROR_INVALID_VALUE;
@@ -81,24 +85,26 @@ kda_status fwd_chunked(bool sg, const void* q, const void* k, const void* v, con
             return KDA_ERROR_LAUNCH;
     }
     if (kda::launch_prefill(sg, dtype == KDA_DTYPE_BF16, o_dtype == KDA_DTYPE_BF16, Dk, Dv, q, k,
-                            v, g, beta, scale, h0, ht, o, cu_seqlens, T, tab, seq_off,
+                            v, g, beta, eb, ew, scale, h0, ht, o, cu_seqlens, T, tab, seq_off,
                             ws + p.blocks_off, p.nseq, H, (int)p.max_slots, s) != hipSuccess)
         return KDA_ERROR_LAUNCH;
     return KDA_SUCCESS;
 }
 
 kda_status decode_step(bool sg, const void* q, const void* k, const void* v, const float* g,
-                       const void* beta, float scale, float* state, void* o, int N, int H,
-                       int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype, void* stream) {
-    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERROR_INVALID_VALUE;
+                       const void* beta, const void* eb, const void* ew, float scale,
+                       float* state, void* o, int N, int H, int Dk, int Dv, kda_dtype dtype,
+                       kda_dtype o_dtype, void* stream) {
+    if (!q || !k || !v || !g || !state || !o) return KDA_ERROR_INVALID_VALUE;
+    if (eb || ew ? !(eb && ew) : !beta) return KDA_ERROR_INVALID_VALUE;
     if (N <= 0 || H <= 0 || !head_ok(Dk) || !head_ok(Dv)) return KDA_ERROR_INVALID_VALUE;
     if (!dtype_ok(dtype) || !dtype_ok(o_dtype)) return KDA_ERROR_INVALID_VALUE;
     if ((long long)N * H > (1LL << 31) - 1) return KDA_ERROR_NOT_SUPPORTED;
-    const void* ptrs[] = {q, k, v, g, beta, state, o};
+    const void* ptrs[] = {q, k, v, g, beta, eb, ew, state, o};
     for (const void* ptr : ptrs)
-        if (!aligned(ptr, 16)) return KDA_ERROR_INVALID_VALUE;
+        if (ptr && !aligned(ptr, 16)) return KDA_ERROR_INVALID_VALUE;
     if (kda::launch_decode(sg, dtype == KDA_DTYPE_BF16, o_dtype == KDA_DTYPE_BF16, Dk, Dv, q, k, v,
-                           g, beta, scale, state, o, N, H,
+                           g, beta, eb, ew, scale, state, o, N, H,
                            reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
         return KDA_ERROR_LAUNCH;
     return KDA_SUCCESS;
@@ -134,8 +140,10 @@ kda_status kda_fwd_chunked(const void* q, const void* k, const void* v, const fl
                            const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int Dk,
                            int Dv, kda_dtype dtype, kda_dtype o_dtype, void* workspace,
                            size_t workspace_bytes, void* stream) {
-    return fwd_chunked(false, q, k, v, g, beta, scale, h0, ht, o, cu_seqlens, num_seqs, B, T, H,
-                       Dk, Dv, dtype, o_dtype, workspace, workspace_bytes, stream);
+    if (!beta) return KDA_ERROR_INVALID_VALUE;
+    return fwd_chunked(false, q, k, v, g, beta, nullptr, nullptr, scale, h0, ht, o, cu_seqlens,
+                       num_seqs, B, T, H, Dk, Dv, dtype, o_dtype, workspace, workspace_bytes,
+                       stream);
 }
 
 kda_status kda_gdn_fwd_chunked(const void* q, const void* k, const void* v, const float* g,
@@ -143,23 +151,47 @@ kda_status kda_gdn_fwd_chunked(const void* q, const void* k, const void* v, cons
                                void* o, const int32_t* cu_seqlens, int num_seqs, int B, int T,
                                int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
                                void* workspace, size_t workspace_bytes, void* stream) {
-    return fwd_chunked(true, q, k, v, g, beta, scale, h0, ht, o, cu_seqlens, num_seqs, B, T, H,
-                       Dk, Dv, dtype, o_dtype, workspace, workspace_bytes, stream);
+    if (!beta) return KDA_ERROR_INVALID_VALUE;
+    return fwd_chunked(true, q, k, v, g, beta, nullptr, nullptr, scale, h0, ht, o, cu_seqlens,
+                       num_seqs, B, T, H, Dk, Dv, dtype, o_dtype, workspace, workspace_bytes,
+                       stream);
+}
+
+kda_status kda_gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* g,
+                                const void* b, const void* w, float scale, const float* h0,
+                                float* ht, void* o, const int32_t* cu_seqlens, int num_seqs,
+                                int B, int T, int H, int Dk, int Dv, kda_dtype dtype,
+                                kda_dtype o_dtype, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    if (!b || !w) return KDA_ERROR_INVALID_VALUE;
+    return fwd_chunked(false, q, k, v, g, nullptr, b, w, scale, h0, ht, o, cu_seqlens, num_seqs,
+                       B, T, H, Dk, Dv, dtype, o_dtype, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
                            const void* beta, float scale, float* state, void* o, int N, int H,
                            int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype, void* stream) {
-    return decode_step(false, q, k, v, g, beta, scale, state, o, N, H, Dk, Dv, dtype, o_dtype,
-                       stream);
+    if (!beta) return KDA_ERROR_INVALID_VALUE;
+    return decode_step(false, q, k, v, g, beta, nullptr, nullptr, scale, state, o, N, H, Dk, Dv,
+                       dtype, o_dtype, stream);
 }
 
 kda_status kda_gdn_decode_step(const void* q, const void* k, const void* v, const float* g,
                                const void* beta, float scale, float* state, void* o, int N,
                                int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
                                void* stream) {
-    return decode_step(true, q, k, v, g, beta, scale, state, o, N, H, Dk, Dv, dtype, o_dtype,
-                       stream);
+    if (!beta) return KDA_ERROR_INVALID_VALUE;
+    return decode_step(true, q, k, v, g, beta, nullptr, nullptr, scale, state, o, N, H, Dk, Dv,
+                       dtype, o_dtype, stream);
+}
+
+kda_status kda_gdn2_decode_step(const void* q, const void* k, const void* v, const float* g,
+                                const void* b, const void* w, float scale, float* state, void* o,
+                                int N, int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
+                                void* stream) {
+    if (!b || !w) return KDA_ERROR_INVALID_VALUE;
+    return decode_step(false, q, k, v, g, nullptr, b, w, scale, state, o, N, H, Dk, Dv, dtype,
+                       o_dtype, stream);
 }
 
 }  // extern "C"

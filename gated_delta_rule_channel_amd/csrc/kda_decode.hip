@@ -20,7 +20,10 @@
 //
 // SG selects the scalar gate of Gated DeltaNet ("Notes on Linear Attention",
 // section 6): g holds one log-decay per (request, head) and every row of S
-// decays by the same factor.
+// decays by the same factor. EW selects the erase and write gates of Gated
+// DeltaNet-2 ("From Fast Weight Programmers to KDA", section "Gated
+// DeltaNet-2"): the prediction reads through b * k (b per key channel) and
+// the error is w * v - v^ (w per value channel); the write stays at k.
 #include "kda_common.h"
 
 namespace kda {
@@ -38,11 +41,11 @@ struct DecodeShape {
     static_assert(NT % CG == 0 && DK % RS == 0 && RPT >= 1, "decode tiling");
 };
 
-template <typename TI, typename TO, int DK, int DV, bool SG>
+template <typename TI, typename TO, int DK, int DV, bool SG, bool EW>
 __global__ __launch_bounds__(1024) void decode_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
-    const float* __restrict__ g, const TI* __restrict__ beta, float scale,
-    float* __restrict__ state, TO* __restrict__ o) {
+    const float* __restrict__ g, const TI* __restrict__ beta, const TI* __restrict__ eb,
+    const TI* __restrict__ ew, float scale, float* __restrict__ state, TO* __restrict__ o) {
     using Sh = DecodeShape<DK, DV>;
     constexpr int CG = Sh::CG, RS = Sh::RS, RPT = Sh::RPT, NW = Sh::NW;
     __shared__ float4 red_vh[NW][CG];
@@ -79,9 +82,11 @@ __global__ __launch_bounds__(1024) void decode_kernel(
         const float kk = to_f(kh[r]);
         const float qq = scale * to_f(qh[r]);
         kr[i] = kk;
+        // the prediction's key: k, or b * k with an erase gate
+        const float kp = EW ? kk * to_f(eb[(size_t)head * DK + r]) : kk;
         s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;       // (1) forget
-        vh.x += kk * s[i].x; vh.y += kk * s[i].y;                  // (2) predict
-        vh.z += kk * s[i].z; vh.w += kk * s[i].w;
+        vh.x += kp * s[i].x; vh.y += kp * s[i].y;                  // (2) predict
+        vh.z += kp * s[i].z; vh.w += kp * s[i].w;
         rq.x += qq * s[i].x; rq.y += qq * s[i].y;                  // read of S~
         rq.z += qq * s[i].z; rq.w += qq * s[i].w;
         kq += kk * qq;
@@ -111,11 +116,17 @@ __global__ __launch_bounds__(1024) void decode_kernel(
         rq.x += b.x; rq.y += b.y; rq.z += b.z; rq.w += b.w;
         kq += red_kq[w];
     }
-    const float bt = to_f(beta[head]);
     const float4 vv = load4f(v + (size_t)head * DV + 4 * cg);
     float4 e;                                                      // (3) correct
-    e.x = bt * (vv.x - vh.x); e.y = bt * (vv.y - vh.y);
-    e.z = bt * (vv.z - vh.z); e.w = bt * (vv.w - vh.w);
+    if constexpr (EW) {
+        const float4 ww = load4f(ew + (size_t)head * DV + 4 * cg);
+        e.x = ww.x * vv.x - vh.x; e.y = ww.y * vv.y - vh.y;
+        e.z = ww.z * vv.z - vh.z; e.w = ww.w * vv.w - vh.w;
+    } else {
+        const float bt = to_f(beta[head]);
+        e.x = bt * (vv.x - vh.x); e.y = bt * (vv.y - vh.y);
+        e.z = bt * (vv.z - vh.z); e.w = bt * (vv.w - vh.w);
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {                                // (4) write, in place
         const int r = rs + RS * i;
@@ -132,29 +143,33 @@ __global__ __launch_bounds__(1024) void decode_kernel(
 
 template <typename TI, typename TO, int DK, int DV>
 static hipError_t launch_decode_t(bool sg, const void* q, const void* k, const void* v,
-                                  const float* g, const void* beta, float scale, float* state,
-                                  void* o, int N, int H, hipStream_t stream) {
+                                  const float* g, const void* beta, const void* eb,
+                                  const void* ew, float scale, float* state, void* o, int N,
+                                  int H, hipStream_t stream) {
     const dim3 grid((unsigned)((long long)N * H));
     const dim3 block(DecodeShape<DK, DV>::NT);
-    if (sg)
-        hipLaunchKernelGGL((decode_kernel<TI, TO, DK, DV, true>), grid, block, 0, stream,
-                           (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
-                           state, (TO*)o);
+    const TI *tq = (const TI*)q, *tk = (const TI*)k, *tv = (const TI*)v, *tb = (const TI*)beta;
+    if (eb)
+        hipLaunchKernelGGL((decode_kernel<TI, TO, DK, DV, false, true>), grid, block, 0, stream,
+                           tq, tk, tv, g, tb, (const TI*)eb, (const TI*)ew, scale, state, (TO*)o);
+    else if (sg)
+        hipLaunchKernelGGL((decode_kernel<TI, TO, DK, DV, true, false>), grid, block, 0, stream,
+                           tq, tk, tv, g, tb, nullptr, nullptr, scale, state, (TO*)o);
     else
-        hipLaunchKernelGGL((decode_kernel<TI, TO, DK, DV, false>), grid, block, 0, stream,
-                           (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
-                           state, (TO*)o);
+        hipLaunchKernelGGL((decode_kernel<TI, TO, DK, DV, false, false>), grid, block, 0, stream,
+                           tq, tk, tv, g, tb, nullptr, nullptr, scale, state, (TO*)o);
     return hipGetLastError();
 }
 
 template <typename TI, typename TO>
 static hipError_t dispatch_decode(bool sg, int Dk, int Dv, const void* q, const void* k,
-                                  const void* v, const float* g, const void* beta, float scale,
-                                  float* state, void* o, int N, int H, hipStream_t s) {
+                                  const void* v, const float* g, const void* beta,
+                                  const void* eb, const void* ew, float scale, float* state,
+                                  void* o, int N, int H, hipStream_t s) {
 #define KDA_DEC(DKV, DVV)                                                                   \
     if (Dk == DKV && Dv == DVV)                                                             \
-        return launch_decode_t<TI, TO, DKV, DVV>(sg, q, k, v, g, beta, scale, state, o, N, H,  \
-                                                 s);
+        return launch_decode_t<TI, TO, DKV, DVV>(sg, q, k, v, g, beta, eb, ew, scale, state, \
+                                                 o, N, H, s);
     KDA_DEC(16, 16) KDA_DEC(16, 32) KDA_DEC(16, 64) KDA_DEC(16, 128)
     KDA_DEC(32, 16) KDA_DEC(32, 32) KDA_DEC(32, 64) KDA_DEC(32, 128)
     KDA_DEC(64, 16) KDA_DEC(64, 32) KDA_DEC(64, 64) KDA_DEC(64, 128)
@@ -163,18 +178,19 @@ static hipError_t dispatch_decode(bool sg, int Dk, int Dv, const void* q, const 
     return hipErrorInvalidValue;
 }
 
+// sg: scalar gate; eb, ew: erase and write gates (non-null together) replacing beta
 hipError_t launch_decode(bool sg, bool bf16_in, bool bf16_out, int Dk, int Dv,
                          const void* q, const void* k, const void* v, const float* g,
-                         const void* beta, float scale, float* state, void* o, int N, int H,
-                         hipStream_t s) {
+                         const void* beta, const void* eb, const void* ew, float scale,
+                         float* state, void* o, int N, int H, hipStream_t s) {
+#define KDA_DEC_ARGS sg, Dk, Dv, q, k, v, g, beta, eb, ew, scale, state, o, N, H, s
     if (bf16_in) {
-        if (bf16_out)
-            return dispatch_decode<bf16, bf16>(sg, Dk, Dv, q, k, v, g, beta, scale, state, o, N, H, s);
-        return dispatch_decode<bf16, float>(sg, Dk, Dv, q, k, v, g, beta, scale, state, o, N, H, s);
+        if (bf16_out) return dispatch_decode<bf16, bf16>(KDA_DEC_ARGS);
+        return dispatch_decode<bf16, float>(KDA_DEC_ARGS);
     }
-    if (bf16_out)
-        return dispatch_decode<float, bf16>(sg, Dk, Dv, q, k, v, g, beta, scale, state, o, N, H, s);
-    return dispatch_decode<float, float>(sg, Dk, Dv, q, k, v, g, beta, scale, state, o, N, H, s);
+    if (bf16_out) return dispatch_decode<float, bf16>(KDA_DEC_ARGS);
+    return dispatch_decode<float, float>(KDA_DEC_ARGS);
+#undef KDA_DEC_ARGS
 }
 
 }  // namespace kda

@@ -295,11 +295,16 @@ __device__ __forceinline__ typename Pol::Frag4 frag4_of(const floatx4& d) {
     return f;
 }
 
-template <typename TI, int DK, int DV, bool SG>
-__global__ __launch_bounds__(256, 2) void prep_kernel(
+// SG: one log-decay per token and head (Gated DeltaNet). EW: Gated DeltaNet-2, where a
+// per-key-channel erase gate eb scales the key on the side that reads the old value (row
+// operands of A_kk and the operand of W) and a per-value-channel write gate ew scales v
+// (U = T (ew v)); beta is not used and T' = T. That variant runs one workgroup per CU.
+template <typename TI, int DK, int DV, bool SG, bool EW>
+__global__ __launch_bounds__(256, EW ? 1 : 2) void prep_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
-    const float* __restrict__ g, const TI* __restrict__ beta, float scale,
-    const int4* __restrict__ tab, int T, int nslots, uint8_t* __restrict__ ws, int H) {
+    const float* __restrict__ g, const TI* __restrict__ beta, const TI* __restrict__ eb,
+    const TI* __restrict__ ew, float scale, const int4* __restrict__ tab, int T, int nslots,
+    uint8_t* __restrict__ ws, int H) {
     using Pol = typename PolOf<TI>::type;
     using Frag = typename Pol::Frag;
     using Frag4 = typename Pol::Frag4;
@@ -368,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                                    sRb + Stg::g_off(wave, I, hg));
                 }
             }
-            if (I == 0 && wave == 0 && lane < L) {
+            if (!EW && I == 0 && wave == 0 && lane < L) {
                 const size_t e = (size_t)(t0 + lane) * H + h;       // beta element index
                 lds_load4(reinterpret_cast<const unsigned*>(beta) + (e >> 1), sBetaRaw);
             }
@@ -433,7 +438,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             if (tid < 64) {
                 const size_t e = (size_t)(t0 + tid) * H + h;
                 const unsigned w = sBetaRaw[tid];
-                sBeta[tid] = tid < L ? __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)) : 0.f;
+                sBeta[tid] = tid < L ? (EW ? 1.f : __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)))
+                                     : 0.f;
             }
         } else {
 #pragma unroll
@@ -460,7 +466,19 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                     Q.zero(I);
                 }
             }
-            if (tid < 64) sBeta[tid] = tid < L ? to_f(beta[(size_t)(t0 + tid) * H + h]) : 0.f;
+            if (tid < 64) sBeta[tid] = tid < L ? (EW ? 1.f : to_f(beta[(size_t)(t0 + tid) * H + h])) : 0.f;
+        }
+        // erase gates of the lane's rows and channels (Gated DeltaNet-2), read from global memory
+        In32<TI> Eb;
+        if constexpr (EW) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int row = 16 * I + m;
+                if (cvalid && row < L)
+                    Eb.load(I, eb + (size_t)(t0 + row) * rowq + (size_t)h * DK + c0);
+                else
+                    Eb.zero(I);
+            }
         }
         // every wave has its inputs (and is past the previous task's reads of sCE): the staging
         // region becomes the A accumulators (the first partial of each block is stored, the
@@ -529,9 +547,18 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
             auto opq = [](float x) { asm volatile("" : "+v"(x)); return x; };
             const int row = 16 * I + m;
             const float bi = sBeta[row];
-            float Gl[8], kk[8], qq[8], pf[8];
+            float Gl[8], kk[8], qq[8], pf[8], kl[8];
             K.get8p(I, kk);
             Q.get8p(I, qq);
+            // key of the reading side (row operands of A_kk): k, or eb * k
+            if constexpr (EW) {
+                Eb.get8p(I, kl);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kl[e] *= kk[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kl[e] = kk[e];
+            }
             ce8(Ip, pf);                                  // cumulative value before block I
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -570,7 +597,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float ea = fast_exp2(Gl[e]);
-                KA.set(e, bi * kk[e] * ea);
+                KA.set(e, bi * kl[e] * ea);
                 QA.set(e, scale * qq[e] * ea);
                 far |= Gl[e] < -120.f;
             }
@@ -592,7 +619,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                         const float x = Gl[e] - row_bcast<7>(Gl[e]);
                         bad |= fabsf(x) > 120.f;
                         const float e1 = fast_exp2(x), e2 = fast_exp2(-x);
-                        KE.set(e, bi * kk[e] * e1);
+                        KE.set(e, bi * kl[e] * e1);
                         QE.set(e, scale * qq[e] * e1);
                         KR.set(e, kk[e] * e2);
                     }
@@ -612,7 +639,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                             const float Gj = __shfl(Gl[e], src);
                             const float kj = __shfl(kk[e], src);
                             const float d = jj <= m ? fast_exp2(Gl[e] - Gj) : 0.f;
-                            skk += kk[e] * kj * d;
+                            skk += kl[e] * kj * d;
                             sqk += scale * qq[e] * kj * d;
                         }
                         skk += __shfl_xor(skk, 16);
@@ -685,6 +712,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                 float k3[8], q3[8], pf3[8];
                 K.get8p(3, k3);
                 Q.get8p(3, q3);
+                if constexpr (EW) {
+                    float e3[8];
+                    Eb.get8p(3, e3);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) k3[e] *= e3[e];
+                }
                 ce8(2, pf3);
                 const float b3 = sBeta[48 + m];
                 Frag KA3, QA3;
@@ -713,14 +746,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
         // ---- value slice of this wave (for U), loaded now so it lands during the inverse ----
         const int vc0 = 32 * wave + 8 * grp;
         const bool vvalid = wave < NVS && vc0 < DV;
-        In32<TI> V;
+        In32<TI> V, Wr;
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             const int row = 16 * I + m;
-            if (vvalid && row < L)
+            if (vvalid && row < L) {
                 V.load(I, v + (size_t)(t0 + row) * rowv + (size_t)h * DV + vc0);
-            else
+                if constexpr (EW) Wr.load(I, ew + (size_t)(t0 + row) * rowv + (size_t)h * DV + vc0);
+            } else {
                 V.zero(I);
+                if constexpr (EW) Wr.zero(I);
+            }
         }
         // A_qk fragment tiles of token tile tw = wave (upper blocks zero)
 #pragma unroll
@@ -829,6 +865,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
                 if (stage_next) stage(t0n, Ln, hn, J);
                 float kJ[8], ceJ[8];
                 K.get8(J, kJ);
+                if constexpr (EW) {
+                    float eJ[8];
+                    Eb.get8(J, eJ);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kJ[e] *= eJ[e];
+                }
                 ce8(J > 0 ? J - 1 : 0, ceJ);
                 Frag kg;
 #pragma unroll
@@ -863,12 +905,28 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(
 #pragma unroll
                     for (int J = 0; J < 4; ++J) {
                         Frag vb;
-                        V.frag(J, vb);
                         floatx4 t = {0.f, 0.f, 0.f, 0.f};
-                        Pol::mma_copy(t, vb, Eid[hh]);        // lane (value n, grp): tokens 4 grp + r
-                        const Frag4 b = frag4_of<Pol>(t);
+                        if constexpr (EW) {
+                            // ew v (a product of two inputs: exact in fp32, not in one bf16)
+                            float vv[8], wv[8];
+                            V.get8(J, vv);
+                            Wr.get8(J, wv);
 #pragma unroll
-                        for (int I = J; I < 4; ++I) Pol::mma16_exact(accU[I], sTp[tri_tile(I, J)][lane], b);
+                            for (int e = 0; e < 8; ++e) vb.set(e, vv[e] * wv[e]);
+                            Pol::mma_exact(t, vb, Eid[hh]);
+                        } else {
+                            V.frag(J, vb);
+                            Pol::mma_copy(t, vb, Eid[hh]);    // lane (value n, grp): tokens 4 grp + r
+                        }
+                        const Frag4 b = frag4_of<Pol>(t);
+                        // v is exact in the input type, ew v is not: it needs the full product
+#pragma unroll
+                        for (int I = J; I < 4; ++I) {
+                            if constexpr (EW)
+                                Pol::mma16(accU[I], sTp[tri_tile(I, J)][lane], b);
+                            else
+                                Pol::mma16_exact(accU[I], sTp[tri_tile(I, J)][lane], b);
+                        }
                     }
 #pragma unroll
                     for (int I = 0; I < 4; ++I)
@@ -1258,8 +1316,9 @@ static hipError_t current_cu_count(int& n) {
 }
 
 template <typename TI, typename TO, int DK, int DV>
-static hipError_t launch_prefill_t(bool sg, const void* q, const void* k, const void* v, const float* g,
-                                   const void* beta, float scale, const float* h0, float* ht,
+static hipError_t launch_prefill_t(bool sg, const void* q, const void* k, const void* v,
+                                   const float* g, const void* beta, const void* eb,
+                                   const void* ew, float scale, const float* h0, float* ht,
                                    void* o, const int32_t* cu, int T, const void* tab,
                                    const int32_t* seq_off, uint8_t* blocks, int N, int H,
                                    int max_slots, hipStream_t s) {
@@ -1267,14 +1326,22 @@ static hipError_t launch_prefill_t(bool sg, const void* q, const void* k, const 
     hipError_t ec = current_cu_count(cu_count);
     if (ec != hipSuccess) return ec;
     const long long ntasks = (long long)max_slots * H;
-    const long long grid = ntasks < 2LL * cu_count ? ntasks : 2LL * cu_count;
-    if (sg)
-        hipLaunchKernelGGL((prep_kernel<TI, DK, DV, true>), dim3((unsigned)grid), dim3(256), 0, s,
-                           (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
+    // two resident workgroups per CU; one for the erase/write-gate variant, whose extra
+    // operands need more than half of the register file
+    const long long per_cu = eb ? 1 : 2;
+    const long long grid = ntasks < per_cu * cu_count ? ntasks : per_cu * cu_count;
+    const TI *tq = (const TI*)q, *tk = (const TI*)k, *tv = (const TI*)v, *tb = (const TI*)beta;
+    if (eb)
+        hipLaunchKernelGGL((prep_kernel<TI, DK, DV, false, true>), dim3((unsigned)grid), dim3(256),
+                           0, s, tq, tk, tv, g, tb, (const TI*)eb, (const TI*)ew, scale,
                            (const int4*)tab, T, max_slots, blocks, H);
+    else if (sg)
+        hipLaunchKernelGGL((prep_kernel<TI, DK, DV, true, false>), dim3((unsigned)grid), dim3(256),
+                           0, s, tq, tk, tv, g, tb, nullptr, nullptr, scale, (const int4*)tab, T,
+                           max_slots, blocks, H);
     else
-        hipLaunchKernelGGL((prep_kernel<TI, DK, DV, false>), dim3((unsigned)grid), dim3(256), 0, s,
-                           (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
+        hipLaunchKernelGGL((prep_kernel<TI, DK, DV, false, false>), dim3((unsigned)grid),
+                           dim3(256), 0, s, tq, tk, tv, g, tb, nullptr, nullptr, scale,
                            (const int4*)tab, T, max_slots, blocks, H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1288,15 +1355,17 @@ static hipError_t launch_prefill_t(bool sg, const void* q, const void* k, const 
 }
 
 template <typename TI, typename TO>
-static hipError_t dispatch_prefill(bool sg, int Dk, int Dv, const void* q, const void* k, const void* v,
-                                   const float* g, const void* beta, float scale,
-                                   const float* h0, float* ht, void* o, const int32_t* cu, int T,
-                                   const void* tab, const int32_t* seq_off, uint8_t* blocks,
-                                   int N, int H, int max_slots, hipStream_t s) {
+static hipError_t dispatch_prefill(bool sg, int Dk, int Dv, const void* q, const void* k,
+                                   const void* v, const float* g, const void* beta,
+                                   const void* eb, const void* ew, float scale, const float* h0,
+                                   float* ht, void* o, const int32_t* cu, int T, const void* tab,
+                                   const int32_t* seq_off, uint8_t* blocks, int N, int H,
+                                   int max_slots, hipStream_t s) {
 #define KDA_PF(DKV, DVV)                                                                    \
     if (Dk == DKV && Dv == DVV)                                                             \
-        return launch_prefill_t<TI, TO, DKV, DVV>(sg, q, k, v, g, beta, scale, h0, ht, o, cu, T,\
-                                                  tab, seq_off, blocks, N, H, max_slots, s);
+        return launch_prefill_t<TI, TO, DKV, DVV>(sg, q, k, v, g, beta, eb, ew, scale, h0, ht, \
+                                                  o, cu, T, tab, seq_off, blocks, N, H,     \
+                                                  max_slots, s);
     KDA_PF(16, 16) KDA_PF(16, 32) KDA_PF(16, 64) KDA_PF(16, 128)
     KDA_PF(32, 16) KDA_PF(32, 32) KDA_PF(32, 64) KDA_PF(32, 128)
     KDA_PF(64, 16) KDA_PF(64, 32) KDA_PF(64, 64) KDA_PF(64, 128)
@@ -1305,23 +1374,22 @@ static hipError_t dispatch_prefill(bool sg, int Dk, int Dv, const void* q, const
     return hipErrorInvalidValue;
 }
 
+// sg: scalar gate; eb, ew: erase and write gates (non-null together) replacing beta
 hipError_t launch_prefill(bool sg, bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
                           const void* k, const void* v, const float* g, const void* beta,
-                          float scale, const float* h0, float* ht, void* o, const int32_t* cu,
-                          int T, const void* tab, const int32_t* seq_off, uint8_t* blocks, int N,
-                          int H, int max_slots, hipStream_t s) {
+                          const void* eb, const void* ew, float scale, const float* h0,
+                          float* ht, void* o, const int32_t* cu, int T, const void* tab,
+                          const int32_t* seq_off, uint8_t* blocks, int N, int H, int max_slots,
+                          hipStream_t s) {
+#define KDA_PF_ARGS sg, Dk, Dv, q, k, v, g, beta, eb, ew, scale, h0, ht, o, cu, T, tab, seq_off, \
+                    blocks, N, H, max_slots, s
     if (bf16_in) {
-        if (bf16_out)
-            return dispatch_prefill<bf16, bf16>(sg, Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T,
-                                                tab, seq_off, blocks, N, H, max_slots, s);
-        return dispatch_prefill<bf16, float>(sg, Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T,
-                                             tab, seq_off, blocks, N, H, max_slots, s);
+        if (bf16_out) return dispatch_prefill<bf16, bf16>(KDA_PF_ARGS);
+        return dispatch_prefill<bf16, float>(KDA_PF_ARGS);
     }
-    if (bf16_out)
-        return dispatch_prefill<float, bf16>(sg, Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T,
-                                             tab, seq_off, blocks, N, H, max_slots, s);
-    return dispatch_prefill<float, float>(sg, Dk, Dv, q, k, v, g, beta, scale, h0, ht, o, cu, T, tab,
-                                          seq_off, blocks, N, H, max_slots, s);
+    if (bf16_out) return dispatch_prefill<float, bf16>(KDA_PF_ARGS);
+    return dispatch_prefill<float, float>(KDA_PF_ARGS);
+#undef KDA_PF_ARGS
 }
 
 }  // namespace kda

@@ -157,6 +157,38 @@ kda_status kda_gdn_decode_step(const void* q, const void* k, const void* v, cons
                                int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
                                void* stream);
 
+/* Gated DeltaNet-2: KDA's per-channel decay with beta split into an erase
+ * gate b (one value per key channel) and a write gate w (one per value
+ * channel), as on "From Fast Weight Programmers to KDA"
+ * (jonahsamost.bearblog.dev), section "Gated DeltaNet-2" (written there for
+ * the transposed state). Steps (2) and (3) become
+ *
+ *   v^  = S~^T (b_t * k_t)          read the old value through the gated key
+ *   e   = w_t * v_t - v^            gated target minus the old value
+ *
+ * and the write S = S~ + k_t e^T stays at the original key. b = beta and
+ * w = beta on every channel give kda_fwd_chunked.
+ *
+ *  b      [B, T, H, Dk]  dtype         erase gate (replaces beta)
+ *  w      [B, T, H, Dv]  dtype         write gate
+ *
+ * Every other argument (g per key channel as for KDA), the workspace (sized
+ * by kda_fwd_chunked_workspace_size), the aliasing rules and the errors are
+ * those of kda_fwd_chunked; a NULL b or w is KDA_ERROR_INVALID_VALUE. */
+kda_status kda_gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* g,
+                                const void* b, const void* w, float scale, const float* h0,
+                                float* ht, void* o, const int32_t* cu_seqlens, int num_seqs,
+                                int B, int T, int H, int Dk, int Dv, kda_dtype dtype,
+                                kda_dtype o_dtype, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* One Gated DeltaNet-2 decode step: as kda_decode_step with b [N, H, Dk] and
+ * w [N, H, Dv] (dtype) in place of beta. */
+kda_status kda_gdn2_decode_step(const void* q, const void* k, const void* v, const float* g,
+                                const void* b, const void* w, float scale, float* state, void* o,
+                                int N, int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ def lib():
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
