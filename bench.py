@@ -7,7 +7,8 @@ over the decode workload (256 requests x 64 heads, 128x128 fp32 states
 updated in place). Inputs are synthetic (seeded generators) and resident in
 HBM before timing starts. Prints one JSON line. Besides the step figures it
 reports the decode step repeated back to back (the sustained rate) and the
-same step for Gated DeltaNet (one scalar gate per token and head).
+same step for Gated DeltaNet (one scalar gate per token and head) and Gated
+DeltaNet-2 (erase and write gates per channel in place of beta).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
   python bench.py --copy-calibration          # 1 GiB device copy (counter calibration)
@@ -116,10 +117,10 @@ def _pmc_per_kernel(path, counter):
 
 
 def _short(name):
-    """Kernel of the KDA path a counter row belongs to; the scalar-gate (Gated DeltaNet)
-    instantiations, whose last template argument is true ("Lb1EE" in a mangled name), are
-    not counted."""
-    if re.search(r"\btrue\s*>|Lb1EE", name):
+    """Kernel of the KDA path a counter row belongs to; the Gated DeltaNet and Gated
+    DeltaNet-2 instantiations (a true gate flag among the template arguments, "Lb1E" in a
+    mangled name) are not counted."""
+    if re.search(r"\btrue\b|Lb1E", name):
         return None
     for key in ("prep_kernel", "state_kernel", "chunk_map_kernel", "decode_kernel"):
         if key in name:
@@ -354,6 +355,34 @@ def main():
     gdn_pf_bytes = pf_bytes - B * T * H * Dk * 4 + B * T * H * 4       # g is one float per token-head
     gdn_dc_bytes = dc_bytes - wd.N * wd.H * wd.Dk * 4 + wd.N * wd.H * 4
 
+    # Gated DeltaNet-2 (erase gate per key channel, write gate per value channel, bf16, in
+    # place of beta) on the same q, k, v, g and state, timed the same way
+    eb2, ew2 = (t.view(B, T, H, -1).to(dev) for t in I.erase_write_gates(wp, list(range(H)), B * T))
+    ebd, ewd = (t.to(dev) for t in I.erase_write_gates(wd, list(range(wd.H)), wd.N))
+
+    def gdn2_prefill():
+        kda.gdn2_fwd_chunked(q, k, v, g, eb2, ew2, scale=1.0, workspace=ws, out=o, final_state=ht)
+
+    def gdn2_decode():
+        kda.gdn2_decode_step(dq, dk, dv, dg, ebd, ewd, state, scale=1.0, out=od)
+
+    for _ in range(args.warmup):
+        gdn2_prefill()
+        gdn2_decode()
+    torch.cuda.synchronize()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        gdn2_prefill()
+        e1.record(stream)
+        gdn2_decode()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    t2p = np.array([a.elapsed_time(bb) for a, bb, _ in ev]) * 1e-3
+    t2d = np.array([bb.elapsed_time(c) for _, bb, c in ev]) * 1e-3
+    del eb2, ew2
+    gdn2_pf_bytes = pf_bytes - B * T * H * 2 + B * T * H * (Dk + Dv) * 2   # b, w instead of beta
+    gdn2_dc_bytes = dc_bytes - wd.N * wd.H * 2 + wd.N * wd.H * (wd.Dk + wd.Dv) * 2
+
     # context for the decode figure: torch's device-to-device copy of 1 GiB (read + write)
     xc = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     yc = torch.empty_like(xc)
@@ -407,6 +436,13 @@ def main():
                            "decode_hbm_gbs": gdn_dc_bytes / float(tgd.mean()) / 1e9,
                            "decode_frac_of_peak": gdn_dc_bytes / float(tgd.mean()) / 1e9
                            / HBM_PEAK_GBS},
+        "gated_deltanet_2": {"prefill_ms": float(t2p.mean()) * 1e3,
+                             "prefill_tokens_per_s": tokens / float(t2p.mean()),
+                             "prefill_hbm_gbs": gdn2_pf_bytes / float(t2p.mean()) / 1e9,
+                             "decode_ms": float(t2d.mean()) * 1e3,
+                             "decode_hbm_gbs": gdn2_dc_bytes / float(t2d.mean()) / 1e9,
+                             "decode_frac_of_peak": gdn2_dc_bytes / float(t2d.mean()) / 1e9
+                             / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": pf_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": pf_gbs / HBM_PEAK_GBS, "traffic": traffic_pf,
                      "kernel": "kda_fwd_chunked call (prep_kernel + state_kernel; packed "

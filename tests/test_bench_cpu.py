@@ -72,11 +72,15 @@ def test_traffic_summary_calibration(tmp_path):
               "Counter_Value": 3000.0} for d in (1, 2)]
     write += [{"Dispatch_Id": 3, "Kernel_Name": "kda::state_kernel<...>",
                "Counter_Name": "WRITE_SIZE", "Counter_Value": 100.0}]
-    # a scalar-gate (Gated DeltaNet) prep dispatch is not part of the KDA figures
+    # Gated DeltaNet and Gated DeltaNet-2 dispatches are not part of the KDA figures
     fetch += [{"Dispatch_Id": 4, "Kernel_Name": "void kda::prep_kernel<__hip_bfloat16, 128, 128, true>(...)",
                "Counter_Name": "FETCH_SIZE", "Counter_Value": 9.0e6},
-              {"Dispatch_Id": 5, "Kernel_Name": "_ZN3kda11prep_kernelIDF16bLi128ELi128ELb1EEEvPKT_",
-               "Counter_Name": "FETCH_SIZE", "Counter_Value": 7.0e6}]
+              {"Dispatch_Id": 5, "Kernel_Name": "_ZN3kda11prep_kernelIDF16bLi128ELi128ELb1ELb0EEEvPKT_",
+               "Counter_Name": "FETCH_SIZE", "Counter_Value": 7.0e6},
+              {"Dispatch_Id": 6, "Kernel_Name": "_ZN3kda11prep_kernelIDF16bLi128ELi128ELb0ELb1EEEvPKT_",
+               "Counter_Name": "FETCH_SIZE", "Counter_Value": 5.0e6},
+              {"Dispatch_Id": 7, "Kernel_Name": "void kda::decode_kernel<__bf16, float, 128, 128, false, true>(...)",
+               "Counter_Name": "FETCH_SIZE", "Counter_Value": 3.0e6}]
     _write_csv(tmp_path / "f.csv", fetch)
     _write_csv(tmp_path / "w.csv", write)
     out_file = str(tmp_path / "traffic.json")
@@ -93,6 +97,7 @@ def test_traffic_summary_calibration(tmp_path):
     assert out["prefill_call_bytes"] == pytest.approx(
         prep["fetch_bytes"] + prep["write_bytes"] + state["fetch_bytes"] + state["write_bytes"])
     assert out["decode_bytes"] is None
+    assert set(out["per_kernel"]) == {"prep_kernel", "state_kernel"}
     # figures are used only while the kernel sources hash to the recorded value
     assert bench.load_traffic(out_file)[0] == pytest.approx(out["prefill_call_bytes"])
     d = json.load(open(out_file))
