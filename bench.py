@@ -79,7 +79,8 @@ def kernels_source_hash():
     counter figures are tied to the code they were taken on)."""
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "gated_delta_rule_channel_amd")
-    files = sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]
+    files = sorted(f for f in glob.glob(os.path.join(pkg, "csrc", "*"))
+                   if f.endswith((".hip", ".h", ".cpp"))) + [os.path.join(pkg, "build.py")]
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "r", encoding="utf-8", errors="replace") as fh:

@@ -15,6 +15,10 @@ the same calls under the names gdn_fwd_chunked and gdn_decode_step; Gated
 DeltaNet-2 (erase gate b per key channel and write gate w per value channel in
 place of beta) under gdn2_fwd_chunked(q, k, v, g, b, w, ...) and
 gdn2_decode_step(q, k, v, g, b, w, state, ...).
+
+Serving state: decode_multi(q, k, v, g, beta, pool, slots=None, snapshots=None)
+runs T tokens per request against a slot-indexed state pool; state_copy(dst,
+dst_slots, src, src_slots) copies whole states (fork, rollback).
 """
 from __future__ import annotations
 
@@ -35,7 +39,8 @@ KDA_DTYPE_BF16 = 1
 
 EXPORTED = ("kda_status_string", "kda_fwd_chunked_workspace_size", "kda_fwd_chunked",
             "kda_decode_step", "kda_gdn_fwd_chunked", "kda_gdn_decode_step",
-            "kda_gdn2_fwd_chunked", "kda_gdn2_decode_step")
+            "kda_gdn2_fwd_chunked", "kda_gdn2_decode_step", "kda_decode_multi",
+            "kda_state_copy")
 
 
 class KDAError(RuntimeError):
@@ -74,6 +79,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_gdn2_fwd_chunked.restype = i
     lib.kda_gdn2_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, f, vp, vp, i, i, i, i, i, i, vp]
     lib.kda_gdn2_decode_step.restype = i
+    lib.kda_decode_multi.argtypes = [vp, vp, vp, vp, vp, f, vp, i, vp, vp, vp, i, i, i, i, i, i,
+                                     i, vp]
+    lib.kda_decode_multi.restype = i
+    lib.kda_state_copy.argtypes = [vp, i, vp, vp, i, vp, i, i, i, i, vp]
+    lib.kda_state_copy.restype = i
     if path is None:
         _lib_handle = lib
     return lib
@@ -271,3 +281,69 @@ def _decode_step(scalar_gate, q, k, v, g, beta, state, scale, out, out_dtype, ga
     if st != KDA_SUCCESS:
         raise KDAError(st, name)
     return o
+
+
+def decode_multi(q, k, v, g, beta, pool, slots=None, snapshots=None, scale: float = 1.0,
+                 out=None, out_dtype=None):
+    """T decode steps per request against a state pool.
+
+    q, k, g: [N,T,H,Dk]; v: [N,T,H,Dv]; beta: [N,T,H]; pool: [P,H,Dk,Dv] float32, slot
+    slots[n] (int32 [N] on the device; None = slot n) updated in place to the state after the
+    T tokens; snapshots: [N,T,H,Dk,Dv] float32 or None, receives the state after every
+    token. Returns o [N,T,H,Dv] (float32 by default)."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if q.dim() != 4 or v.dim() != 4 or pool.dim() != 4:
+        raise ValueError("q, k, g must be [N,T,H,Dk], v [N,T,H,Dv], pool [P,H,Dk,Dv]")
+    N, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    P = pool.shape[0]
+    code = _dtype_code(q)
+    _check_same_dtype(q, k=k, v=v, beta=beta)
+    _check_shape("k", k, (N, T, H, Dk))
+    _check_shape("g", g, (N, T, H, Dk))
+    _check_shape("v", v, (N, T, H, Dv))
+    _check_shape("beta", beta, (N, T, H))
+    _check_shape("pool", pool, (P, H, Dk, Dv))
+    _check_shape("slots", slots, (N,))
+    _check_shape("snapshots", snapshots, (N, T, H, Dk, Dv))
+    _check_shape("out", out, (N, T, H, Dv))
+    if g.dtype != torch.float32 or pool.dtype != torch.float32:
+        raise TypeError("g and pool must be float32")
+    if snapshots is not None and snapshots.dtype != torch.float32:
+        raise TypeError("snapshots must be float32")
+    if slots is not None and slots.dtype != torch.int32:
+        raise TypeError("slots must be int32")
+    if slots is None and P < N:
+        raise ValueError("without slots the pool needs one state per request")
+    _check_gpu(q, k, v, g, beta, pool, slots, snapshots, out)
+    o = out if out is not None else torch.empty((N, T, H, Dv), dtype=out_dtype, device=q.device)
+    st = load_library().kda_decode_multi(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(pool), int(P),
+        _ptr(slots), _ptr(snapshots), _ptr(o), int(N), int(T), int(H), int(Dk), int(Dv), code,
+        _dtype_code(o), _stream(q.device))
+    if st != KDA_SUCCESS:
+        raise KDAError(st, "kda_decode_multi")
+    return o
+
+
+def state_copy(dst, dst_slots, src, src_slots):
+    """dst[dst_slots[i]] = src[src_slots[i]] for whole states. dst: [Pd,H,Dk,Dv] float32;
+    src: [Ps,H,Dk,Dv] float32 (a snapshot array may be passed as [N*T,H,Dk,Dv]); slots:
+    int32 [n] on the device."""
+    import torch
+    if dst.dim() != 4 or src.dim() != 4 or tuple(dst.shape[1:]) != tuple(src.shape[1:]):
+        raise ValueError("dst and src must be [P,H,Dk,Dv] with the same H, Dk, Dv")
+    if dst.dtype != torch.float32 or src.dtype != torch.float32:
+        raise TypeError("states must be float32")
+    if dst_slots.dtype != torch.int32 or src_slots.dtype != torch.int32:
+        raise TypeError("slots must be int32")
+    if dst_slots.dim() != 1 or tuple(src_slots.shape) != tuple(dst_slots.shape):
+        raise ValueError("dst_slots and src_slots must be 1-D and of one length")
+    _check_gpu(dst, src, dst_slots, src_slots)
+    _, H, Dk, Dv = dst.shape
+    st = load_library().kda_state_copy(
+        _ptr(dst), int(dst.shape[0]), _ptr(dst_slots), _ptr(src), int(src.shape[0]),
+        _ptr(src_slots), int(dst_slots.numel()), int(H), int(Dk), int(Dv), _stream(dst.device))
+    if st != KDA_SUCCESS:
+        raise KDAError(st, "kda_state_copy")

@@ -20,6 +20,13 @@ hipError_t launch_prefill(bool sg, bool bf16_in, bool bf16_out, int Dk, int Dv, 
                           const int32_t* seq_off, uint8_t* blocks, int N, int H, int max_slots,
                           hipStream_t s);
 size_t prefill_block_bytes(int Dk, int Dv, bool bf16_in);
+hipError_t launch_decode_multi(bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
+                               const void* k, const void* v, const float* g, const void* beta,
+                               float scale, float* pool, const int32_t* slots, int num_slots,
+                               float* snapshots, void* o, int N, int T, int H, hipStream_t s);
+hipError_t launch_state_copy(float* dst, const int32_t* dst_slots, int dst_count,
+                             const float* src, const int32_t* src_slots, int src_count,
+                             int pairs, long long state_floats, hipStream_t s);
 }  // namespace kda
 
 namespace {
@@ -192,6 +199,47 @@ kda_status kda_gdn2_decode_step(const void* q, const void* k, const void* v, con
     if (!b || !w) return KDA_ERROR_INVALID_VALUE;
     return decode_step(false, q, k, v, g, nullptr, b, w, scale, state, o, N, H, Dk, Dv, dtype,
                        o_dtype, stream);
+}
+
+kda_status kda_decode_multi(const void* q, const void* k, const void* v, const float* g,
+                            const void* beta, float scale, float* pool, int num_slots,
+                            const int32_t* slots, float* snapshots, void* o, int N, int T,
+                            int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
+                            void* stream) {
+    if (!q || !k || !v || !g || !beta || !pool || !o) return KDA_ERROR_INVALID_VALUE;
+    if (N <= 0 || T <= 0 || H <= 0 || num_slots <= 0) return KDA_ERROR_INVALID_VALUE;
+    if (!slots && num_slots < N) return KDA_ERROR_INVALID_VALUE;
+    if (!head_ok(Dk) || !head_ok(Dv)) return KDA_ERROR_INVALID_VALUE;
+    if (!dtype_ok(dtype) || !dtype_ok(o_dtype)) return KDA_ERROR_INVALID_VALUE;
+    if ((long long)N * H > (1LL << 31) - 1 || (long long)N * T > (1LL << 31) - 1)
+        return KDA_ERROR_NOT_SUPPORTED;
+    const void* ptrs[] = {q, k, v, g, beta, pool, snapshots, o};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned(ptr, 16)) return KDA_ERROR_INVALID_VALUE;
+    if (slots && !aligned(slots, 4)) return KDA_ERROR_INVALID_VALUE;
+    if (kda::launch_decode_multi(dtype == KDA_DTYPE_BF16, o_dtype == KDA_DTYPE_BF16, Dk, Dv, q, k,
+                                 v, g, beta, scale, pool, slots, num_slots, snapshots, o, N, T,
+                                 H, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return KDA_ERROR_LAUNCH;
+    return KDA_SUCCESS;
+}
+
+kda_status kda_state_copy(float* dst, int dst_count, const int32_t* dst_slots, const float* src,
+                          int src_count, const int32_t* src_slots, int pairs, int H, int Dk,
+                          int Dv, void* stream) {
+    if (pairs == 0) return KDA_SUCCESS;
+    if (!dst || !dst_slots || !src || !src_slots) return KDA_ERROR_INVALID_VALUE;
+    if (pairs < 0 || dst_count <= 0 || src_count <= 0 || H <= 0) return KDA_ERROR_INVALID_VALUE;
+    if (!head_ok(Dk) || !head_ok(Dv)) return KDA_ERROR_INVALID_VALUE;
+    if (pairs > 65535) return KDA_ERROR_NOT_SUPPORTED;
+    if (!aligned(dst, 16) || !aligned(src, 16) || !aligned(dst_slots, 4) ||
+        !aligned(src_slots, 4))
+        return KDA_ERROR_INVALID_VALUE;
+    if (kda::launch_state_copy(dst, dst_slots, dst_count, src, src_slots, src_count, pairs,
+                               (long long)H * Dk * Dv,
+                               reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return KDA_ERROR_LAUNCH;
+    return KDA_SUCCESS;
 }
 
 }  // extern "C"

@@ -189,6 +189,54 @@ kda_status kda_gdn2_decode_step(const void* q, const void* k, const void* v, con
                                 int N, int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
                                 void* stream);
 
+/* Serving state. A request's state is request-scoped serving state, kept
+ * like a KV-cache slot: carried across turns, and copied or restored when a
+ * request forks or a speculative draft is rolled back ("Module 03 - KDA I:
+ * The Delta-Rule Recurrence", jared-hpc.com, section 5). */
+
+/* T consecutive decode steps per request against a pool of states.
+ *
+ *  q, k, g    [N, T, H, Dk]  (g float32)     tokens t = 0 .. T-1 of request n
+ *  v          [N, T, H, Dv]
+ *  beta       [N, T, H]
+ *  pool       [num_slots, H, Dk, Dv] float32; request n uses state slot
+ *             slots[n] (device int32[N]), or slot n when slots is NULL
+ *             (then num_slots >= N). On return the slot holds the state after
+ *             the request's T tokens.
+ *  snapshots  [N, T, H, Dk, Dv] float32 or NULL: the state after each token,
+ *             so that the state after any accepted prefix of the T tokens can
+ *             be restored with kda_state_copy (speculative verification).
+ *  o          [N, T, H, Dv]  o_dtype
+ *
+ * Each step is the recurrent step of kda_decode_step, in token order; the
+ * state stays in registers between steps, so it is read and written once per
+ * call (plus the snapshots). Requests must use distinct slots. A slot outside
+ * [0, num_slots) is skipped on the device: its request's o, snapshots and
+ * state are not touched.
+ * Errors (nothing is enqueued): KDA_ERROR_INVALID_VALUE for NULL q, k, v, g,
+ * beta, pool or o, non-positive sizes, slots NULL with num_slots < N,
+ * misalignment or an unsupported head size; KDA_ERROR_LAUNCH if the launch
+ * fails. */
+kda_status kda_decode_multi(const void* q, const void* k, const void* v, const float* g,
+                            const void* beta, float scale, float* pool, int num_slots,
+                            const int32_t* slots, float* snapshots, void* o, int N, int T,
+                            int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
+                            void* stream);
+
+/* Copy whole states: dst[dst_slots[i]] = src[src_slots[i]] for i < pairs,
+ * where dst holds dst_count states and src holds src_count states, each
+ * [H, Dk, Dv] float32 (a snapshot array [N, T, H, Dk, Dv] is N * T states,
+ * state n * T + t). Forks a request (pool to pool) or restores a snapshot
+ * (snapshots to pool). dst_slots must be distinct and no destination state may
+ * be the source of another pair; a slot outside its array's range skips that
+ * pair on the device. pairs == 0 is a no-op.
+ * Errors: KDA_ERROR_INVALID_VALUE for NULL pointers, negative sizes,
+ * misalignment or an unsupported head size; KDA_ERROR_NOT_SUPPORTED for more
+ * than 65535 pairs; KDA_ERROR_LAUNCH if the launch fails. */
+kda_status kda_state_copy(float* dst, int dst_count, const int32_t* dst_slots, const float* src,
+                          int src_count, const int32_t* src_slots, int pairs, int H, int Dk,
+                          int Dv, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -186,3 +186,51 @@ def test_gdn_entry_points_validate_like_kda(lib):
     assert d(g=None) == E
     assert d(N=0) == E
     assert d(g=FAKE + 8) == E
+
+
+def test_serving_entry_points_validate(lib):
+    """Host checks of the serving-state calls (nothing reaches the device)."""
+    E = kda.KDA_ERROR_INVALID_VALUE
+    m = lambda **o: lib.kda_decode_multi(
+        o.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, 1.0, o.get("pool", FAKE), o.get("P", 4),
+        o.get("slots", None), o.get("snap", None), FAKE, o.get("N", 4), o.get("T", 2), 2,
+        o.get("Dk", 64), 64, 1, 0, None)
+    assert m(q=None) == E
+    assert m(pool=None) == E
+    assert m(T=0) == E
+    assert m(P=3) == E                        # no slot table: one state per request needed
+    assert m(Dk=40) == E
+    assert m(snap=FAKE + 8) == E              # misaligned snapshots
+    assert m(slots=FAKE + 2, P=8) == E        # misaligned slot table
+    c = lambda **o: lib.kda_state_copy(o.get("dst", FAKE), 4, o.get("ds", FAKE), FAKE, 4, FAKE,
+                                       o.get("pairs", 2), 2, 64, o.get("Dv", 64), None)
+    assert c(pairs=0, dst=None) == kda.KDA_SUCCESS      # nothing to copy
+    assert c(dst=None) == E
+    assert c(pairs=-1) == E
+    assert c(Dv=24) == E
+    assert c(ds=FAKE + 2) == E
+    assert c(pairs=70000) == kda.KDA_ERROR_NOT_SUPPORTED
+
+
+def test_binding_serving_shapes():
+    import torch
+    kda_ = pytest.importorskip("gated_delta_rule_channel_amd")
+    N, T, H, D = 2, 3, 2, 16
+    q = torch.zeros(N, T, H, D)
+    beta = torch.zeros(N, T, H)
+    pool = torch.zeros(4, H, D, D)
+    with pytest.raises(ValueError, match="beta has shape"):
+        kda_.decode_multi(q, q, q, q, torch.zeros(N, T), pool)
+    with pytest.raises(ValueError, match="pool has shape"):
+        kda_.decode_multi(q, q, q, q, beta, torch.zeros(4, H, D, 2 * D))
+    with pytest.raises(TypeError, match="slots must be int32"):
+        kda_.decode_multi(q, q, q, q, beta, pool, slots=torch.zeros(N, dtype=torch.int64))
+    with pytest.raises(ValueError, match="one state per request"):
+        kda_.decode_multi(q, q, q, q, beta, torch.zeros(1, H, D, D))
+    with pytest.raises(ValueError, match="contiguous GPU"):
+        kda_.decode_multi(q, q, q, q, beta, pool)
+    s = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="same H, Dk, Dv"):
+        kda_.state_copy(pool, s, torch.zeros(4, H, D, 2 * D), s)
+    with pytest.raises(ValueError, match="one length"):
+        kda_.state_copy(pool, s, pool, torch.zeros(2, dtype=torch.int32))
