@@ -8,7 +8,9 @@ updated in place). Inputs are synthetic (seeded generators) and resident in
 HBM before timing starts. Prints one JSON line. Besides the step figures it
 reports the decode step repeated back to back (the sustained rate) and the
 same step for Gated DeltaNet (one scalar gate per token and head) and Gated
-DeltaNet-2 (erase and write gates per channel in place of beta).
+DeltaNet-2 (erase and write gates per channel in place of beta), and the
+serving-state operations (4-token verification against a slot-indexed state
+pool, with and without per-token snapshots, and a 256-state fork copy).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
   python bench.py --copy-calibration          # 1 GiB device copy (counter calibration)
@@ -384,6 +386,45 @@ def main():
     gdn2_pf_bytes = pf_bytes - B * T * H * 2 + B * T * H * (Dk + Dv) * 2   # b, w instead of beta
     gdn2_dc_bytes = dc_bytes - wd.N * wd.H * 2 + wd.N * wd.H * (wd.Dk + wd.Dv) * 2
 
+    # serving state: 4 drafted tokens per request verified against a pool of 512 slots (the
+    # 256 requests at permuted slots), without and with per-token snapshots, and a fork of
+    # 256 states to free slots
+    TV, PS = 4, 2 * wd.N
+    xs = I.decode_inputs(wd, N=wd.N * TV, with_state=False)
+    mv = [t.view(wd.N, TV, *t.shape[1:]).to(dev) for t in (xs.q, xs.k, xs.v, xs.g, xs.beta)]
+    del xs
+    spool = torch.empty((PS, wd.H, wd.Dk, wd.Dv), dtype=torch.float32, device=dev)
+    spool[:wd.N].copy_(state)
+    spool[wd.N:].copy_(state)
+    perm = np.random.default_rng(5).permutation(PS).astype(np.int32)
+    sslots = torch.from_numpy(perm[:wd.N]).to(dev)
+    fork_src = torch.from_numpy(perm[:wd.N]).to(dev)
+    fork_dst = torch.from_numpy(perm[wd.N:]).to(dev)
+    snaps = torch.empty((wd.N, TV, wd.H, wd.Dk, wd.Dv), dtype=torch.float32, device=dev)
+    omv = torch.empty((wd.N, TV, wd.H, wd.Dv), dtype=torch.float32, device=dev)
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(n):
+            fn()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) * 1e-3 / n
+
+    n_serv = max(5, args.steps // 2)
+    t_mv = timed(lambda: kda.decode_multi(*mv, spool, slots=sslots, scale=1.0, out=omv), n_serv)
+    t_mvs = timed(lambda: kda.decode_multi(*mv, spool, slots=sslots, snapshots=snaps, scale=1.0,
+                                           out=omv), n_serv)
+    t_fork = timed(lambda: kda.state_copy(spool, fork_dst, spool, fork_src), n_serv)
+    st_bytes = wd.N * wd.H * wd.Dk * wd.Dv * 4
+    tok_bytes = TV * (decode_bytes(wd.N, wd.H, wd.Dk, wd.Dv, 2, 4) - 2 * st_bytes)
+    mv_bytes = 2 * st_bytes + tok_bytes
+    mvs_bytes = mv_bytes + TV * st_bytes
+    del spool, snaps, mv, omv
+
     # context for the decode figure: torch's device-to-device copy of 1 GiB (read + write)
     xc = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     yc = torch.empty_like(xc)
@@ -444,6 +485,13 @@ def main():
                              "decode_hbm_gbs": gdn2_dc_bytes / float(t2d.mean()) / 1e9,
                              "decode_frac_of_peak": gdn2_dc_bytes / float(t2d.mean()) / 1e9
                              / HBM_PEAK_GBS},
+        "serving": {"verify_tokens": TV, "pool_slots": PS,
+                    "decode_multi_ms": t_mv * 1e3, "decode_multi_tokens_per_s": wd.N * TV / t_mv,
+                    "decode_multi_hbm_gbs": mv_bytes / t_mv / 1e9,
+                    "decode_multi_snapshots_ms": t_mvs * 1e3,
+                    "decode_multi_snapshots_hbm_gbs": mvs_bytes / t_mvs / 1e9,
+                    "state_copy_256_ms": t_fork * 1e3,
+                    "state_copy_hbm_gbs": 2 * st_bytes / t_fork / 1e9},
         "roofline": {"bound": "hbm", "achieved": pf_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": pf_gbs / HBM_PEAK_GBS, "traffic": traffic_pf,
                      "kernel": "kda_fwd_chunked call (prep_kernel + state_kernel; packed "

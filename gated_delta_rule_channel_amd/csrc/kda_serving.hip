@@ -10,9 +10,11 @@
 // written once; optionally the state after every token is written to a
 // snapshot array, so that a caller verifying T drafted tokens can restore the
 // state after any accepted prefix. The work split is that of the single-step
-// decode kernel: a thread owns four value columns of RPT rows; column sums go
+// decode kernel with at most 512 threads: a thread owns four value columns of
+// RPT rows; column sums go
 // through lane shuffles and LDS, double-buffered by token parity so that one
-// barrier per token suffices.
+// barrier per token suffices. The next token's inputs are loaded, unconverted,
+// while the current token is processed.
 //
 // state_copy_kernel: dst[dst_slots[i]] = src[src_slots[i]] for whole states,
 // 16-byte vector copies, one workgroup per (pair, 1024 float4 chunk).
@@ -24,15 +26,35 @@ template <int DK, int DV>
 struct MultiShape {
     static constexpr int CG = DV / 4;
     static constexpr int NT0 = DK * DV / 16;
-    static constexpr int NT = NT0 < 64 ? 64 : (NT0 > 1024 ? 1024 : NT0);
+    // at most 512 threads (8 rows each at d = 128), two workgroups per CU: the state and two
+    // tokens' inputs stay in registers across the token loop (at 128 x 128 the compiler
+    // spills 16-128 bytes a lane at this occupancy; one workgroup per CU without spills
+    // measured slower)
+    static constexpr int NT = NT0 < 64 ? 64 : (NT0 > 512 ? 512 : NT0);
     static constexpr int RS = NT / CG;
     static constexpr int RPT = DK / RS;
     static constexpr int NW = NT / 64;
     static_assert(NT % CG == 0 && DK % RS == 0 && RPT >= 1, "decode tiling");
 };
 
+// four consecutive input elements, loaded raw and converted at use
+template <typename TI> struct Raw4;
+template <> struct Raw4<float> {
+    float4 x;
+    __device__ __forceinline__ void load(const float* p) { x = *reinterpret_cast<const float4*>(p); }
+    __device__ __forceinline__ float4 get() const { return x; }
+};
+template <> struct Raw4<bf16> {
+    uint2 x;                                                 // two bfloat16 per word
+    __device__ __forceinline__ void load(const bf16* p) { x = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ float4 get() const {
+        return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                           __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
+    }
+};
+
 template <typename TI, typename TO, int DK, int DV>
-__global__ __launch_bounds__(1024) void decode_multi_kernel(
+__global__ __launch_bounds__(512, 4) void decode_multi_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
     const float* __restrict__ g, const TI* __restrict__ beta, float scale,
     float* __restrict__ pool, const int32_t* __restrict__ slots, int num_slots,
@@ -53,6 +75,24 @@ __global__ __launch_bounds__(1024) void decode_multi_kernel(
     const int wave = tid >> 6;
     const int lane = tid & 63;
 
+    // inputs of the current token (c*) and of the next one (n*), raw
+    float cg_[RPT], ng_[RPT];
+    TI ck[RPT], cq[RPT], nk[RPT], nq[RPT], cb, nb;
+    Raw4<TI> cv, nv;
+    {
+        const size_t tok = (size_t)n * T * H + h;
+        const float* gb = g + tok * DK;                    // wave-uniform bases
+        const TI *kb = k + tok * DK, *qb = q + tok * DK;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rs + RS * i;
+            cg_[i] = gb[r];
+            ck[i] = kb[r];
+            cq[i] = qb[r];
+        }
+        cv.load(v + tok * DV + 4 * cg);
+        cb = beta[tok];
+    }
     float* S = pool + ((size_t)slot * H + h) * DK * DV;
     float4 s[RPT];
 #pragma unroll
@@ -63,19 +103,30 @@ __global__ __launch_bounds__(1024) void decode_multi_kernel(
 #pragma unroll 1
     for (int t = 0; t < T; ++t) {
         const size_t tok = ((size_t)n * T + t) * H + h;     // token (n, t) of head h
-        const TI* qh = q + tok * DK;
-        const TI* kh = k + tok * DK;
-        const float* gh = g + tok * DK;
+        if (t + 1 < T) {
+            const size_t tn = tok + H;                      // token (n, t + 1)
+            const float* gb = g + tn * DK;
+            const TI *kb = k + tn * DK, *qb = q + tn * DK;
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int r = rs + RS * i;
+                ng_[i] = gb[r];
+                nk[i] = kb[r];
+                nq[i] = qb[r];
+            }
+            nv.load(v + tn * DV + 4 * cg);
+            nb = beta[tn];
+        }
+        asm volatile("" ::: "memory");                      // keep those loads issued here
         const int b = t & 1;
         float kr[RPT];
         float4 vh = make_float4(0.f, 0.f, 0.f, 0.f), rq = vh;
         float kq = 0.f;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            const int r = rs + RS * i;
-            const float a = fast_exp2(gh[r] * kLog2e);
-            const float kk = to_f(kh[r]);
-            const float qq = scale * to_f(qh[r]);
+            const float a = fast_exp2(cg_[i] * kLog2e);
+            const float kk = to_f(ck[i]);
+            const float qq = scale * to_f(cq[i]);
             kr[i] = kk;
             s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;     // forget
             vh.x += kk * s[i].x; vh.y += kk * s[i].y;                // predict
@@ -110,12 +161,14 @@ __global__ __launch_bounds__(1024) void decode_multi_kernel(
             rq.x += y.x; rq.y += y.y; rq.z += y.z; rq.w += y.w;
             kq += red_kq[b][w];
         }
-        const float bt = to_f(beta[tok]);
-        const float4 vv = load4f(v + tok * DV + 4 * cg);
+        const float bt = to_f(cb);
+        const float4 vv = cv.get();
         float4 e;                                                    // correct
         e.x = bt * (vv.x - vh.x); e.y = bt * (vv.y - vh.y);
         e.z = bt * (vv.z - vh.z); e.w = bt * (vv.w - vh.w);
-        float* snap = snapshots ? snapshots + (((size_t)n * T + t) * H + h) * DK * DV : nullptr;
+        floatx4* snap = snapshots ? reinterpret_cast<floatx4*>(
+                                        snapshots + (((size_t)n * T + t) * H + h) * DK * DV)
+                                  : nullptr;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {                              // write
             const int r = rs + RS * i;
@@ -123,11 +176,19 @@ __global__ __launch_bounds__(1024) void decode_multi_kernel(
             s[i].z += kr[i] * e.z; s[i].w += kr[i] * e.w;
             if (snap)
                 __builtin_nontemporal_store(floatx4{s[i].x, s[i].y, s[i].z, s[i].w},
-                                            reinterpret_cast<floatx4*>(snap + (size_t)r * DV) + cg);
+                                            snap + (r * (DV / 4) + cg));
         }
         if (rs == 0)                                                 // read after the write
             store4(o + tok * DV + 4 * cg, rq.x + kq * e.x, rq.y + kq * e.y, rq.z + kq * e.z,
                    rq.w + kq * e.w);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            cg_[i] = ng_[i];
+            ck[i] = nk[i];
+            cq[i] = nq[i];
+        }
+        cv = nv;
+        cb = nb;
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i)

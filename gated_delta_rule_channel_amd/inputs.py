@@ -227,8 +227,9 @@ class DecodeInputs:
 
 
 def decode_inputs(w: Workload, heads: Optional[Sequence[int]] = None,
-                  N: Optional[int] = None) -> DecodeInputs:
-    """Inputs of the decode workload: one token per request against a random state."""
+                  N: Optional[int] = None, with_state: bool = True) -> DecodeInputs:
+    """Inputs of the decode workload: one token per request against a random state
+    (state None when with_state is false; the token draws are the same either way)."""
     assert w.decode
     heads = list(range(w.H)) if heads is None else list(heads)
     n = w.N if N is None else int(N)
@@ -239,7 +240,7 @@ def decode_inputs(w: Workload, heads: Optional[Sequence[int]] = None,
     v = torch.empty((n, Hs, w.Dv), dtype=dt)
     g = torch.empty((n, Hs, w.Dk), dtype=torch.float32)
     beta = torch.empty((n, Hs), dtype=dt)
-    state = torch.empty((n, Hs, w.Dk, w.Dv), dtype=torch.float32)
+    state = torch.empty((n, Hs, w.Dk, w.Dv), dtype=torch.float32) if with_state else None
 
     def fill(j_h):
         j, h = j_h
@@ -249,8 +250,9 @@ def decode_inputs(w: Workload, heads: Optional[Sequence[int]] = None,
         v[:, j] = _cast(vv, dt)
         beta[:, j] = _cast(bb, dt)
         g[:, j] = _cast(gg, torch.float32)
-        state[:, j] = _cast(0.1 * _rng(w.wid, _STATE, h).standard_normal((n, w.Dk, w.Dv)),
-                            torch.float32)
+        if with_state:
+            state[:, j] = _cast(0.1 * _rng(w.wid, _STATE, h).standard_normal((n, w.Dk, w.Dv)),
+                                torch.float32)
 
     with _cf.ThreadPoolExecutor(_n_threads()) as ex:
         list(ex.map(fill, list(enumerate(heads))))

@@ -21,7 +21,7 @@ DEV = torch.device("cuda:0")
 
 def _tokens(w, N, T, heads=None):
     """Decode-workload draws for N requests x T tokens, laid out [N, T, H, D]."""
-    x = I.decode_inputs(w, heads=heads, N=N * T)
+    x = I.decode_inputs(w, heads=heads, N=N * T, with_state=False)
     r = lambda a: a.view(N, T, *a.shape[1:]).contiguous()
     return r(x.q), r(x.k), r(x.v), r(x.g), r(x.beta)
 
