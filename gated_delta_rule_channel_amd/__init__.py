@@ -19,6 +19,10 @@ gdn2_decode_step(q, k, v, g, b, w, state, ...).
 Serving state: decode_multi(q, k, v, g, beta, pool, slots=None, snapshots=None)
 runs T tokens per request against a slot-indexed state pool; state_copy(dst,
 dst_slots, src, src_slots) copies whole states (fork, rollback).
+
+Input preparation: prepare_inputs(q, k, a, b, scale) -> (q^, k^, g, beta) turns raw
+projections into the inputs above (normalised q and k, g = log sigmoid(a),
+beta = sigmoid(b)) in one pass.
 """
 from __future__ import annotations
 
@@ -40,7 +44,7 @@ KDA_DTYPE_BF16 = 1
 EXPORTED = ("kda_status_string", "kda_fwd_chunked_workspace_size", "kda_fwd_chunked",
             "kda_decode_step", "kda_gdn_fwd_chunked", "kda_gdn_decode_step",
             "kda_gdn2_fwd_chunked", "kda_gdn2_decode_step", "kda_decode_multi",
-            "kda_state_copy")
+            "kda_state_copy", "kda_prepare_inputs")
 
 
 class KDAError(RuntimeError):
@@ -84,6 +88,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_decode_multi.restype = i
     lib.kda_state_copy.argtypes = [vp, i, vp, vp, i, vp, i, i, i, i, vp]
     lib.kda_state_copy.restype = i
+    lib.kda_prepare_inputs.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, vp, ctypes.c_longlong, i, i,
+                                       i, vp]
+    lib.kda_prepare_inputs.restype = i
     if path is None:
         _lib_handle = lib
     return lib
@@ -347,3 +354,39 @@ def state_copy(dst, dst_slots, src, src_slots):
         _ptr(src_slots), int(dst_slots.numel()), int(H), int(Dk), int(Dv), _stream(dst.device))
     if st != KDA_SUCCESS:
         raise KDAError(st, "kda_state_copy")
+
+
+def prepare_inputs(q, k, a, b, scale: float = 1.0, out=None):
+    """q, k, a: [..., H, Dk] raw projections; b: [..., H]. Returns (scale q / |q|, k / |k|,
+    g = log sigmoid(a) float32, beta = sigmoid(b)) with the leading dimensions of q; out may
+    pass the four output tensors (q and k themselves for in-place normalisation)."""
+    import torch
+    if q.dim() < 2:
+        raise ValueError("q must be [..., H, Dk]")
+    H, Dk = q.shape[-2:]
+    lead = tuple(q.shape[:-2])
+    code = _dtype_code(q)
+    _check_same_dtype(q, k=k, v=a, beta=b)
+    _check_shape("k", k, q.shape)
+    _check_shape("a", a, q.shape)
+    _check_shape("b", b, lead + (H,))
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k),
+               torch.empty(q.shape, dtype=torch.float32, device=q.device), torch.empty_like(b))
+    qo, ko, go, bo = out
+    _check_shape("q_out", qo, q.shape)
+    _check_shape("k_out", ko, q.shape)
+    _check_shape("g_out", go, q.shape)
+    _check_shape("beta_out", bo, lead + (H,))
+    if go.dtype != torch.float32 or qo.dtype != q.dtype or ko.dtype != q.dtype or bo.dtype != q.dtype:
+        raise TypeError("g_out must be float32 and the other outputs of q's dtype")
+    _check_gpu(q, k, a, b, qo, ko, go, bo)
+    tokens = 1
+    for d in lead:
+        tokens *= int(d)
+    st = load_library().kda_prepare_inputs(
+        _ptr(q), _ptr(k), _ptr(a), _ptr(b), float(scale), _ptr(qo), _ptr(ko), _ptr(go), _ptr(bo),
+        int(tokens), int(H), int(Dk), code, _stream(q.device))
+    if st != KDA_SUCCESS:
+        raise KDAError(st, "kda_prepare_inputs")
+    return qo, ko, go, bo

@@ -24,6 +24,9 @@ hipError_t launch_decode_multi(bool bf16_in, bool bf16_out, int Dk, int Dv, cons
                                const void* k, const void* v, const float* g, const void* beta,
                                float scale, float* pool, const int32_t* slots, int num_slots,
                                float* snapshots, void* o, int N, int T, int H, hipStream_t s);
+hipError_t launch_prepare_inputs(bool bf16_io, int Dk, const void* q, const void* k,
+                                 const void* a, const void* b, float scale, void* qo, void* ko,
+                                 float* go, void* bo, long long rows, hipStream_t s);
 hipError_t launch_state_copy(float* dst, const int32_t* dst_slots, int dst_count,
                              const float* src, const int32_t* src_slots, int src_count,
                              int pairs, long long state_floats, hipStream_t s);
@@ -238,6 +241,26 @@ kda_status kda_state_copy(float* dst, int dst_count, const int32_t* dst_slots, c
     if (kda::launch_state_copy(dst, dst_slots, dst_count, src, src_slots, src_count, pairs,
                                (long long)H * Dk * Dv,
                                reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return KDA_ERROR_LAUNCH;
+    return KDA_SUCCESS;
+}
+
+kda_status kda_prepare_inputs(const void* q, const void* k, const void* a, const void* b,
+                              float scale, void* q_out, void* k_out, float* g_out,
+                              void* beta_out, long long tokens, int H, int Dk, kda_dtype dtype,
+                              void* stream) {
+    if (!q || !k || !a || !b || !q_out || !k_out || !g_out || !beta_out)
+        return KDA_ERROR_INVALID_VALUE;
+    if (tokens <= 0 || H <= 0 || !head_ok(Dk) || !dtype_ok(dtype)) return KDA_ERROR_INVALID_VALUE;
+    if (tokens > (1LL << 34) / H) return KDA_ERROR_NOT_SUPPORTED;   // grid size
+    const void* ptrs[] = {q, k, a, q_out, k_out, g_out};
+    for (const void* ptr : ptrs)
+        if (!aligned(ptr, 16)) return KDA_ERROR_INVALID_VALUE;
+    const size_t el = dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    if (!aligned(b, el) || !aligned(beta_out, el)) return KDA_ERROR_INVALID_VALUE;
+    if (kda::launch_prepare_inputs(dtype == KDA_DTYPE_BF16, Dk, q, k, a, b, scale, q_out, k_out,
+                                   g_out, beta_out, tokens * H,
+                                   reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
         return KDA_ERROR_LAUNCH;
     return KDA_SUCCESS;
 }

@@ -237,6 +237,36 @@ kda_status kda_state_copy(float* dst, int dst_count, const int32_t* dst_slots, c
                           int src_count, const int32_t* src_slots, int pairs, int H, int Dk,
                           int Dv, void* stream);
 
+/* Input preparation: the raw projections of `tokens` token positions
+ * (B * T, or the packed total) to the inputs the calls above take, in one
+ * pass over memory:
+ *
+ *   q_out = scale q / |q|     k_out = k / |k|      L2 norm over the Dk channels
+ *   g_out = log sigmoid(a)    (float32, one log-decay per key channel, < 0)
+ *   beta_out = sigmoid(b)
+ *
+ * Normalised queries and keys are those of "Notes on Linear Attention"
+ * (zhilingong.com), sections 4 and 5.3; beta as a sigmoid of a projection is
+ * the write strength of "From Fast Weight Programmers to KDA"; the pages fix
+ * g = log(alpha) with alpha in (0, 1) but not its parameterisation, and
+ * alpha = sigmoid(a) is the plainest map onto that range.
+ *
+ *  q, k, a   [tokens, H, Dk]  dtype
+ *  b         [tokens, H]      dtype
+ *  q_out, k_out [tokens, H, Dk] dtype; g_out [tokens, H, Dk] float32;
+ *  beta_out  [tokens, H] dtype. Outputs are rounded to nearest even when
+ *  dtype is bfloat16. q_out, k_out and beta_out may alias q, k and b, and
+ *  g_out may alias a when dtype is float32; a row of zeros stays zero.
+ * Errors (nothing is enqueued): KDA_ERROR_INVALID_VALUE for NULL pointers,
+ * non-positive sizes, an unsupported Dk or dtype, q, k, a, q_out, k_out or
+ * g_out not 16-byte aligned, b or beta_out not element-aligned;
+ * KDA_ERROR_NOT_SUPPORTED above 2^34 token-head rows; KDA_ERROR_LAUNCH if the
+ * launch fails. */
+kda_status kda_prepare_inputs(const void* q, const void* k, const void* a, const void* b,
+                              float scale, void* q_out, void* k_out, float* g_out,
+                              void* beta_out, long long tokens, int H, int Dk, kda_dtype dtype,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

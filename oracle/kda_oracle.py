@@ -233,3 +233,18 @@ def gdn2_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, b: n
     v_hat = np.einsum("nhkv,nhk->nhv", S_bar, b * k)
     S = S_bar + k[..., :, None] * (w * v - v_hat)[..., None, :]
     return np.einsum("nhkv,nhk->nhv", S, scale * q), S
+
+
+def prepare_inputs(q: np.ndarray, k: np.ndarray, a: np.ndarray, b: np.ndarray,
+                   scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Raw projections to the recurrence's inputs, in float64 (one token-head row per last
+    axis): q^ = scale q / |q| and k^ = k / |k| (normalised queries and keys, zhilingong.com
+    sections 4 and 5.3; a zero row stays zero), g = log sigmoid(a) (so that alpha = exp(g)
+    lies in (0, 1)), beta = sigmoid(b) (jonahsamost.bearblog.dev)."""
+    q, k, a, b = (np.asarray(x, dtype=np.float64) for x in (q, k, a, b))
+
+    def unit(x):
+        n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+    return scale * unit(q), unit(k), -np.logaddexp(0.0, -a), 1.0 / (1.0 + np.exp(-b))

@@ -234,3 +234,19 @@ def test_binding_serving_shapes():
         kda_.state_copy(pool, s, torch.zeros(4, H, D, 2 * D), s)
     with pytest.raises(ValueError, match="one length"):
         kda_.state_copy(pool, s, pool, torch.zeros(2, dtype=torch.int32))
+
+
+def test_prepare_inputs_validates(lib):
+    E = kda.KDA_ERROR_INVALID_VALUE
+    p = lambda **o: lib.kda_prepare_inputs(
+        o.get("q", FAKE), FAKE, FAKE, o.get("b", FAKE), 1.0, FAKE, FAKE, o.get("g", FAKE),
+        o.get("bo", FAKE), o.get("tokens", 8), o.get("H", 2), o.get("Dk", 64), o.get("dt", 1),
+        None)
+    assert p(q=None) == E
+    assert p(g=None) == E
+    assert p(tokens=0) == E
+    assert p(Dk=48) == E
+    assert p(dt=3) == E
+    assert p(g=FAKE + 4) == E                 # g_out not 16-byte aligned
+    assert p(bo=FAKE + 1) == E                # beta_out not element-aligned
+    assert p(tokens=1 << 34) == kda.KDA_ERROR_NOT_SUPPORTED

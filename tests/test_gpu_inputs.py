@@ -1,0 +1,93 @@
+"""Input preparation on the GPU (kda_prepare_inputs through the C ABI) against the float64
+oracle: normalised q and k, g = log sigmoid(a), beta = sigmoid(b).
+
+Bounds: a bfloat16 output is the float32 result rounded to nearest even, which is at most
+half an ulp (2^-8 relative) from that float32 value; where the float32 value and the exact
+one straddle a rounding boundary the two roundings differ by one ulp, so the check is one
+bfloat16 ulp, 2^-7 relative, from the oracle's value. Float32 outputs: within 1e-5
+relative (g, through expf and log1pf) and 2e-6 (q, k).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_channel_amd as kda
+from gated_delta_rule_channel_amd import inputs as I
+from oracle import kda_oracle, native
+from tests.parity_util import check
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _raw(tokens, H, Dk, dtype, seed):
+    rng = np.random.default_rng(seed)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = torch.from_numpy(2.0 * rng.standard_normal((tokens, H, Dk))).to(dt)
+    k = torch.from_numpy(0.5 * rng.standard_normal((tokens, H, Dk))).to(dt)
+    a = torch.from_numpy(3.0 * rng.standard_normal((tokens, H, Dk))).to(dt)
+    a[0, 0, :4] = torch.tensor([30.0, -30.0, 0.0, 12.0]).to(dt)      # both tails
+    b = torch.from_numpy(2.0 * rng.standard_normal((tokens, H))).to(dt)
+    q[1, 0] = 0.0                                                     # a zero row
+    return q, k, a, b
+
+
+def _close(name, got, ref, rtol):
+    got = got.double().numpy() if isinstance(got, torch.Tensor) else got
+    err = np.abs(got - ref)
+    lim = rtol * np.abs(ref)
+    worst = float(np.max(err / np.maximum(lim, 1e-300)))
+    print(f"  {name}: worst err / bound {worst:.3f}", flush=True)
+    assert np.all(err <= lim), f"{name}: worst err / bound {worst:.3f}"
+
+
+@pytest.mark.parametrize("Dk", [16, 32, 64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prepare_inputs_matches_oracle(Dk, dtype):
+    tokens, H = 77, 3
+    print(f"[inputs] Dk={Dk} {dtype}", flush=True)
+    q, k, a, b = _raw(tokens, H, Dk, dtype, 90 + Dk)
+    qh, kh, g, beta = kda.prepare_inputs(*(t.to(DEV) for t in (q, k, a, b)), scale=Dk ** -0.5)
+    torch.cuda.synchronize()
+    rq, rk, rg, rb = kda_oracle.prepare_inputs(*(t.double().numpy() for t in (q, k, a, b)),
+                                               scale=Dk ** -0.5)
+    r16 = 2.0 ** -7
+    _close("q^", qh.cpu(), rq, r16 if dtype == "bf16" else 2e-6)
+    _close("k^", kh.cpu(), rk, r16 if dtype == "bf16" else 2e-6)
+    _close("g", g.cpu(), rg, 1e-5)
+    _close("beta", beta.cpu(), rb, r16 if dtype == "bf16" else 2e-6)
+    assert torch.all(qh[1, 0] == 0)
+    assert g.dtype == torch.float32 and bool(torch.all(g < 0))
+
+
+def test_prepare_inputs_in_place_equals_out_of_place():
+    q, k, a, b = (t.to(DEV) for t in _raw(130, 4, 128, "bf16", 7))
+    print("[inputs] in place", flush=True)
+    ref = kda.prepare_inputs(q, k, a, b, scale=0.3)
+    g = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    out = kda.prepare_inputs(q, k, a, b, scale=0.3, out=(q, k, g, b))
+    torch.cuda.synchronize()
+    for x, y in zip(out, ref):
+        assert torch.equal(x, y)
+
+
+def test_prepared_inputs_feed_the_prefill():
+    """Raw projections -> prepare_inputs -> fwd_chunked, against the oracle's own preparation
+    and recurrence (B1 T300 H4 d128 bf16)."""
+    B, T, H, D = 1, 300, 4, 128
+    print("[inputs] prepare + prefill", flush=True)
+    q, k, a, b = _raw(B * T, H, D, "bf16", 8)
+    v = torch.from_numpy(np.random.default_rng(9).standard_normal((B, T, H, D))).bfloat16()
+    qh, kh, g, beta = kda.prepare_inputs(*(t.to(DEV) for t in (q, k, a, b)), scale=D ** -0.5)
+    rs = lambda t: t.view(B, T, *t.shape[1:])
+    o, ht = kda.fwd_chunked(rs(qh), rs(kh), v.to(DEV), rs(g), rs(beta))
+    torch.cuda.synchronize()
+    rq, rk, rg, rb = kda_oracle.prepare_inputs(*(t.double().numpy() for t in (q, k, a, b)),
+                                               scale=D ** -0.5)
+    cast = lambda x: torch.from_numpy(x).to(torch.bfloat16)
+    o_ref, ht_ref = native.prefill(rs(cast(rq)), rs(cast(rk)), v, rs(torch.from_numpy(rg).float()),
+                                   rs(cast(rb)))
+    check("o", o.cpu().numpy(), o_ref, "bf16")
+    check("ht", ht.cpu().numpy(), ht_ref, "bf16")

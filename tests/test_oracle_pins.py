@@ -535,3 +535,37 @@ def test_gdn2_decode_steps_equal_forward():
         od, S = kda_oracle.gdn2_decode(q[:, t], k[:, t], v[:, t], g[:, t], bn[:, t], wn[:, t], S)
         np.testing.assert_allclose(od, o[:, t], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(S, ht, rtol=1e-12, atol=1e-12)
+
+
+# --- input preparation ------------------------------------------------------------------------
+def test_prepare_inputs_closed_forms():
+    """Normalised q and k (zhilingong.com, sections 4 and 5.3): unit k parallel to k, |q^| =
+    scale, a zero row stays zero; alpha = exp(g) = sigmoid(a) in (0, 1), log sigmoid(0) =
+    -log 2, g -> a for a -> -inf and g -> -exp(-a) for a -> +inf without cancelling to 0;
+    beta = sigmoid(b) with beta(0) = 1/2 and beta(x) + beta(-x) = 1."""
+    import math
+    rng = np.random.default_rng(81)
+    q = rng.standard_normal((5, 3, 16)) * 3.0
+    k = rng.standard_normal((5, 3, 16)) * 0.2
+    q[2, 1] = 0.0
+    a = np.array([0.0, -40.0, 30.0, 1.5, -2.25])
+    b = np.array([0.0, 3.0, -3.0, 0.7, -0.7])
+    qh, kh, g, beta = kda_oracle.prepare_inputs(q, k, np.broadcast_to(a[:, None, None], q.shape),
+                                                np.broadcast_to(b[:, None], q.shape[:2]),
+                                                scale=0.25)
+    np.testing.assert_allclose(np.linalg.norm(kh, axis=-1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(np.sum(kh * k, axis=-1), np.linalg.norm(k, axis=-1), rtol=1e-14)
+    nq = np.linalg.norm(qh, axis=-1)
+    assert nq[2, 1] == 0.0 and np.all(qh[2, 1] == 0.0)
+    np.testing.assert_allclose(np.delete(nq.ravel(), 2 * 3 + 1), 0.25, rtol=1e-14)
+    gs = g[:, 0, 0]
+    assert gs[0] == pytest.approx(-math.log(2.0), rel=1e-15)
+    assert gs[1] == pytest.approx(-40.0, rel=1e-15)
+    assert gs[2] == pytest.approx(-math.exp(-30.0), rel=1e-12) and gs[2] < 0.0
+    for i in (3, 4):
+        assert gs[i] == pytest.approx(math.log(1.0 / (1.0 + math.exp(-a[i]))), rel=1e-14)
+    assert np.all(np.exp(gs) < 1.0) and np.all(np.exp(gs) > 0.0)
+    bs = beta[:, 0]
+    assert bs[0] == 0.5
+    assert bs[1] + bs[2] == pytest.approx(1.0, rel=1e-15)
+    assert bs[3] + bs[4] == pytest.approx(1.0, rel=1e-15)
