@@ -10,7 +10,8 @@ reports the decode step repeated back to back (the sustained rate) and the
 same step for Gated DeltaNet (one scalar gate per token and head) and Gated
 DeltaNet-2 (erase and write gates per channel in place of beta), and the
 serving-state operations (4-token verification against a slot-indexed state
-pool, with and without per-token snapshots, and a 256-state fork copy).
+pool, with and without per-token snapshots, and a 256-state fork copy), and the
+input preparation pass at the main prefill's shape.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
   python bench.py --copy-calibration          # 1 GiB device copy (counter calibration)
@@ -425,6 +426,19 @@ def main():
     mvs_bytes = mv_bytes + TV * st_bytes
     del spool, snaps, mv, omv
 
+    # input preparation at the main prefill's shape: raw bf16 q, k, a [T, H, Dk] and b [T, H]
+    # to normalised q, k (bf16), g (fp32) and beta (bf16), one pass
+    rng_i = torch.Generator(device=dev).manual_seed(3)
+    raw = [torch.randn((B * T, H, Dk), generator=rng_i, device=dev).to(torch.bfloat16)
+           for _ in range(3)]
+    raw.append(torch.randn((B * T, H), generator=rng_i, device=dev).to(torch.bfloat16))
+    prep_out = (torch.empty_like(raw[0]), torch.empty_like(raw[1]),
+                torch.empty((B * T, H, Dk), dtype=torch.float32, device=dev),
+                torch.empty_like(raw[3]))
+    t_prep = timed(lambda: kda.prepare_inputs(*raw, scale=Dk ** -0.5, out=prep_out), n_serv)
+    prep_bytes = B * T * H * (Dk * 2 * 5 + Dk * 4 + 2 * 2)
+    del raw, prep_out
+
     # context for the decode figure: torch's device-to-device copy of 1 GiB (read + write)
     xc = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     yc = torch.empty_like(xc)
@@ -492,6 +506,9 @@ def main():
                     "decode_multi_snapshots_hbm_gbs": mvs_bytes / t_mvs / 1e9,
                     "state_copy_256_ms": t_fork * 1e3,
                     "state_copy_hbm_gbs": 2 * st_bytes / t_fork / 1e9},
+        "input_prep": {"ms": t_prep * 1e3, "bytes": prep_bytes,
+                       "hbm_gbs": prep_bytes / t_prep / 1e9,
+                       "frac_of_peak": prep_bytes / t_prep / 1e9 / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": pf_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": pf_gbs / HBM_PEAK_GBS, "traffic": traffic_pf,
                      "kernel": "kda_fwd_chunked call (prep_kernel + state_kernel; packed "

@@ -17,11 +17,20 @@
 
 namespace kda {
 
+// log(1 + y) for y in [0, 1]: a four-term series below 2^-6 (truncation below y^5 / 5, under
+// 2^-24 relative there), else the hardware log2 of 1 + y (its rounding of 1 + y costs at most
+// 2^-24 / y <= 2^-18 relative)
+__device__ __forceinline__ float log1p_unit(float y) {
+    if (y < 0.015625f) return y * (1.f - y * (0.5f - y * (1.f / 3.f - 0.25f * y)));
+    return __builtin_amdgcn_logf(1.f + y) * 0.69314718055994531f;
+}
 __device__ __forceinline__ float log_sigmoid(float x) {
     // log(1 / (1 + e^-x)) = -(max(-x, 0) + log(1 + e^-|x|)), without overflow
-    return -(fmaxf(-x, 0.f) + log1pf(expf(-fabsf(x))));
+    return -(fmaxf(-x, 0.f) + log1p_unit(fast_exp2(-fabsf(x) * kLog2e)));
 }
-__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float sigmoid(float x) {
+    return 1.f / (1.f + fast_exp2(-x * kLog2e));
+}
 
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16> {

@@ -7,14 +7,11 @@ one straddle a rounding boundary the two roundings differ by one ulp, so the che
 bfloat16 ulp, 2^-7 relative, from the oracle's value. Float32 outputs: within 1e-5
 relative (g, through expf and log1pf) and 2e-6 (q, k).
 """
-import dataclasses
-
 import numpy as np
 import pytest
 import torch
 
 import gated_delta_rule_channel_amd as kda
-from gated_delta_rule_channel_amd import inputs as I
 from oracle import kda_oracle, native
 from tests.parity_util import check
 
