@@ -24,9 +24,23 @@
 // DeltaNet-2 ("From Fast Weight Programmers to KDA", section "Gated
 // DeltaNet-2"): the prediction reads through b * k (b per key channel) and
 // the error is w * v - v^ (w per value channel); the write stays at k.
+#include <atomic>
+
 #include "kda_common.h"
 
 namespace kda {
+
+// Successive decode steps on a device walk the (request, head) states in alternating order:
+// a step's last ~256 MB of state writes are still in the Infinity Cache when the next step
+// starts, and the next step then starts on exactly those states (its first reads hit in the
+// cache and the dirty lines are rewritten before they reach HBM). Each state is updated on
+// its own, so the order never changes a result. Shared by the single- and multi-token steps.
+int next_decode_order() {
+    static std::atomic<unsigned> calls[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    return (int)(calls[dev].fetch_add(1, std::memory_order_relaxed) & 1u);
+}
 
 template <int DK, int DV>
 struct DecodeShape {
@@ -45,14 +59,16 @@ template <typename TI, typename TO, int DK, int DV, bool SG, bool EW>
 __global__ __launch_bounds__(1024) void decode_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
     const float* __restrict__ g, const TI* __restrict__ beta, const TI* __restrict__ eb,
-    const TI* __restrict__ ew, float scale, float* __restrict__ state, TO* __restrict__ o) {
+    const TI* __restrict__ ew, float scale, float* __restrict__ state, TO* __restrict__ o,
+    int reverse) {
     using Sh = DecodeShape<DK, DV>;
     constexpr int CG = Sh::CG, RS = Sh::RS, RPT = Sh::RPT, NW = Sh::NW;
     __shared__ float4 red_vh[NW][CG];
     __shared__ float4 red_rq[NW][CG];
     __shared__ float red_kq[NW];
 
-    const int head = blockIdx.x;                 // n * H + h
+    // n * H + h, in the order of this step (see next_decode_order)
+    const int head = reverse ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
     const int tid = threadIdx.x;
     const int cg = tid % CG;
     const int rs = tid / CG;
@@ -149,15 +165,17 @@ static hipError_t launch_decode_t(bool sg, const void* q, const void* k, const v
     const dim3 grid((unsigned)((long long)N * H));
     const dim3 block(DecodeShape<DK, DV>::NT);
     const TI *tq = (const TI*)q, *tk = (const TI*)k, *tv = (const TI*)v, *tb = (const TI*)beta;
+    const int rev = next_decode_order();
     if (eb)
         hipLaunchKernelGGL((decode_kernel<TI, TO, DK, DV, false, true>), grid, block, 0, stream,
-                           tq, tk, tv, g, tb, (const TI*)eb, (const TI*)ew, scale, state, (TO*)o);
+                           tq, tk, tv, g, tb, (const TI*)eb, (const TI*)ew, scale, state, (TO*)o,
+                           rev);
     else if (sg)
         hipLaunchKernelGGL((decode_kernel<TI, TO, DK, DV, true, false>), grid, block, 0, stream,
-                           tq, tk, tv, g, tb, nullptr, nullptr, scale, state, (TO*)o);
+                           tq, tk, tv, g, tb, nullptr, nullptr, scale, state, (TO*)o, rev);
     else
         hipLaunchKernelGGL((decode_kernel<TI, TO, DK, DV, false, false>), grid, block, 0, stream,
-                           tq, tk, tv, g, tb, nullptr, nullptr, scale, state, (TO*)o);
+                           tq, tk, tv, g, tb, nullptr, nullptr, scale, state, (TO*)o, rev);
     return hipGetLastError();
 }
 

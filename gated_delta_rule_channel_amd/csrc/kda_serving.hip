@@ -22,6 +22,8 @@
 
 namespace kda {
 
+int next_decode_order();                         // alternating state order (kda_decode.hip)
+
 template <int DK, int DV>
 struct MultiShape {
     static constexpr int CG = DV / 4;
@@ -58,14 +60,15 @@ __global__ __launch_bounds__(512, 4) void decode_multi_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
     const float* __restrict__ g, const TI* __restrict__ beta, float scale,
     float* __restrict__ pool, const int32_t* __restrict__ slots, int num_slots,
-    float* __restrict__ snapshots, TO* __restrict__ o, int T, int H) {
+    float* __restrict__ snapshots, TO* __restrict__ o, int T, int H, int reverse) {
     using Sh = MultiShape<DK, DV>;
     constexpr int CG = Sh::CG, RS = Sh::RS, RPT = Sh::RPT, NW = Sh::NW;
     __shared__ float4 red_vh[2][NW][CG];
     __shared__ float4 red_rq[2][NW][CG];
     __shared__ float red_kq[2][NW];
 
-    const int nh = blockIdx.x;                   // n * H + h
+    // n * H + h, in the order of this call (alternating between calls, as the one-step decode)
+    const int nh = reverse ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
     const int n = nh / H, h = nh % H;
     const int slot = slots ? slots[n] : n;
     if (slot < 0 || slot >= num_slots) return;   // uniform over the workgroup
@@ -219,7 +222,7 @@ static hipError_t launch_multi_t(const void* q, const void* k, const void* v, co
     hipLaunchKernelGGL((decode_multi_kernel<TI, TO, DK, DV>),
                        dim3((unsigned)((long long)N * H)), dim3(MultiShape<DK, DV>::NT), 0, s,
                        (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
-                       pool, slots, num_slots, snapshots, (TO*)o, T, H);
+                       pool, slots, num_slots, snapshots, (TO*)o, T, H, next_decode_order());
     return hipGetLastError();
 }
 

@@ -23,7 +23,10 @@
  *  - All tensor pointers are DEVICE pointers, row-major and contiguous, owned
  *    by the caller. The library allocates no memory; its only global state is
  *    a per-device cache of the compute-unit count (filled on first use,
- *    thread-safe). Calls on different streams are independent.
+ *    thread-safe) and a per-device parity of decode calls, which makes
+ *    successive decode steps visit the states in alternating order (each
+ *    state is updated on its own, so results never depend on it). Calls on
+ *    different streams are independent.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    default stream). Arguments are validated on the host before anything is
  *    enqueued: on any error nothing runs and no output is touched. Faults that

@@ -109,3 +109,24 @@ def test_decode_no_decay_unit_beta_stores_pair():
     check("state", S, S_ref, "f32")
     got = np.einsum("nhi,nhij->nhj", x.k.double().numpy(), S.astype(np.float64))
     check("k^T S' vs v", got, x.v.double().numpy(), "f32")
+
+
+def test_alternating_state_order_gives_identical_results():
+    """Successive decode calls visit the states in opposite orders (for the Infinity Cache);
+    two consecutive calls on copies of one state must agree bit for bit, for the single-step
+    and the multi-token decode."""
+    w = I.WORKLOADS[3]
+    x = I.decode_inputs(w, heads=list(range(16)), N=32)
+    dev = torch.device("cuda:0")
+    a = [t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta)]
+    print("[decode] alternating order", flush=True)
+    s1, s2 = x.state.to(dev), x.state.to(dev)
+    o1 = kda.decode_step(*a, s1)
+    o2 = kda.decode_step(*a, s2)
+    m = [t[:, None].expand(-1, 3, *t.shape[1:]).contiguous() for t in a]
+    p1, p2 = x.state.to(dev), x.state.to(dev)
+    r1 = kda.decode_multi(*m, p1)
+    r2 = kda.decode_multi(*m, p2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert torch.equal(r1, r2) and torch.equal(p1, p2)
