@@ -521,11 +521,25 @@ __global__ __launch_bounds__(256, EW ? 1 : 2) void prep_kernel(
                 }
             }
         }
+        // with a scalar gate the 8 channels of a row hold the same values: reading one of them
+        // for all 8 lets the compiler form each decay factor once
+        if constexpr (SG) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int e = 1; e < 8; ++e) G[8 * I + e] = G[8 * I];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) gtot[e] = gtot[0];
+        }
         // the 8 cumulative values of this lane's channels at the end of block I
         auto ce8 = [&](int I, float* o) {
             const float4 a = sCE[I][2 * (c0 / 8)], b = sCE[I][2 * (c0 / 8) + 1];
             o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
             o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+            if constexpr (SG) {
+#pragma unroll
+                for (int e = 1; e < 8; ++e) o[e] = o[0];
+            }
         };
         if (cvalid && m == 0) {
 #pragma unroll
@@ -560,9 +574,10 @@ __global__ __launch_bounds__(256, EW ? 1 : 2) void prep_kernel(
                 for (int e = 0; e < 8; ++e) kl[e] = kk[e];
             }
             ce8(Ip, pf);                                  // cumulative value before block I
+            const float gI0 = SG ? opq(G[8 * I]) : 0.f;   // the row's gate (scalar gate)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                Gl[e] = opq(G[8 * I + e]);
+                Gl[e] = SG ? gI0 : opq(G[8 * I + e]);
                 if (I == 0) pf[e] = 0.f;
             }
             // (a) chunk-start / chunk-end references: Qd and Kd^T to the workspace
@@ -684,10 +699,11 @@ __global__ __launch_bounds__(256, EW ? 1 : 2) void prep_kernel(
                 K.get8p(J, kJ);
                 ce8(Jp, ceJ);
                 Frag b;
+                const float gJ0 = SG ? opq(G[8 * J]) : 0.f;  // the row's gate (scalar gate)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float cj = J > 0 ? ceJ[e] : 0.f;
-                    b.set(e, kJ[e] * fast_exp2(pfI[e] - cj - opq(G[8 * J + e])));
+                    b.set(e, kJ[e] * fast_exp2(pfI[e] - cj - (SG ? gJ0 : opq(G[8 * J + e]))));
                 }
                 floatx4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
                 Pol::mma(akk, b, KA2);
@@ -721,9 +737,10 @@ __global__ __launch_bounds__(256, EW ? 1 : 2) void prep_kernel(
                 ce8(2, pf3);
                 const float b3 = sBeta[48 + m];
                 Frag KA3, QA3;
+                const float g30 = SG ? opq(G[24]) : 0.f;    // the row's gate (scalar gate)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float ea = fast_exp2(opq(G[24 + e]));
+                    const float ea = fast_exp2(SG ? g30 : opq(G[24 + e]));
                     KA3.set(e, b3 * k3[e] * ea);
                     QA3.set(e, scale * q3[e] * ea);
                 }
