@@ -42,6 +42,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 METRIC = "KDA prefill tokens/s (H=64,d=128,bf16) + decode-step state GB/s vs peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_main_prefill_and_decode.json")
 COPY_BYTES = 1 << 30
+KERNEL_DESC = ("kda_fwd_chunked call (prep_kernel + state_kernel; packed input adds "
+               "chunk_map_kernel), one launch sequence per step")
 
 
 def prefill_bytes(T, H, Dk, Dv, in_bytes, out_bytes, n_seq):
@@ -313,14 +315,23 @@ def main():
     tp_mean, td_mean = float(tp.mean()), float(td.mean())
 
     tokens = B * T
-    pf_bytes = prefill_bytes(T, H, Dk, Dv, 2, 4, B)
+    # algorithmic bytes of the hot-path table: q, k, v, beta bf16, g fp32, o bf16, ht fp32
+    # (810,549,248 B here); the fp32 o this bench writes moves 2 more bytes per output
+    # element, reported apart and never counted as compulsory
+    pf_bytes = prefill_bytes(T, H, Dk, Dv, 2, 2, B)
+    pf_o_f32_extra = B * T * H * Dv * 2
     dc_bytes = decode_bytes(wd.N, wd.H, wd.Dk, wd.Dv, 2, 4)
     pf_flops = prefill_flops(T, H, Dk, Dv)
     value = tokens / tp_mean
     pf_gbs = pf_bytes / tp_mean / 1e9
     dc_gbs = dc_bytes / td_mean / 1e9
-    # split-bf16 operands: every product runs as three bf16 MFMAs
-    mfma_busy = 3.0 * pf_flops / (BF16_PEAK_TFLOPS * 1e12) / tp_mean
+    # roofline time of the call: max(algorithmic bytes / 8 TB/s, MFMA time); with split-bf16
+    # operands every product runs as three bf16 MFMAs
+    t_hbm = pf_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = 3.0 * pf_flops / (BF16_PEAK_TFLOPS * 1e12)
+    t_roof = max(t_hbm, t_mfma)
+    mfma_busy = t_mfma / tp_mean
+    mfma_alg = pf_flops / (BF16_PEAK_TFLOPS * 1e12) / tp_mean
     traffic_pf, traffic_dc = load_traffic()
 
     def run_extras():
@@ -460,7 +471,8 @@ def main():
         htv = torch.empty((len(lens), H, Dk, Dv), dtype=torch.float32, device=dev)
         t_var = timed(lambda: kda.fwd_chunked(vq, vk, vv, vg, vb, cu_seqlens=cu_v, workspace=wsv,
                                               out=ov, final_state=htv), max(3, n_serv // 5))
-        var_bytes = TV_ * H * (3 * Dk * 2 + Dk * 4 + 2 + Dv * 4) + len(lens) * H * Dk * Dv * 4
+        # algorithmic bytes per token as for the main prefill (bf16 o): 98,432 at H64 d128
+        var_bytes = TV_ * H * (3 * Dk * 2 + Dk * 4 + 2 + Dv * 2) + len(lens) * H * Dk * Dv * 4
         del vq, vk, vv, vb, vg, wsv, ov, htv
 
         # input preparation at the main prefill's shape: raw bf16 q, k, a [T, H, Dk] and b [T, H]
@@ -546,9 +558,13 @@ def main():
                    "chunk": 64, "parallelism": "single GPU"},
         "prefill": {"ms": tp_mean * 1e3, "ms_median": float(np.median(tp)) * 1e3,
                     "ms_min": float(tp.min()) * 1e3, "tokens_per_s": value,
-                    "compulsory_bytes": pf_bytes, "hbm_gbs": pf_gbs,
+                    "compulsory_bytes": pf_bytes, "o_fp32_extra_bytes": pf_o_f32_extra,
+                    "hbm_gbs": pf_gbs,
                     "algorithmic_flops": pf_flops, "tflops": pf_flops / tp_mean / 1e12,
-                    "mfma_busy_frac_split_bf16": mfma_busy},
+                    "t_roof_us": t_roof * 1e6, "t_hbm_us": t_hbm * 1e6, "t_mfma_us": t_mfma * 1e6,
+                    "frac_of_roofline": t_roof / tp_mean,
+                    "mfma_busy_frac_split_bf16": mfma_busy,
+                    "mfma_frac_algorithmic_flops": mfma_alg},
         "decode": {"ms": td_mean * 1e3, "ms_median": float(np.median(td)) * 1e3,
                    "ms_min": float(td.min()) * 1e3,
                    "state_updates_per_s": wd.N * wd.H / td_mean, "tokens_per_s": wd.N / td_mean,
@@ -559,8 +575,10 @@ def main():
         **{k: v for k, v in extra.items() if k != "decode_b2b"},
         "roofline": {"bound": "hbm", "achieved": pf_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": pf_gbs / HBM_PEAK_GBS, "traffic": traffic_pf,
-                     "kernel": "kda_fwd_chunked call (prep_kernel + state_kernel; packed "
-                               "input adds chunk_map_kernel), one launch sequence per step"},
+                     "byte_basis": "algorithmic: q, k, v, beta bf16 + g fp32 + o bf16 + ht fp32 "
+                                   f"= {pf_bytes} B per call (the fp32 o adds "
+                                   f"{pf_o_f32_extra} B, not counted)",
+                     "kernel": KERNEL_DESC},
         "roofline_decode": {"bound": "hbm", "achieved": dc_gbs, "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": dc_gbs / HBM_PEAK_GBS, "traffic": traffic_dc,
                             "kernel": "decode_kernel"},

@@ -131,6 +131,7 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERROR_NOT_SUPPORTED: return "KDA_ERROR_NOT_SUPPORTED";
         case KDA_ERROR_WORKSPACE: return "KDA_ERROR_WORKSPACE";
         case KDA_ERROR_LAUNCH: return "KDA_ERROR_LAUNCH";
+        default: break;
     }
     return "KDA_ERROR_UNKNOWN";
 }

@@ -126,8 +126,10 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
         const int n = base + tid;
         int st = 0, en = 0, cnt = 0;
         if (n < N) {
-            st = cu ? cu[n] : n * T;
-            en = cu ? cu[n + 1] : (n + 1) * T;
+            // packed bounds are clamped to [0, T] with en >= st, so a malformed cu_seqlens
+            // can only mis-assign tokens, never address outside the inputs
+            st = cu ? min(max(cu[n], 0), T) : n * T;
+            en = cu ? min(max(cu[n + 1], st), T) : (n + 1) * T;
             const int len = en > st ? en - st : 0;
             cnt = (len + kChunk - 1) / kChunk;
         }
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(256, EW ? 1 : 2) void prep_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
     const float* __restrict__ g, const TI* __restrict__ beta, const TI* __restrict__ eb,
     const TI* __restrict__ ew, float scale, const int4* __restrict__ tab, int T, int nslots,
-    uint8_t* __restrict__ ws, int H) {
+    uint8_t* __restrict__ ws, int H, long long beta_elems) {
     using Pol = typename PolOf<TI>::type;
     using Frag = typename Pol::Frag;
     using Frag4 = typename Pol::Frag4;
@@ -375,7 +377,13 @@ __global__ __launch_bounds__(256, EW ? 1 : 2) void prep_kernel(
             }
             if (!EW && I == 0 && wave == 0 && lane < L) {
                 const size_t e = (size_t)(t0 + lane) * H + h;       // beta element index
-                lds_load4(reinterpret_cast<const unsigned*>(beta) + (e >> 1), sBetaRaw);
+                if ((e & 1) == 0 && (long long)e + 1 >= beta_elems) {
+                    // the word holding the last element would extend past the array: read
+                    // that element alone (once per call, so its wait costs nothing)
+                    sBetaRaw[lane] = reinterpret_cast<const unsigned short*>(beta)[e];
+                } else {
+                    lds_load4(reinterpret_cast<const unsigned*>(beta) + (e >> 1), sBetaRaw);
+                }
             }
         }
     };
@@ -1000,7 +1008,7 @@ __device__ __forceinline__ void decode_pairs(typename Pol::Frag (&d)[KS],
 template <typename TI, typename TO, int DK, int DV, int BV>
 __global__ __launch_bounds__(768) void state_kernel(
     const int32_t* __restrict__ cu, int T, const int32_t* __restrict__ seq_off,
-    const uint8_t* __restrict__ ws, const float* __restrict__ h0, float* __restrict__ ht,
+    const uint8_t* __restrict__ ws, const float* h0, float* ht,   // ht may equal h0
     TO* __restrict__ o, int N, int H) {
     using Pol = typename PolOf<TI>::type;
     using Frag = typename Pol::Frag;
@@ -1065,7 +1073,9 @@ __global__ __launch_bounds__(768) void state_kernel(
     // around loads.
     const int nck = (T + kChunk - 1) / kChunk;
     const int c_beg = seq_off ? seq_off[n] : n * nck, c_end = seq_off ? seq_off[n + 1] : (n + 1) * nck;
-    const int s_beg = cu ? cu[n] : n * T, s_end = cu ? cu[n + 1] : (n + 1) * T;
+    // the same clamped bounds as the chunk map
+    const int s_beg = cu ? min(max(cu[n], 0), T) : n * T;
+    const int s_end = cu ? min(max(cu[n + 1], s_beg), T) : (n + 1) * T;
     const int last = c_end - 1;
     const size_t rowo = (size_t)H * DV;
     auto block = [&](int c) { return ws + ((size_t)c * H + h) * Ly::BYTES; };
@@ -1348,18 +1358,19 @@ static hipError_t launch_prefill_t(bool sg, const void* q, const void* k, const 
     const long long per_cu = eb ? 1 : 2;
     const long long grid = ntasks < per_cu * cu_count ? ntasks : per_cu * cu_count;
     const TI *tq = (const TI*)q, *tk = (const TI*)k, *tv = (const TI*)v, *tb = (const TI*)beta;
+    const long long beta_elems = (cu ? (long long)T : (long long)N * T) * H;   // [tokens, H]
     if (eb)
         hipLaunchKernelGGL((prep_kernel<TI, DK, DV, false, true>), dim3((unsigned)grid), dim3(256),
                            0, s, tq, tk, tv, g, tb, (const TI*)eb, (const TI*)ew, scale,
-                           (const int4*)tab, T, max_slots, blocks, H);
+                           (const int4*)tab, T, max_slots, blocks, H, beta_elems);
     else if (sg)
         hipLaunchKernelGGL((prep_kernel<TI, DK, DV, true, false>), dim3((unsigned)grid), dim3(256),
                            0, s, tq, tk, tv, g, tb, nullptr, nullptr, scale, (const int4*)tab, T,
-                           max_slots, blocks, H);
+                           max_slots, blocks, H, beta_elems);
     else
         hipLaunchKernelGGL((prep_kernel<TI, DK, DV, false, false>), dim3((unsigned)grid),
                            dim3(256), 0, s, tq, tk, tv, g, tb, nullptr, nullptr, scale,
-                           (const int4*)tab, T, max_slots, blocks, H);
+                           (const int4*)tab, T, max_slots, blocks, H, beta_elems);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int BV = DV >= 32 ? 32 : DV;

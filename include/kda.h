@@ -61,10 +61,14 @@ typedef enum {
     KDA_ERROR_INVALID_VALUE = 1,  /* bad pointer, size, alignment or combination */
     KDA_ERROR_NOT_SUPPORTED = 2,  /* valid request the library does not implement */
     KDA_ERROR_WORKSPACE = 3,      /* workspace missing or smaller than required */
-    KDA_ERROR_LAUNCH = 4          /* the HIP runtime refused a kernel launch */
+    KDA_ERROR_LAUNCH = 4,         /* the HIP runtime refused a kernel launch */
+    KDA_STATUS_FORCE_INT32 = 0x7fffffff   /* not a status: gives the type the range of int32 */
 } kda_status;
 
-typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
+/* KDA_DTYPE_FORCE_INT32 is not a type: it makes every int32 value a valid kda_dtype, so
+ * that an unknown value passed from C is rejected (KDA_ERROR_INVALID_VALUE) rather than
+ * being undefined behaviour in the C++ implementation. */
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1, KDA_DTYPE_FORCE_INT32 = 0x7fffffff } kda_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kda_status_string(kda_status s);

@@ -6,22 +6,23 @@ TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 
 What it computes is the recurrence itself, token by token, in float64 with
 no blocking, chunking or reordering. The state S of one head is d_k x d_v
-with one row per key channel (the [..., d_k, d_v] layout used by the
-reference PyTorch code quoted on "Kimi Delta Attention (KDA)", brain.bigb.es,
-section "KDA: one gate per key channel"). One step at token t, in the order
-given as five named operations on "Module 03 - KDA I: The Delta-Rule
-Recurrence" (jared-hpc.com), section 2:
+with one row per key channel and the read is o = S^T q ("Notes on Linear
+Attention", zhilingong.com, sections 3 and 11, where S_t = sum_i k_i v_i^T;
+the pages that write the state d_v x d_k use its transpose). One step at
+token t is the sequence of five operations of "Module 03 - KDA I: The
+Delta-Rule Recurrence" (jared-hpc.com), section 2, written out here per key
+channel i (row i of S) and value channel j:
 
-  (1) forget   S~ = Diag(exp(g_t)) S          per key channel (rows of S)
-  (2) predict  v^ = S~^T k_t
-  (3) correct  e  = beta_t (v_t - v^)         beta inside the error, as on the
-                                              brain.bigb.es page; the same S_t
-                                              as applying beta at the write
-  (4) write    S  = S~ + k_t e^T
-  (5) read     o_t = S^T (scale * q_t)        read after the write
+  (1) forget   S~[i][j] = alpha_t[i] S[i][j],          alpha_t = exp(g_t)
+  (2) predict  v^[j]    = sum_i k_t[i] S~[i][j]
+  (3) correct  e[j]     = beta_t (v_t[j] - v^[j])      beta inside the error
+  (4) write    S[i][j]  = S~[i][j] + k_t[i] e[j]
+  (5) read     o_t[j]   = sum_i (scale q_t[i]) S[i][j]  after the write
 
-Implementations keep g_t = log(alpha_t) <= 0 and decay by exp(g_t)
-(brain.bigb.es, "KDA: one gate per key channel").
+Putting beta inside the error gives the same S_t as applying it at the write
+("Kimi Delta Attention (KDA)", brain.bigb.es, section "KDA: one gate per key
+channel", which also fixes g_t = log(alpha_t) <= 0 as the stored gate). The
+loops run over the key channel; heads and value channels are numpy axes.
 
 Gated DeltaNet (gdn_forward, gdn_decode) is the same recurrence with one
 scalar retention gate alpha_t = exp(g_t) per token and head instead of one
@@ -45,6 +46,7 @@ closed form at beta = 0, and the per-channel recurrence with an equal gate; for
 the erase/write gates: the matrix form, the collapse to KDA at b = beta 1,
 w = beta 1, and the additive closed form at b = 0).
 """
+
 from __future__ import annotations
 
 from typing import Optional, Tuple
@@ -52,19 +54,50 @@ from typing import Optional, Tuple
 import numpy as np
 
 
+# ------------------------------------------------------------------------------------------
+# the five operations, per key channel. S has shape [..., Dk, Dv] (leading axes: heads, or
+# requests and heads) and is updated in place; every vector argument has the matching
+# leading axes.
+# ------------------------------------------------------------------------------------------
+def _forget_and_predict(S: np.ndarray, alpha: np.ndarray, k_read: np.ndarray) -> np.ndarray:
+    """(1) row i of S decays by alpha[i]; (2) v^ = sum_i k_read[i] S~[i]. Returns v^."""
+    v_hat = np.zeros(S.shape[:-2] + S.shape[-1:])
+    for i in range(S.shape[-2]):
+        S[..., i, :] *= alpha[..., i, None]
+        v_hat += k_read[..., i, None] * S[..., i, :]
+    return v_hat
+
+
+def _write_and_read(S: np.ndarray, k: np.ndarray, e: np.ndarray, q: np.ndarray,
+                    scale: float) -> np.ndarray:
+    """(4) row i of S moves by k[i] e; (5) o = sum_i (scale q[i]) S[i]. Returns o."""
+    o = np.zeros(S.shape[:-2] + S.shape[-1:])
+    for i in range(S.shape[-2]):
+        S[..., i, :] += k[..., i, None] * e
+        o += (scale * q[..., i, None]) * S[..., i, :]
+    return o
+
+
+def _additive_write_and_read(S: np.ndarray, k: np.ndarray, v: np.ndarray, q: np.ndarray,
+                             scale: float) -> np.ndarray:
+    """Plain linear attention: S[i] += k[i] v (no decay, no error), then the same read."""
+    return _write_and_read(S, k, v, q, scale)
+
+
 def kda_step(S: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray,
              beta: float, scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray, dict]:
     """One KDA step for one head. S is [Dk, Dv]; returns (S_t, o_t, intermediates).
 
-    Five steps of "Module 03 - KDA I" (jared-hpc.com) section 2, with the
+    The five operations of "Module 03 - KDA I" (jared-hpc.com) section 2, with the
     beta-scaled error of brain.bigb.es "Kimi Delta Attention (KDA)".
     """
-    S_tilde = np.exp(g)[:, None] * S            # (1) forget, per key channel
-    v_hat = S_tilde.T @ k                       # (2) predict
-    e = beta * (v - v_hat)                      # (3) correct
-    S_new = S_tilde + np.outer(k, e)            # (4) rank-one write
-    o = S_new.T @ (scale * q)                   # (5) read after write
-    return S_new, o, {"S_tilde": S_tilde, "v_hat": v_hat, "e": e}
+    S = np.array(S, dtype=np.float64)
+    q, k, v, g = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g))
+    v_hat = _forget_and_predict(S, np.exp(g), k)
+    S_tilde = S.copy()
+    e = float(beta) * (v - v_hat)
+    o = _write_and_read(S, k, e, q, scale)
+    return S, o, {"S_tilde": S_tilde, "v_hat": v_hat, "e": e}
 
 
 def _segments(Ttot: int, B: int, T: int, cu_seqlens: Optional[np.ndarray]):
@@ -91,17 +124,11 @@ def kda_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta
     and its causality can be pinned against a brute-force masked (QK^T)V.
     All heads advance together, one token at a time.
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    g = np.asarray(g, dtype=np.float64)
-    beta = np.asarray(beta, dtype=np.float64)
+    q, k, v, g, beta = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta))
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
-    qf = q.reshape(B * T, H, Dk)
-    kf = k.reshape(B * T, H, Dk)
+    qf, kf, gf = q.reshape(B * T, H, Dk), k.reshape(B * T, H, Dk), g.reshape(B * T, H, Dk)
     vf = v.reshape(B * T, H, Dv)
-    gf = g.reshape(B * T, H, Dk)
     bf = beta.reshape(B * T, H)
     segs = _segments(B * T, B, T, cu_seqlens)
     o = np.zeros((B * T, H, Dv))
@@ -110,13 +137,11 @@ def kda_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta
         S = np.zeros((H, Dk, Dv)) if h0 is None else np.array(h0[n], dtype=np.float64)
         for t in range(s, e_):
             if mode == "additive":
-                S = S + kf[t][:, :, None] * vf[t][:, None, :]
+                o[t] = _additive_write_and_read(S, kf[t], vf[t], qf[t], scale)
             else:
-                S = np.exp(gf[t])[:, :, None] * S                       # (1) forget
-                v_hat = np.einsum("hkv,hk->hv", S, kf[t])               # (2) predict
-                err = bf[t][:, None] * (vf[t] - v_hat)                  # (3) correct
-                S = S + kf[t][:, :, None] * err[:, None, :]             # (4) write
-            o[t] = np.einsum("hkv,hk->hv", S, scale * qf[t])            # (5) read
+                v_hat = _forget_and_predict(S, np.exp(gf[t]), kf[t])
+                err = bf[t][:, None] * (vf[t] - v_hat)
+                o[t] = _write_and_read(S, kf[t], err, qf[t], scale)
         ht[n] = S
     return o.reshape(B, T, H, Dv), ht
 
@@ -129,16 +154,11 @@ def kda_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta:
     Returns (o [N, H, Dv], new state). The decode step is the loop body of
     kda_forward applied once.
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    g = np.asarray(g, dtype=np.float64)
-    beta = np.asarray(beta, dtype=np.float64)
-    S = np.exp(g)[..., :, None] * np.asarray(state, dtype=np.float64)   # (1)
-    v_hat = np.einsum("nhkv,nhk->nhv", S, k)                            # (2)
-    err = beta[..., None] * (v - v_hat)                                 # (3)
-    S = S + k[..., :, None] * err[..., None, :]                         # (4)
-    o = np.einsum("nhkv,nhk->nhv", S, scale * q)                        # (5)
+    q, k, v, g, beta = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta))
+    S = np.array(state, dtype=np.float64)
+    v_hat = _forget_and_predict(S, np.exp(g), k)
+    err = beta[..., None] * (v - v_hat)
+    o = _write_and_read(S, k, err, q, scale)
     return o, S
 
 
@@ -149,15 +169,11 @@ def gdn_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta
 
     q, k: [B, T, H, Dk]; v: [B, T, H, Dv]; g, beta: [B, T, H] (g = log alpha, one
     scalar per token and head); h0, cu_seqlens and the returns as in kda_forward.
-    Per token, following zhilingong.com section 6: S_bar = alpha_t S, then the delta
-    rule on the decayed state, S = S_bar + k_t (beta_t (v_t - S_bar^T k_t))^T, and the
-    read o_t = S^T (scale q_t) of the updated state.
+    Per token, following zhilingong.com section 6: every row of the state decays by the
+    one gate alpha_t, then the delta rule acts on the decayed state (predict, beta-scaled
+    error, rank-one write) and the updated state is read with scale q_t.
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    g = np.asarray(g, dtype=np.float64)
-    beta = np.asarray(beta, dtype=np.float64)
+    q, k, v, g, beta = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta))
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     qf, kf, vf = q.reshape(B * T, H, Dk), k.reshape(B * T, H, Dk), v.reshape(B * T, H, Dv)
@@ -169,10 +185,10 @@ def gdn_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta
     for n, (s, e_) in enumerate(segs):
         S = np.zeros((H, Dk, Dv)) if h0 is None else np.array(h0[n], dtype=np.float64)
         for t in range(s, e_):
-            S_bar = af[t][:, None, None] * S                            # retention gate
-            err = bf[t][:, None] * (vf[t] - np.einsum("hkv,hk->hv", S_bar, kf[t]))
-            S = S_bar + kf[t][:, :, None] * err[:, None, :]             # delta rule
-            o[t] = np.einsum("hkv,hk->hv", S, scale * qf[t])            # read
+            alpha = np.repeat(af[t][:, None], Dk, axis=1)               # the same for every row
+            v_hat = _forget_and_predict(S, alpha, kf[t])
+            err = bf[t][:, None] * (vf[t] - v_hat)
+            o[t] = _write_and_read(S, kf[t], err, qf[t], scale)
         ht[n] = S
     return o.reshape(B, T, H, Dv), ht
 
@@ -181,15 +197,12 @@ def gdn_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta:
                state: np.ndarray, scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
     """One Gated DeltaNet step per (request, head): q, k [N, H, Dk]; v [N, H, Dv];
     g, beta [N, H]; state [N, H, Dk, Dv]. Returns (o [N, H, Dv], new state)."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    beta = np.asarray(beta, dtype=np.float64)
-    S_bar = np.exp(np.asarray(g, dtype=np.float64))[..., None, None] * np.asarray(
-        state, dtype=np.float64)
-    err = beta[..., None] * (v - np.einsum("nhkv,nhk->nhv", S_bar, k))
-    S = S_bar + k[..., :, None] * err[..., None, :]
-    return np.einsum("nhkv,nhk->nhv", S, scale * q), S
+    q, k, v, g, beta = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta))
+    S = np.array(state, dtype=np.float64)
+    alpha = np.repeat(np.exp(g)[..., None], S.shape[-2], axis=-1)
+    v_hat = _forget_and_predict(S, alpha, k)
+    err = beta[..., None] * (v - v_hat)
+    return _write_and_read(S, k, err, q, scale), S
 
 
 def gdn2_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, b: np.ndarray,
@@ -200,8 +213,9 @@ def gdn2_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, b: 
     q, k, g, b: [B, T, H, Dk] (b = erase gate per key channel); v, w: [B, T, H, Dv]
     (w = write gate per value channel); h0, cu_seqlens and the returns as in kda_forward.
     Per token, following jonahsamost.bearblog.dev, "Gated DeltaNet-2" (in the d_k x d_v
-    layout): S_bar = Diag(exp g_t) S; v^ = S_bar^T (b_t * k_t); S = S_bar + k_t (w_t * v_t - v^)^T;
-    then the read o_t = S^T (scale q_t) of the updated state.
+    layout): decay each key channel's row by exp(g_t[i]); read the old value through the
+    gated key, v^ = sum_i b_t[i] k_t[i] S~[i]; write the residual w_t * v_t - v^ at the
+    original key; then read the updated state with scale q_t.
     """
     q, k, v, g, b, w = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, b, w))
     B, T, H, Dk = q.shape
@@ -215,10 +229,8 @@ def gdn2_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, b: 
     for n, (s, e_) in enumerate(segs):
         S = np.zeros((H, Dk, Dv)) if h0 is None else np.array(h0[n], dtype=np.float64)
         for t in range(s, e_):
-            S_bar = np.exp(gf[t])[:, :, None] * S                          # decay
-            v_hat = np.einsum("hkv,hk->hv", S_bar, bf[t] * kf[t])          # gated-key read
-            S = S_bar + kf[t][:, :, None] * (wf[t] * vf[t] - v_hat)[:, None, :]
-            o[t] = np.einsum("hkv,hk->hv", S, scale * qf[t])               # read
+            v_hat = _forget_and_predict(S, np.exp(gf[t]), bf[t] * kf[t])
+            o[t] = _write_and_read(S, kf[t], wf[t] * vf[t] - v_hat, qf[t], scale)
         ht[n] = S
     return o.reshape(B, T, H, Dv), ht
 
@@ -229,10 +241,9 @@ def gdn2_decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, b: n
     """One Gated DeltaNet-2 step per (request, head): q, k, g, b [N, H, Dk]; v, w [N, H, Dv];
     state [N, H, Dk, Dv]. Returns (o [N, H, Dv], new state)."""
     q, k, v, g, b, w = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, b, w))
-    S_bar = np.exp(g)[..., :, None] * np.asarray(state, dtype=np.float64)
-    v_hat = np.einsum("nhkv,nhk->nhv", S_bar, b * k)
-    S = S_bar + k[..., :, None] * (w * v - v_hat)[..., None, :]
-    return np.einsum("nhkv,nhk->nhv", S, scale * q), S
+    S = np.array(state, dtype=np.float64)
+    v_hat = _forget_and_predict(S, np.exp(g), b * k)
+    return _write_and_read(S, k, w * v - v_hat, q, scale), S
 
 
 def prepare_inputs(q: np.ndarray, k: np.ndarray, a: np.ndarray, b: np.ndarray,

@@ -26,3 +26,67 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _nan_filled_outputs(request, monkeypatch):
+    """GPU tests get every output buffer pre-filled with NaN: an element a kernel fails to
+    write then shows up as a non-finite value in the parity check instead of passing on
+    whatever the allocator left there. Applies where a test lets the binding allocate o,
+    the final state or the prepared inputs."""
+    if "gpu" not in request.keywords:
+        return
+    import torch
+    import gated_delta_rule_channel_amd as kda
+
+    nan = float("nan")
+
+    def full(shape, dtype, device):
+        return torch.full(shape, nan, dtype=dtype, device=device)
+
+    def prefill(fn):
+        def w(*a, **kw):
+            q, v = a[0], a[2]
+            B, T, H, Dk = q.shape
+            Dv = v.shape[-1]
+            cu = kw.get("cu_seqlens")
+            N = (cu.numel() - 1) if cu is not None else B
+            if kw.get("out") is None:
+                kw["out"] = full((B, T, H, Dv), kw.get("out_dtype") or torch.float32, q.device)
+            if kw.get("output_final_state", True) and kw.get("final_state") is None:
+                kw["final_state"] = full((N, H, Dk, Dv), torch.float32, q.device)
+            return fn(*a, **kw)
+        return w
+
+    def decode(fn):
+        def w(*a, **kw):
+            q, v = a[0], a[2]
+            if kw.get("out") is None:
+                kw["out"] = full(q.shape[:2] + (v.shape[-1],), kw.get("out_dtype") or torch.float32,
+                                 q.device)
+            return fn(*a, **kw)
+        return w
+
+    def multi(fn):
+        def w(*a, **kw):
+            q, v = a[0], a[2]
+            if kw.get("out") is None:
+                kw["out"] = full(q.shape[:3] + (v.shape[-1],), kw.get("out_dtype") or torch.float32,
+                                 q.device)
+            return fn(*a, **kw)
+        return w
+
+    for name in ("fwd_chunked", "gdn_fwd_chunked", "gdn2_fwd_chunked"):
+        monkeypatch.setattr(kda, name, prefill(getattr(kda, name)))
+    for name in ("decode_step", "gdn_decode_step", "gdn2_decode_step"):
+        monkeypatch.setattr(kda, name, decode(getattr(kda, name)))
+    monkeypatch.setattr(kda, "decode_multi", multi(kda.decode_multi))
+
+    prep = kda.prepare_inputs
+
+    def prepare(q, k, a, b, scale=1.0, out=None):
+        if out is None:
+            out = (full(q.shape, q.dtype, q.device), full(k.shape, k.dtype, k.device),
+                   full(q.shape, torch.float32, q.device), full(b.shape, b.dtype, b.device))
+        return prep(q, k, a, b, scale=scale, out=out)
+    monkeypatch.setattr(kda, "prepare_inputs", prepare)

@@ -130,3 +130,22 @@ def test_alternating_state_order_gives_identical_results():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
     assert torch.equal(r1, r2) and torch.equal(p1, p2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_nan_in_one_state_stays_there(dtype):
+    """A NaN in one (request, head)'s inputs and another in one state element corrupt only
+    those two states and outputs; every other one matches the oracle."""
+    import dataclasses
+    w = dataclasses.replace(I.WORKLOADS[3], dtype=dtype, H=4, N=6)
+    x = I.decode_inputs(w)
+    x.k[2, 1, 3] = float("nan")
+    x.state[4, 2, 10, 20] = float("nan")
+    print(f"[decode] NaN in two states {dtype}", flush=True)
+    o_ref, S_ref = native.decode(x.q, x.k, x.v, x.g, x.beta, x.state)
+    o, S = _run(x, dtype)
+    ok = np.ones((w.N, w.H), dtype=bool)
+    ok[2, 1] = ok[4, 2] = False
+    check("o (other states)", o[ok], o_ref[ok], dtype)
+    check("state (other states)", S[ok], S_ref[ok], dtype)
+    assert not np.all(np.isfinite(o[2, 1])) and not np.all(np.isfinite(S[4, 2]))

@@ -244,3 +244,24 @@ def test_bf16_output_is_rounded_fp32_output(dtype):
     assert o16.dtype == torch.bfloat16
     assert torch.equal(o16, o32.to(torch.bfloat16))
     assert torch.equal(h16, h32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nan_in_one_head_stays_in_that_head(dtype):
+    """Heads are independent recurrences: a NaN in one head's inputs (a value, a gate and a
+    query element at different tokens) must leave every other head's o and final state
+    equal to the oracle's, and must not hide that head's own corruption."""
+    w = dataclasses.replace(I.WORKLOADS[2], T=300, H=8, dtype=dtype)
+    x = I.prefill_inputs(w)
+    bad = 3
+    x.v[0, 100, bad, 5] = float("nan")
+    x.g[0, 150, bad, 7] = float("nan")
+    x.q[0, 220, bad, 9] = float("nan")
+    print(f"[prefill] NaN in head {bad} {dtype}", flush=True)
+    o_ref, ht_ref = _ref(x)
+    o, ht = _gpu(x)
+    keep = [h for h in range(w.H) if h != bad]
+    check("o (other heads)", o[:, :, keep], o_ref[:, :, keep], dtype)
+    check("ht (other heads)", ht[:, keep], ht_ref[:, keep], dtype)
+    assert not np.all(np.isfinite(o[:, 100:, bad])), "the NaN head shows no corruption"
+    assert not np.all(np.isfinite(ht[:, bad]))
