@@ -44,7 +44,9 @@ KDA_DTYPE_BF16 = 1
 EXPORTED = ("kda_status_string", "kda_fwd_chunked_workspace_size", "kda_fwd_chunked",
             "kda_decode_step", "kda_gdn_fwd_chunked", "kda_gdn_decode_step",
             "kda_gdn2_fwd_chunked", "kda_gdn2_decode_step", "kda_decode_multi",
-            "kda_state_copy", "kda_prepare_inputs")
+            "kda_state_copy", "kda_prepare_inputs", "kda_fwd_chunked_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024     # KDA_NOALLOC_SCRATCH_BYTES of kda.h
 
 
 class KDAError(RuntimeError):
@@ -74,6 +76,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
         fn.restype = i
+    lib.kda_fwd_chunked_noalloc.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, vp, vp, i, i, i, i, i,
+                                            i, i, i, vp]
+    lib.kda_fwd_chunked_noalloc.restype = i
     for name in ("kda_decode_step", "kda_gdn_decode_step"):
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, i, i, i, i, i, i, vp]
@@ -233,6 +238,52 @@ def _fwd_chunked(scalar_gate, q, k, v, g, beta, scale, initial_state, output_fin
         code, ocode, _ptr(workspace), nbytes, _stream(q.device))
     if st != KDA_SUCCESS:
         raise KDAError(st, name)
+    return o, ht
+
+
+def fwd_chunked_noalloc(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
+                        output_final_state: bool = True, cu_seqlens=None, out=None,
+                        final_state=None, out_dtype=None):
+    """kda_fwd_chunked_noalloc: the chunked prefill on the library's built-in device scratch
+    (no workspace). Arguments and returns as fwd_chunked; o and ht are allocated here only
+    when not passed. Raises KDAError (KDA_ERROR_WORKSPACE) when the call needs more than
+    NOALLOC_SCRATCH_BYTES of workspace."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, g must be [B,T,H,Dk] and v [B,T,H,Dv]")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    code = _dtype_code(q)
+    _check_same_dtype(q, k=k, v=v, beta=beta)
+    _check_shape("beta", beta, (B, T, H))
+    varlen = cu_seqlens is not None
+    N = (cu_seqlens.numel() - 1) if varlen else B
+    _check_shape("k", k, (B, T, H, Dk))
+    _check_shape("g", g, (B, T, H, Dk))
+    _check_shape("v", v, (B, T, H, Dv))
+    _check_shape("initial_state", initial_state, (N, H, Dk, Dv))
+    _check_shape("out", out, (B, T, H, Dv))
+    _check_shape("final_state", final_state, (N, H, Dk, Dv))
+    if g.dtype != torch.float32:
+        raise TypeError("g must be float32")
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if varlen and (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1):
+        raise TypeError("cu_seqlens must be a 1-D int32 tensor")
+    _check_gpu(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    o = out if out is not None else torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
+    ht = None
+    if output_final_state:
+        ht = final_state if final_state is not None else torch.empty(
+            (N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    st = load_library().kda_fwd_chunked_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(initial_state),
+        _ptr(ht), _ptr(o), _ptr(cu_seqlens), int(N), int(B), int(T), int(H), int(Dk), int(Dv),
+        code, _dtype_code(o), _stream(q.device))
+    if st != KDA_SUCCESS:
+        raise KDAError(st, "kda_fwd_chunked_noalloc")
     return o, ht
 
 

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/kda.h"
 
 namespace kda {
@@ -120,6 +123,35 @@ kda_status decode_step(bool sg, const void* q, const void* k, const void* v, con
     return KDA_SUCCESS;
 }
 
+// ------------------------------------------------------------------------------------------
+// built-in scratch of kda_fwd_chunked_noalloc: one array per device, held until the process
+// ends. Host code never uses the array's name as an address (on the host it is a stand-in,
+// not device memory): the device address comes from hipGetSymbolAddress, once per device,
+// with that device current.
+// ------------------------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// device address of the current device's scratch array, or nullptr on failure
+void* scratch_of_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void* addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+        g_scratch_ptr[dev].store(addr, std::memory_order_release);
+        p = addr;
+    }
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,6 +186,24 @@ kda_status kda_fwd_chunked(const void* q, const void* k, const void* v, const fl
     if (!beta) return KDA_ERROR_INVALID_VALUE;
     return fwd_chunked(false, q, k, v, g, beta, nullptr, nullptr, scale, h0, ht, o, cu_seqlens,
                        num_seqs, B, T, H, Dk, Dv, dtype, o_dtype, workspace, workspace_bytes,
+                       stream);
+}
+
+kda_status kda_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                   const void* beta, float scale, const float* h0, float* ht,
+                                   void* o, const int32_t* cu_seqlens, int num_seqs, int B, int T,
+                                   int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
+                                   void* stream) {
+    if (!beta) return KDA_ERROR_INVALID_VALUE;
+    // the size check first: a call the scratch cannot hold is rejected before any device call
+    PrefillPlan p;
+    const kda_status st = plan_prefill(B, T, H, Dk, Dv, num_seqs, cu_seqlens != nullptr, dtype, &p);
+    if (st != KDA_SUCCESS) return st;
+    if (p.total > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERROR_WORKSPACE;
+    void* ws = scratch_of_current_device();
+    if (!ws) return KDA_ERROR_LAUNCH;
+    return fwd_chunked(false, q, k, v, g, beta, nullptr, nullptr, scale, h0, ht, o, cu_seqlens,
+                       num_seqs, B, T, H, Dk, Dv, dtype, o_dtype, ws, KDA_NOALLOC_SCRATCH_BYTES,
                        stream);
 }
 

@@ -135,6 +135,31 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
                            const void* beta, float scale, float* state, void* o, int N, int H,
                            int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype, void* stream);
 
+/* Size of the device scratch built into the library for kda_fwd_chunked_noalloc:
+ * 64 MiB on each device the library runs on, held until the process ends. */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+/* kda_fwd_chunked without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). The workspace is a fixed array of KDA_NOALLOC_SCRATCH_BYTES in the
+ * library's device memory, one per device; the call itself allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine). Its address is looked up once per
+ * device on the first call made with that device current.
+ *
+ * Every other argument, the results and the errors are those of kda_fwd_chunked, plus:
+ * KDA_ERROR_WORKSPACE when kda_fwd_chunked_workspace_size() for these sizes exceeds
+ * KDA_NOALLOC_SCRATCH_BYTES (about 680 chunk-heads of 64 tokens at d = 128 with bf16
+ * input, e.g. H = 16 and T = 2700); KDA_ERROR_LAUNCH if the scratch address cannot be
+ * obtained. All calls on one device share its scratch, and each call's results depend
+ * only on its own inputs (nothing in the scratch needs clearing between calls), but two
+ * calls whose execution overlaps on one device race on it: serialise them (one stream,
+ * or events between streams). */
+kda_status kda_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                   const void* beta, float scale, const float* h0, float* ht,
+                                   void* o, const int32_t* cu_seqlens, int num_seqs, int B, int T,
+                                   int H, int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
+                                   void* stream);
+
 /* Gated DeltaNet: the same recurrence with one scalar retention gate per
  * token and head instead of one per key channel. Step (1) becomes
  * S~ = exp(g_t) S, every row decaying alike; steps (2)-(5) are unchanged.

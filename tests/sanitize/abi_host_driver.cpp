@@ -230,6 +230,20 @@ int main() {
                                           nullptr),
           KDA_ERROR_NOT_SUPPORTED, 0);
 
+    // the allocation-free prefill: a call beyond the built-in scratch is refused before any
+    // device call; argument errors are those of kda_fwd_chunked
+    CHECK("noalloc too big", kda_fwd_chunked_noalloc(q, k, v, g, beta, 1.f, nullptr, nullptr, o,
+                                                     nullptr, 1, 1, 8192, 64, 128, 128, BF, F,
+                                                     nullptr),
+          KDA_ERROR_WORKSPACE, 0);
+    CHECK("noalloc null beta", kda_fwd_chunked_noalloc(q, k, v, g, nullptr, 1.f, nullptr, nullptr,
+                                                       o, nullptr, 1, 1, 64, 1, 16, 16, F, F,
+                                                       nullptr),
+          KDA_ERROR_INVALID_VALUE, 0);
+    CHECK("noalloc bad dims", kda_fwd_chunked_noalloc(q, k, v, g, beta, 1.f, nullptr, nullptr, o,
+                                                      nullptr, 1, 1, 64, 1, 24, 16, F, F, nullptr),
+          KDA_ERROR_INVALID_VALUE, 0);
+
     printf("%d checks, %d failures\n", g_checks, g_failures);
     return g_failures == 0 ? 0 : 1;
 }
