@@ -44,7 +44,8 @@ KDA_DTYPE_BF16 = 1
 EXPORTED = ("kda_status_string", "kda_fwd_chunked_workspace_size", "kda_fwd_chunked",
             "kda_decode_step", "kda_gdn_fwd_chunked", "kda_gdn_decode_step",
             "kda_gdn2_fwd_chunked", "kda_gdn2_decode_step", "kda_decode_multi",
-            "kda_state_copy", "kda_prepare_inputs", "kda_fwd_chunked_noalloc")
+            "kda_state_copy", "kda_prepare_inputs", "kda_fwd_chunked_noalloc",
+            "kda_fwd_chunked_raw")
 
 NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024     # KDA_NOALLOC_SCRATCH_BYTES of kda.h
 
@@ -72,7 +73,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_fwd_chunked_workspace_size.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
     lib.kda_fwd_chunked_workspace_size.restype = i
-    for name in ("kda_fwd_chunked", "kda_gdn_fwd_chunked"):
+    for name in ("kda_fwd_chunked", "kda_gdn_fwd_chunked", "kda_fwd_chunked_raw"):
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
         fn.restype = i
@@ -238,6 +239,54 @@ def _fwd_chunked(scalar_gate, q, k, v, g, beta, scale, initial_state, output_fin
         code, ocode, _ptr(workspace), nbytes, _stream(q.device))
     if st != KDA_SUCCESS:
         raise KDAError(st, name)
+    return o, ht
+
+
+def fwd_chunked_raw(q, k, v, a, b, scale: float = 1.0, initial_state=None,
+                    output_final_state: bool = True, cu_seqlens=None, workspace=None,
+                    out=None, final_state=None, out_dtype=None):
+    """Chunked prefill from the raw projections (kda_fwd_chunked_raw): q, k, a [B,T,H,128] and
+    v [B,T,H,128] bfloat16, b [B,T,H] bfloat16; q and k are normalised (q scaled by `scale`),
+    g = log sigmoid(a) and beta = sigmoid(b) inside the kernel. Other arguments and the
+    returns as fwd_chunked."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, a must be [B,T,H,Dk] and v [B,T,H,Dv]")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    code = _dtype_code(q)
+    _check_same_dtype(q, k=k, v=v, beta=b)
+    _check_same_dtype(q, a=a)
+    _check_shape("b", b, (B, T, H))
+    varlen = cu_seqlens is not None
+    N = (cu_seqlens.numel() - 1) if varlen else B
+    for name, t, shape in (("k", k, (B, T, H, Dk)), ("a", a, (B, T, H, Dk)),
+                           ("v", v, (B, T, H, Dv)), ("initial_state", initial_state, (N, H, Dk, Dv)),
+                           ("out", out, (B, T, H, Dv)), ("final_state", final_state, (N, H, Dk, Dv))):
+        _check_shape(name, t, shape)
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if varlen and (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1):
+        raise TypeError("cu_seqlens must be a 1-D int32 tensor")
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
+    _check_gpu(q, k, v, a, b, initial_state, cu_seqlens, workspace, out, final_state)
+    nbytes = workspace_size(B, T, H, Dk, Dv, N, varlen, code)
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    o = out if out is not None else torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
+    ht = None
+    if output_final_state:
+        ht = final_state if final_state is not None else torch.empty(
+            (N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    st = load_library().kda_fwd_chunked_raw(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), float(scale), _ptr(initial_state),
+        _ptr(ht), _ptr(o), _ptr(cu_seqlens), int(N), int(B), int(T), int(H), int(Dk), int(Dv),
+        code, _dtype_code(o), _ptr(workspace), nbytes, _stream(q.device))
+    if st != KDA_SUCCESS:
+        raise KDAError(st, "kda_fwd_chunked_raw")
     return o, ht
 
 

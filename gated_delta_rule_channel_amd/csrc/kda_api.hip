@@ -22,6 +22,11 @@ hipError_t launch_prefill(bool sg, bool bf16_in, bool bf16_out, int Dk, int Dv, 
                           float* ht, void* o, const int32_t* cu, int T, const void* tab,
                           const int32_t* seq_off, uint8_t* blocks, int N, int H, int max_slots,
                           hipStream_t s);
+hipError_t launch_prefill_raw(bool bf16_out, const void* q, const void* k, const void* v,
+                              const void* a, const void* b, float scale, const float* h0,
+                              float* ht, void* o, const int32_t* cu, int T, const void* tab,
+                              const int32_t* seq_off, uint8_t* blocks, int N, int H,
+                              int max_slots, hipStream_t s);
 size_t prefill_block_bytes(int Dk, int Dv, bool bf16_in);
 hipError_t launch_decode_multi(bool bf16_in, bool bf16_out, int Dk, int Dv, const void* q,
                                const void* k, const void* v, const float* g, const void* beta,
@@ -100,6 +105,43 @@ kda_status fwd_chunked(bool sg, const void* q, const void* k, const void* v, con
     if (kda::launch_prefill(sg, dtype == KDA_DTYPE_BF16, o_dtype == KDA_DTYPE_BF16, Dk, Dv, q, k,
                             v, g, beta, eb, ew, scale, h0, ht, o, cu_seqlens, T, tab, seq_off,
                             ws + p.blocks_off, p.nseq, H, (int)p.max_slots, s) != hipSuccess)
+        return KDA_ERROR_LAUNCH;
+    return KDA_SUCCESS;
+}
+
+// the raw-projection prefill: same checks and workspace as fwd_chunked
+kda_status fwd_chunked_raw(const void* q, const void* k, const void* v, const void* a,
+                           const void* b, float scale, const float* h0, float* ht, void* o,
+                           const int32_t* cu_seqlens, int num_seqs, int B, int T, int H, int Dk,
+                           int Dv, kda_dtype dtype, kda_dtype o_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !a || !b || !o) return KDA_ERROR_INVALID_VALUE;
+    if (!dtype_ok(o_dtype)) return KDA_ERROR_INVALID_VALUE;
+    PrefillPlan p;
+    const kda_status st = plan_prefill(B, T, H, Dk, Dv, num_seqs, cu_seqlens != nullptr, dtype, &p);
+    if (st != KDA_SUCCESS) return st;
+    if (dtype != KDA_DTYPE_BF16 || Dk != 128 || Dv != 128) return KDA_ERROR_NOT_SUPPORTED;
+    const void* ptrs[] = {q, k, v, a, o, h0, ht};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned(ptr, 16)) return KDA_ERROR_INVALID_VALUE;
+    if (!aligned(b, 2)) return KDA_ERROR_INVALID_VALUE;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERROR_INVALID_VALUE;
+    if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256))
+        return KDA_ERROR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    void* tab = nullptr;
+    int32_t* seq_off = nullptr;
+    if (cu_seqlens) {
+        tab = ws + p.tab_off;
+        seq_off = reinterpret_cast<int32_t*>(ws + p.seq_off);
+        if (kda::launch_chunk_map(cu_seqlens, p.nseq, T, (int)p.max_slots, tab, seq_off, s) !=
+            hipSuccess)
+            return KDA_ERROR_LAUNCH;
+    }
+    if (kda::launch_prefill_raw(o_dtype == KDA_DTYPE_BF16, q, k, v, a, b, scale, h0, ht, o,
+                                cu_seqlens, T, tab, seq_off, ws + p.blocks_off, p.nseq, H,
+                                (int)p.max_slots, s) != hipSuccess)
         return KDA_ERROR_LAUNCH;
     return KDA_SUCCESS;
 }
@@ -205,6 +247,15 @@ kda_status kda_fwd_chunked_noalloc(const void* q, const void* k, const void* v, 
     return fwd_chunked(false, q, k, v, g, beta, nullptr, nullptr, scale, h0, ht, o, cu_seqlens,
                        num_seqs, B, T, H, Dk, Dv, dtype, o_dtype, ws, KDA_NOALLOC_SCRATCH_BYTES,
                        stream);
+}
+
+kda_status kda_fwd_chunked_raw(const void* q, const void* k, const void* v, const void* a,
+                               const void* b, float scale, const float* h0, float* ht, void* o,
+                               const int32_t* cu_seqlens, int num_seqs, int B, int T, int H,
+                               int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    return fwd_chunked_raw(q, k, v, a, b, scale, h0, ht, o, cu_seqlens, num_seqs, B, T, H, Dk,
+                           Dv, dtype, o_dtype, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_gdn_fwd_chunked(const void* q, const void* k, const void* v, const float* g,

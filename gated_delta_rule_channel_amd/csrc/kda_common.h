@@ -50,6 +50,21 @@ template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// log(1 + y) for y in [0, 1]: a four-term series below 2^-6 (truncation below y^5 / 5, under
+// 2^-24 relative there), else the hardware log2 of 1 + y (its rounding of 1 + y costs at most
+// 2^-24 / y <= 2^-18 relative)
+__device__ __forceinline__ float log1p_unit(float y) {
+    if (y < 0.015625f) return y * (1.f - y * (0.5f - y * (1.f / 3.f - 0.25f * y)));
+    return __builtin_amdgcn_logf(1.f + y) * 0.69314718055994531f;
+}
+// log sigmoid(x) = -(max(-x, 0) + log(1 + e^-|x|)), without overflow
+__device__ __forceinline__ float log_sigmoid(float x) {
+    return -(fmaxf(-x, 0.f) + log1p_unit(fast_exp2(-fabsf(x) * kLog2e)));
+}
+__device__ __forceinline__ float sigmoid(float x) {
+    return 1.f / (1.f + fast_exp2(-x * kLog2e));
+}
+
 // ---- input / output element access (q, k, v, beta, o) -----------------------------------
 // Load 8 consecutive input elements as floats.
 __device__ __forceinline__ void load8f(float* d, const bf16* p) {

@@ -53,6 +53,36 @@ __device__ __forceinline__ void ld8(float* o, const float* p) {
     o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
 }
 
+// The next task's decay input of a lane, loaded while the current task finishes: g itself
+// (float32, 32 values), or in raw mode the gate logits a (bfloat16, 32 values in 16 words)
+template <bool RAW> struct GateBuf {
+    float v[32];
+    __device__ __forceinline__ void load(const void* p, size_t off, int st) {
+        load8f(&v[8 * st], reinterpret_cast<const float*>(p) + off);
+    }
+    __device__ __forceinline__ void zero(int st) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[8 * st + e] = 0.f;
+    }
+    __device__ __forceinline__ float log_decay(int i) const { return v[i]; }
+};
+template <> struct GateBuf<true> {
+    u32x4 w[4];
+    __device__ __forceinline__ void load(const void* p, size_t off, int st) {
+        w[st] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(p) + off);
+    }
+    // rows past the chunk's end: a = +inf, so that g = log sigmoid(a) = 0 (no decay) and the
+    // chunk-end decay exp(G_end) counts only the chunk's tokens
+    __device__ __forceinline__ void zero(int st) {
+        w[st] = u32x4{0x7f807f80u, 0x7f807f80u, 0x7f807f80u, 0x7f807f80u};
+    }
+    // g = log sigmoid(a)
+    __device__ __forceinline__ float log_decay(int i) const {
+        const unsigned x = w[i >> 3][(i & 7) >> 1];
+        return log_sigmoid(__uint_as_float((i & 1) ? (x & 0xffff0000u) : (x << 16)));
+    }
+};
+
 }  // namespace
 
 // Persistent workgroups of 4 waves, two per CU, over the (chunk, head) tasks with a stride of
@@ -66,9 +96,16 @@ __device__ __forceinline__ void ld8(float* o, const float* p) {
 // operand k exp(G) of every block handed over through LDS in transposed fragment layout.
 // The next task's k and q are staged in LDS during the W phase (direct-to-LDS loads) and its
 // g is loaded into registers while W and U run.
+//
+// RAW: the inputs are the raw projections of the input-preparation entry point (q and k not
+// normalised, gate logits a in place of g, write-strength logits b in place of beta), and
+// the normalisation q^ = scale q / |q|, k^ = k / |k| (norm over the 128 channels of the
+// row, which the four lanes of a row hold between them), g = log sigmoid(a) and
+// beta = sigmoid(b) are applied as the inputs are read.
+template <bool RAW>
 __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ g, const bf16* __restrict__ beta, float scale,
+    const void* __restrict__ gate, const bf16* __restrict__ beta, float scale,
     const int4* __restrict__ tab, int T, int nslots, uint8_t* __restrict__ ws, int H,
     long long beta_elems) {
     using Ly = FLy;
@@ -130,17 +167,16 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
                 lds_load4(reinterpret_cast<const unsigned*>(beta) + (e >> 1), sBetaRaw);
         }
     };
-    // g of this wave's rows of a task (32 values a lane: steps s, channels 32 s + 8 grp + e)
-    auto load_g = [&](float (&G)[32], int t0, int L, int h) {
+    // decay input of this wave's rows of a task (32 values a lane: steps s, channels
+    // 32 s + 8 grp + e)
+    auto load_g = [&](GateBuf<RAW>& G, int t0, int L, int h) {
         const int row = 16 * wave + m;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            if (row < L) {
-                load8f(&G[8 * st], g + (size_t)(t0 + row) * rowq + (size_t)h * FD + 32 * st + 8 * grp);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) G[8 * st + e] = 0.f;
-            }
+            if (row < L)
+                G.load(gate, (size_t)(t0 + row) * rowq + (size_t)h * FD + 32 * st + 8 * grp, st);
+            else
+                G.zero(st);
         }
     };
     FFrag Eid[2];
@@ -150,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
         for (int e = 0; e < 8; ++e) Eid[hh].set(e, (8 * grp + e == 16 * hh + m) ? 1.f : 0.f);
 
     bool staged = false;
-    float Gn[32];                                               // g of the next task
+    GateBuf<RAW> Gn;                                            // decay input, next task
 #pragma unroll 1
     for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
         const int slot = task / H, h = task % H;
@@ -183,12 +219,36 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
                 Q.zero(st);
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) G[8 * st + e] = Gn[8 * st + e] * kLog2e;
+            for (int e = 0; e < 8; ++e) G[8 * st + e] = Gn.log_decay(8 * st + e) * kLog2e;
         }
         if (tid < 64) {
             const size_t e = (size_t)(t0 + tid) * H + h;
             const unsigned w = sBetaRaw[tid];
-            sBeta[tid] = tid < L ? __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)) : 0.f;
+            const float bv = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+            sBeta[tid] = tid < L ? (RAW ? sigmoid(bv) : bv) : 0.f;
+        }
+        // row scales: k^ = rk k, scale q^ = rq q (raw mode: the norms over the row's 128
+        // channels, held by the four lanes m, m + 16, m + 32, m + 48; a zero row stays zero)
+        float rk = 1.f, rq = scale;
+        if constexpr (RAW) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                float kf[8], qf[8];
+                K.get8(st, kf);
+                Q.get8(st, qf);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sk += kf[e] * kf[e];
+                    sq += qf[e] * qf[e];
+                }
+            }
+            sk += __shfl_xor(sk, 16);
+            sk += __shfl_xor(sk, 32);
+            sq += __shfl_xor(sq, 16);
+            sq += __shfl_xor(sq, 32);
+            rk = sk > 0.f ? 1.f / sqrtf(sk) : 0.f;
+            rq = sq > 0.f ? scale / sqrtf(sq) : 0.f;
         }
         __syncthreads();                                        // staging region free
 
@@ -239,6 +299,8 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
             const int c0 = 32 * st + 8 * grp;
             float kf[8], pe[8], ib[8], kc[8];
             K.get8(st, kf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kf[e] *= rk;
             ld8(pe, &sFac[1][I][c0]);
             ld8(ib, &sFac[2][I][c0]);
             FFrag Kd;
@@ -283,6 +345,11 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
             float kf[8], qf[8], pr[8], ib[8], qd[8], kc[8];
             K.get8(st, kf);
             Q.get8(st, qf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kf[e] *= rk;
+                qf[e] *= rq;
+            }
             ld8(pr, &sFac[0][I][c0]);
             ld8(ib, &sFac[2][I][c0]);
             if (I < 3) {
@@ -298,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float f = fast_exp2(G[8 * st + e]);
-                const float sq = scale * qf[e] * f;
+                const float sq = qf[e] * f;
                 KR.set(e, bi * kf[e] * f);
                 QR.set(e, sq);
                 qd[e] = sq * pr[e];
@@ -339,9 +406,10 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
             const size_t off = (size_t)(t0 + (rv ? row : 0)) * rowq + (size_t)h * FD + 8 * grp;
             auto gl8 = [&](int st, float (&x)[8]) {           // prefix sums inside the block
                 if (rv) {
-                    load8f(x, g + off + 32 * st);
+                    GateBuf<RAW> gb;
+                    gb.load(gate, off + 32 * st, 0);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] *= kLog2e;
+                    for (int e = 0; e < 8; ++e) x[e] = gb.log_decay(e) * kLog2e;
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) x[e] = 0.f;
@@ -352,6 +420,11 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
                 if (rv) {
                     load8f(kf, k + off + 32 * st);
                     load8f(qf, q + off + 32 * st);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        kf[e] *= rk;
+                        qf[e] *= rq;
+                    }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) { kf[e] = 0.f; qf[e] = 0.f; }
@@ -377,7 +450,7 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
                         const float d = x[e] - row_bcast<7>(x[e]);
                         const float e1 = fast_exp2(d), e2 = fast_exp2(-d);
                         KE.set(e, bi * kf[e] * e1);
-                        QE.set(e, scale * qf[e] * e1);
+                        QE.set(e, qf[e] * e1);
                         KX.set(e, kf[e] * e2);
                     }
                     FPol::mma(dkk, KX, KE);
@@ -400,7 +473,7 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
                             const float kj = __shfl(kf[e], src);
                             const float d = jj <= m ? fast_exp2(x[e] - Gj) : 0.f;
                             skk += kf[e] * kj * d;
-                            sqk += scale * qf[e] * kj * d;
+                            sqk += qf[e] * kj * d;
                         }
                     }
                     skk += __shfl_xor(skk, 16);
@@ -522,6 +595,8 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
             K.get8(st, kf);
             FFrag xg;
 #pragma unroll
+            for (int e = 0; e < 8; ++e) kf[e] *= rk;
+#pragma unroll
             for (int e = 0; e < 8; ++e) xg.set(e, kf[e] * fast_exp2(G[8 * st + e]) * pr[e]);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) sX[I][2 * st + hh][lane] = FPol::transpose4(xg, Eid[hh]);
@@ -546,7 +621,7 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
             load_g(Gn, t0n, Ln, hn);
         } else {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) Gn[i] = 0.f;
+            for (int st = 0; st < 4; ++st) Gn.zero(st);
         }
 
         // ---- W = T' (k exp G) for this wave's 32 channels: the result lane (m = token, grp)
@@ -601,16 +676,24 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
 }
 
 // Launches the prep kernel above over nslots x H tasks (the workspace blocks start at
-// `blocks`); two workgroups per CU.
-hipError_t launch_prep_fast(const void* q, const void* k, const void* v, const float* g,
-                            const void* beta, float scale, const void* tab, int T, int nslots,
-                            uint8_t* blocks, int H, long long beta_elems, int cu_count,
-                            hipStream_t s) {
+// `blocks`); two workgroups per CU. raw: gate holds the logits a (bf16) and beta the logits
+// b, and q, k are normalised in the kernel; otherwise gate is g (float32).
+hipError_t launch_prep_fast(bool raw, const void* q, const void* k, const void* v,
+                            const void* gate, const void* beta, float scale, const void* tab,
+                            int T, int nslots, uint8_t* blocks, int H, long long beta_elems,
+                            int cu_count, hipStream_t s) {
     const long long ntasks = (long long)nslots * H;
     const long long grid = ntasks < 2LL * cu_count ? ntasks : 2LL * cu_count;
-    hipLaunchKernelGGL(prep_fast_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, g, (const bf16*)beta, scale,
-                       (const int4*)tab, T, nslots, blocks, H, beta_elems);
+    if (raw)
+        hipLaunchKernelGGL(prep_fast_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s,
+                           (const bf16*)q, (const bf16*)k, (const bf16*)v, gate,
+                           (const bf16*)beta, scale, (const int4*)tab, T, nslots, blocks, H,
+                           beta_elems);
+    else
+        hipLaunchKernelGGL(prep_fast_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s,
+                           (const bf16*)q, (const bf16*)k, (const bf16*)v, gate,
+                           (const bf16*)beta, scale, (const int4*)tab, T, nslots, blocks, H,
+                           beta_elems);
     return hipGetLastError();
 }
 

@@ -1142,10 +1142,10 @@ hipError_t launch_chunk_map(const int32_t* cu, int N, int T, int max_slots, void
     return hipGetLastError();
 }
 
-hipError_t launch_prep_fast(const void* q, const void* k, const void* v, const float* g,
-                            const void* beta, float scale, const void* tab, int T, int nslots,
-                            uint8_t* blocks, int H, long long beta_elems, int cu_count,
-                            hipStream_t s);
+hipError_t launch_prep_fast(bool raw, const void* q, const void* k, const void* v,
+                            const void* gate, const void* beta, float scale, const void* tab,
+                            int T, int nslots, uint8_t* blocks, int H, long long beta_elems,
+                            int cu_count, hipStream_t s);
 
 // compute units of the current device (the prep kernel keeps two workgroups on each)
 static hipError_t current_cu_count(int& n) {
@@ -1180,8 +1180,8 @@ static hipError_t launch_prefill_t(bool sg, const void* q, const void* k, const 
     const long long beta_elems = (cu ? (long long)T : (long long)N * T) * H;   // [tokens, H]
     constexpr bool kFastPrep = std::is_same<TI, bf16>::value && DK == 128 && DV == 128;
     if (kFastPrep && !eb && !sg)
-        ec = launch_prep_fast(q, k, v, g, beta, scale, tab, T, max_slots, blocks, H, beta_elems,
-                              cu_count, s);
+        ec = launch_prep_fast(false, q, k, v, g, beta, scale, tab, T, max_slots, blocks, H,
+                              beta_elems, cu_count, s);
     else if (eb)
         hipLaunchKernelGGL((prep_kernel<TI, DK, DV, false, true>), dim3((unsigned)grid), dim3(256),
                            0, s, tq, tk, tv, g, tb, (const TI*)eb, (const TI*)ew, scale,
@@ -1203,6 +1203,31 @@ static hipError_t launch_prefill_t(bool sg, const void* q, const void* k, const 
     const long long nblk = ((chains + 7) / 8) * 8 * VT;
     hipLaunchKernelGGL((state_kernel<TI, TO, DK, DV, BV>), dim3((unsigned)nblk), dim3(768), 0, s,
                        cu, T, seq_off, (const uint8_t*)blocks, h0, ht, (TO*)o, N, H);
+    return hipGetLastError();
+}
+
+// Prefill from the raw projections (bf16, d_k = d_v = 128): the prep kernel normalises q and
+// k and forms g = log sigmoid(a), beta = sigmoid(b) as it reads them; the state pass is the
+// usual one.
+hipError_t launch_prefill_raw(bool bf16_out, const void* q, const void* k, const void* v,
+                              const void* a, const void* b, float scale, const float* h0,
+                              float* ht, void* o, const int32_t* cu, int T, const void* tab,
+                              const int32_t* seq_off, uint8_t* blocks, int N, int H,
+                              int max_slots, hipStream_t s) {
+    int cu_count = 0;
+    hipError_t e = current_cu_count(cu_count);
+    if (e != hipSuccess) return e;
+    const long long beta_elems = (cu ? (long long)T : (long long)N * T) * H;
+    e = launch_prep_fast(true, q, k, v, a, b, scale, tab, T, max_slots, blocks, H, beta_elems,
+                         cu_count, s);
+    if (e != hipSuccess) return e;
+    const long long nblk = ((N * (long long)H + 7) / 8) * 8 * 4;
+    if (bf16_out)
+        hipLaunchKernelGGL((state_kernel<bf16, bf16, 128, 128, 32>), dim3((unsigned)nblk), dim3(768), 0,
+                           s, cu, T, seq_off, (const uint8_t*)blocks, h0, ht, (bf16*)o, N, H);
+    else
+        hipLaunchKernelGGL((state_kernel<bf16, float, 128, 128, 32>), dim3((unsigned)nblk), dim3(768), 0,
+                           s, cu, T, seq_off, (const uint8_t*)blocks, h0, ht, (float*)o, N, H);
     return hipGetLastError();
 }
 

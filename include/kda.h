@@ -135,6 +135,31 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
                            const void* beta, float scale, float* state, void* o, int N, int H,
                            int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype, void* stream);
 
+/* Chunked prefill from the raw projections: the input preparation of kda_prepare_inputs
+ * (q^ = scale q / |q|, k^ = k / |k| over the Dk channels of each row, g = log sigmoid(a),
+ * beta = sigmoid(b)) applied inside the prefill as the inputs are read, instead of as a
+ * separate pass that writes the prepared tensors to memory. The prepared values stay in
+ * float32 (they are not rounded to the input type), so results agree with kda_prepare_inputs
+ * followed by kda_fwd_chunked up to that rounding. Normalised queries and keys are those of
+ * "Notes on Linear Attention" (zhilingong.com), sections 4 and 5.3; the recurrence and its
+ * chunkwise evaluation are those of kda_fwd_chunked.
+ *
+ *  q, k   [B, T, H, Dk]  bfloat16      raw projections (a zero row stays zero)
+ *  v      [B, T, H, Dv]  bfloat16
+ *  a      [B, T, H, Dk]  bfloat16      gate logits: g = log sigmoid(a)
+ *  b      [B, T, H]      bfloat16      write-strength logits: beta = sigmoid(b)
+ *
+ * Every other argument, the workspace (sized by kda_fwd_chunked_workspace_size with
+ * KDA_DTYPE_BF16), the aliasing rules and the errors are those of kda_fwd_chunked, except
+ * that b needs only 2-byte alignment; KDA_ERROR_NOT_SUPPORTED unless dtype is
+ * KDA_DTYPE_BF16 and Dk = Dv = 128 (kda_prepare_inputs and kda_fwd_chunked cover the other
+ * cases). */
+kda_status kda_fwd_chunked_raw(const void* q, const void* k, const void* v, const void* a,
+                               const void* b, float scale, const float* h0, float* ht, void* o,
+                               const int32_t* cu_seqlens, int num_seqs, int B, int T, int H,
+                               int Dk, int Dv, kda_dtype dtype, kda_dtype o_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Size of the device scratch built into the library for kda_fwd_chunked_noalloc:
  * 64 MiB on each device the library runs on, held until the process ends. */
 #define KDA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)

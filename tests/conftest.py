@@ -76,7 +76,7 @@ def _nan_filled_outputs(request, monkeypatch):
             return fn(*a, **kw)
         return w
 
-    for name in ("fwd_chunked", "gdn_fwd_chunked", "gdn2_fwd_chunked"):
+    for name in ("fwd_chunked", "gdn_fwd_chunked", "gdn2_fwd_chunked", "fwd_chunked_raw"):
         monkeypatch.setattr(kda, name, prefill(getattr(kda, name)))
     for name in ("decode_step", "gdn_decode_step", "gdn2_decode_step"):
         monkeypatch.setattr(kda, name, decode(getattr(kda, name)))

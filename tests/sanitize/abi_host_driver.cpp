@@ -33,6 +33,13 @@ hipError_t launch_prefill(bool, bool, bool, int, int, const void*, const void*, 
     ++g_launches;
     return hipSuccess;
 }
+hipError_t launch_prefill_raw(bool, const void*, const void*, const void*, const void*,
+                              const void*, float, const float*, float*, void*, const int32_t*,
+                              int, const void*, const int32_t*, uint8_t*, int, int, int,
+                              hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
 // block size of the bf16 and fp32 layouts at d = 128 (any positive size exercises the
 // workspace checks the same way)
 size_t prefill_block_bytes(int Dk, int Dv, bool bf16_in) {
@@ -229,6 +236,29 @@ int main() {
     CHECK("prep huge", kda_prepare_inputs(q, k, v, beta, 1.f, o, o, st, o, 1LL << 40, 64, 16, F,
                                           nullptr),
           KDA_ERROR_NOT_SUPPORTED, 0);
+
+    // the raw-projection prefill: bf16 at d = 128 only
+    CHECK("raw ok", kda_fwd_chunked_raw(q, k, v, g, beta, 1.f, nullptr, nullptr, o, nullptr, 1, 1,
+                                        8192, 64, 128, 128, BF, F, ws, need, nullptr),
+          KDA_SUCCESS, 1);
+    CHECK("raw varlen ok", kda_fwd_chunked_raw(q, k, v, g, beta, 1.f, st, st, o, cu, 8, 1, 8192, 64,
+                                               128, 128, BF, BF, ws, need_var, nullptr),
+          KDA_SUCCESS, 2);
+    CHECK("raw f32", kda_fwd_chunked_raw(q, k, v, g, beta, 1.f, nullptr, nullptr, o, nullptr, 1, 1,
+                                         64, 1, 128, 128, F, F, ws, need, nullptr),
+          KDA_ERROR_NOT_SUPPORTED, 0);
+    CHECK("raw d64", kda_fwd_chunked_raw(q, k, v, g, beta, 1.f, nullptr, nullptr, o, nullptr, 1, 1,
+                                         64, 1, 64, 64, BF, F, ws, need, nullptr),
+          KDA_ERROR_NOT_SUPPORTED, 0);
+    CHECK("raw null a", kda_fwd_chunked_raw(q, k, v, nullptr, beta, 1.f, nullptr, nullptr, o,
+                                            nullptr, 1, 1, 64, 1, 128, 128, BF, F, ws, need, nullptr),
+          KDA_ERROR_INVALID_VALUE, 0);
+    CHECK("raw b odd", kda_fwd_chunked_raw(q, k, v, g, base + 1025, 1.f, nullptr, nullptr, o,
+                                           nullptr, 1, 1, 64, 1, 128, 128, BF, F, ws, need, nullptr),
+          KDA_ERROR_INVALID_VALUE, 0);
+    CHECK("raw small ws", kda_fwd_chunked_raw(q, k, v, g, beta, 1.f, nullptr, nullptr, o, nullptr,
+                                              1, 1, 8192, 64, 128, 128, BF, F, ws, need - 1, nullptr),
+          KDA_ERROR_WORKSPACE, 0);
 
     // the allocation-free prefill: a call beyond the built-in scratch is refused before any
     // device call; argument errors are those of kda_fwd_chunked

@@ -88,3 +88,51 @@ def test_prepared_inputs_feed_the_prefill():
                                    rs(cast(rb)))
     check("o", o.cpu().numpy(), o_ref, "bf16")
     check("ht", ht.cpu().numpy(), ht_ref, "bf16")
+
+
+def _raw_v(B, T, H, D, seed):
+    q, k, a, b = _raw(B * T, H, D, "bf16", seed)
+    v = torch.from_numpy(np.random.default_rng(seed + 1).standard_normal((B * T, H, D))).bfloat16()
+    rs = lambda t: t.reshape(B, T, *t.shape[1:]).contiguous()
+    return rs(q), rs(k), rs(v), rs(a), rs(b)
+
+
+def _raw_ref(q, k, v, a, b, scale, h0=None, cu=None):
+    """The oracle's float64 preparation, then its recurrence."""
+    rq, rk, rg, rb = kda_oracle.prepare_inputs(*(t.double().numpy() for t in (q, k, a, b)),
+                                               scale=scale)
+    f = lambda x: torch.from_numpy(x).float()
+    return native.prefill(f(rq), f(rk), v, f(rg), f(rb), h0=h0, cu_seqlens=cu)
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 300, 4), (2, 130, 3), (1, 64, 2)])
+def test_raw_prefill_matches_oracle(B, T, H):
+    """kda_fwd_chunked_raw (preparation inside the prefill) against the oracle's preparation
+    and recurrence, with a zero query row and saturated gate logits, ragged last chunks."""
+    D = 128
+    print(f"[inputs] raw prefill B{B} T{T} H{H}", flush=True)
+    q, k, v, a, b = _raw_v(B, T, H, D, 20 + T)
+    o, ht = kda.fwd_chunked_raw(*(t.to(DEV) for t in (q, k, v, a, b)), scale=D ** -0.5)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = _raw_ref(q, k, v, a, b, D ** -0.5)
+    check("o", o.cpu().numpy(), o_ref, "bf16")
+    check("ht", ht.cpu().numpy(), ht_ref, "bf16")
+
+
+def test_raw_prefill_packed_with_initial_state():
+    """Packed sequences (one empty) and an initial state through the raw entry point."""
+    D, H = 128, 3
+    lens = [70, 0, 129, 5]
+    T = sum(lens)
+    print("[inputs] raw prefill packed", flush=True)
+    q, k, v, a, b = _raw_v(1, T, H, D, 31)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    h0 = torch.from_numpy(0.1 * np.random.default_rng(32).standard_normal((len(lens), H, D, D))).float()
+    o, ht = kda.fwd_chunked_raw(*(t.to(DEV) for t in (q, k, v, a, b)), scale=0.1,
+                                initial_state=h0.to(DEV), cu_seqlens=cu.to(DEV))
+    torch.cuda.synchronize()
+    o_ref, ht_ref = _raw_ref(q, k, v, a, b, 0.1, h0=h0, cu=cu.numpy())
+    check("o", o.cpu().numpy(), o_ref, "bf16")
+    check("ht", ht.cpu().numpy(), ht_ref, "bf16")
+    np.testing.assert_array_equal(ht.cpu().numpy()[1], h0.numpy()[1])
+
