@@ -4,17 +4,22 @@
 // ("Module 03 - KDA I: The Delta-Rule Recurrence", jared-hpc.com, section 5).
 //
 // decode_multi_kernel: T consecutive tokens per request against the state in
-// slot slots[n] of a pool (one workgroup per (request, head)). The state is
-// read once, kept in registers across the T steps (each the recurrent step of
-// "Kimi Delta Attention (KDA)", "Two schedules for the same recurrence"), and
-// written once; optionally the state after every token is written to a
-// snapshot array, so that a caller verifying T drafted tokens can restore the
-// state after any accepted prefix. The work split is that of the single-step
-// decode kernel with at most 512 threads: a thread owns four value columns of
-// RPT rows; column sums go
-// through lane shuffles and LDS, double-buffered by token parity so that one
-// barrier per token suffices. The next token's inputs are loaded, unconverted,
-// while the current token is processed.
+// slot slots[n] of a pool. The state is read once, kept in registers across
+// the T steps (each the recurrent step of "Kimi Delta Attention (KDA)", "Two
+// schedules for the same recurrence"), and written once; optionally the state
+// after every token is written to a snapshot array, so that a caller verifying
+// T drafted tokens can restore the state after any accepted prefix.
+//
+// Column-sliced work split: in one step, value column c of S is forgotten,
+// predicted (v^_c = sum_r k_r S~_rc), corrected and written using only column
+// c and the per-row alpha, k and q, so the columns are independent for the
+// whole token loop. Each wavefront owns CW value columns over all DK rows
+// (lane (cq, rg): four columns, DK / RG consecutive rows) and runs every token
+// on them without a barrier: the column sums reduce across the row groups of
+// the wavefront with a DPP rotate and the permlane16/permlane32 swaps, which
+// give every lane of a column the same bits. The token inputs, shared by the
+// wavefronts of a state, are staged in LDS in groups of TG tokens, already as
+// alpha = exp(g), k, scale q, v and beta in fp32.
 //
 // state_copy_kernel: dst[dst_slots[i]] = src[src_slots[i]] for whole states,
 // 16-byte vector copies, one workgroup per (pair, 1024 float4 chunk).
@@ -24,179 +29,191 @@ namespace kda {
 
 int next_decode_order();                         // alternating state order (kda_decode.hip)
 
-template <int DK, int DV>
+template <typename TI, int DK, int DV>
 struct MultiShape {
-    static constexpr int CG = DV / 4;
-    static constexpr int NT0 = DK * DV / 16;
-    // at most 512 threads (8 rows each at d = 128), two workgroups per CU: the state and two
-    // tokens' inputs stay in registers across the token loop (at 128 x 128 the compiler
-    // spills 16-128 bytes a lane at this occupancy; one workgroup per CU without spills
-    // measured slower)
-    static constexpr int NT = NT0 < 64 ? 64 : (NT0 > 512 ? 512 : NT0);
-    static constexpr int RS = NT / CG;
-    static constexpr int RPT = DK / RS;
-    static constexpr int NW = NT / 64;
-    static_assert(NT % CG == 0 && DK % RS == 0 && RPT >= 1, "decode tiling");
+    static constexpr int CW = DV < 32 ? DV : 32;            // value columns per wavefront
+    static constexpr int CQ = CW / 4;                       // lanes per row (a float4 each)
+    static constexpr int RG = 64 / CQ;                      // row groups per wavefront
+    static constexpr int RPL = DK / RG;                     // consecutive rows per lane
+    static constexpr int RB = RPL < 4 ? RPL : 4;            // rows per LDS vector read
+    static constexpr int NW = DV / CW;                      // wavefronts per state
+    static constexpr int NT = 64 * NW;
+    static constexpr int TG = 8;                            // tokens per staged group
+    // staged token (bytes): g fp32 [DK], k, q [DK], v [DV] in the input type, as 16-byte pieces
+    static constexpr int SZ = (int)sizeof(TI);
+    static constexpr int OK = 4 * DK, OQ = OK + DK * SZ, OV = OQ + DK * SZ;
+    static constexpr int TOKB = OV + DV * SZ;
+    static constexpr int PIECES = TOKB / 16;
+    static_assert(RPL >= 1 && RPL * RG == DK && RPL % RB == 0 && TOKB % 16 == 0, "decode tiling");
 };
 
-// four consecutive input elements, loaded raw and converted at use
-template <typename TI> struct Raw4;
-template <> struct Raw4<float> {
-    float4 x;
-    __device__ __forceinline__ void load(const float* p) { x = *reinterpret_cast<const float4*>(p); }
-    __device__ __forceinline__ float4 get() const { return x; }
-};
-template <> struct Raw4<bf16> {
-    uint2 x;                                                 // two bfloat16 per word
-    __device__ __forceinline__ void load(const bf16* p) { x = *reinterpret_cast<const uint2*>(p); }
-    __device__ __forceinline__ float4 get() const {
-        return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
-                           __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
+// sum over the row groups of a wavefront (lane bits log2(CQ) .. 5); every lane of a column
+// gets the same bits (each stage adds a pair in an order both partners share)
+template <int CQ>
+__device__ __forceinline__ float rowgroup_sum(float x) {
+    if constexpr (CQ == 4) x += __shfl_xor(x, 4);
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// N consecutive staged values (fp32 or bf16) from LDS, as floats
+template <typename T, int N>
+__device__ __forceinline__ void lds_vals(float (&x)[N], const uint8_t* p) {
+    if constexpr (sizeof(T) == 4) {
+        if constexpr (N == 4) {
+            const float4 t = *reinterpret_cast<const float4*>(p);
+            x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+        } else if constexpr (N == 2) {
+            const float2 t = *reinterpret_cast<const float2*>(p);
+            x[0] = t.x; x[1] = t.y;
+        } else {
+            x[0] = *reinterpret_cast<const float*>(p);
+        }
+    } else {
+        if constexpr (N == 4) {
+            const u32x2 t = *reinterpret_cast<const u32x2*>(p);
+            x[0] = __uint_as_float(t[0] << 16); x[1] = __uint_as_float(t[0] & 0xffff0000u);
+            x[2] = __uint_as_float(t[1] << 16); x[3] = __uint_as_float(t[1] & 0xffff0000u);
+        } else if constexpr (N == 2) {
+            const unsigned t = *reinterpret_cast<const unsigned*>(p);
+            x[0] = __uint_as_float(t << 16); x[1] = __uint_as_float(t & 0xffff0000u);
+        } else {
+            x[0] = __uint_as_float((unsigned)*reinterpret_cast<const unsigned short*>(p) << 16);
+        }
     }
-};
+}
 
 template <typename TI, typename TO, int DK, int DV>
-__global__ __launch_bounds__(512, 4) void decode_multi_kernel(
+__global__ __launch_bounds__(256, 4) void decode_multi_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v,
     const float* __restrict__ g, const TI* __restrict__ beta, float scale,
     float* __restrict__ pool, const int32_t* __restrict__ slots, int num_slots,
     float* __restrict__ snapshots, TO* __restrict__ o, int T, int H, int reverse) {
-    using Sh = MultiShape<DK, DV>;
-    constexpr int CG = Sh::CG, RS = Sh::RS, RPT = Sh::RPT, NW = Sh::NW;
-    __shared__ float4 red_vh[2][NW][CG];
-    __shared__ float4 red_rq[2][NW][CG];
-    __shared__ float red_kq[2][NW];
+    using Sh = MultiShape<TI, DK, DV>;
+    constexpr int CW = Sh::CW, CQ = Sh::CQ, RPL = Sh::RPL, RB = Sh::RB, NT = Sh::NT;
+    constexpr int NW = Sh::NW, TG = Sh::TG, SZ = Sh::SZ, TOKB = Sh::TOKB, PIECES = Sh::PIECES;
+    constexpr int OK = Sh::OK, OQ = Sh::OQ, OV = Sh::OV;
+    // the staged pieces of a group, rounded up to whole 1 KB wavefront loads
+    constexpr int LOADS = (TG * PIECES + 64 * NW - 1) / (64 * NW);
+    __shared__ __attribute__((aligned(16))) uint8_t sIn[LOADS * NW * 1024];
+    __shared__ float sBeta[TG];
 
     // n * H + h, in the order of this call (alternating between calls, as the one-step decode)
     const int nh = reverse ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
     const int n = nh / H, h = nh % H;
     const int slot = slots ? slots[n] : n;
     if (slot < 0 || slot >= num_slots) return;   // uniform over the workgroup
-    const int tid = threadIdx.x;
-    const int cg = tid % CG;
-    const int rs = tid / CG;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cq = lane % CQ, rg = lane / CQ;
+    const int r0 = rg * RPL;                              // first row of this lane
+    const int c0 = CW * wave + 4 * cq;                    // first column of this lane
 
-    // inputs of the current token (c*) and of the next one (n*), raw
-    float cg_[RPT], ng_[RPT];
-    TI ck[RPT], cq[RPT], nk[RPT], nq[RPT], cb, nb;
-    Raw4<TI> cv, nv;
-    {
-        const size_t tok = (size_t)n * T * H + h;
-        const float* gb = g + tok * DK;                    // wave-uniform bases
-        const TI *kb = k + tok * DK, *qb = q + tok * DK;
+    // the inputs of tokens t0 .. t0 + tg - 1 to LDS, piece by piece straight from global
+    // memory (no registers); beta through a register
+    auto fill = [&](int t0, int tg) {
+        // the lane index through an opaque move, so that the per-lane piece addresses are
+        // formed here, on use, rather than hoisted out of the token loop into registers
+        int ln;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = rs + RS * i;
-            cg_[i] = gb[r];
-            ck[i] = kb[r];
-            cq[i] = qb[r];
-        }
-        cv.load(v + tok * DV + 4 * cg);
-        cb = beta[tok];
-    }
-    float* S = pool + ((size_t)slot * H + h) * DK * DV;
-    float4 s[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const floatx4 x = reinterpret_cast<const floatx4*>(S + (size_t)(rs + RS * i) * DV)[cg];
-        s[i] = make_float4(x[0], x[1], x[2], x[3]);
-    }
-#pragma unroll 1
-    for (int t = 0; t < T; ++t) {
-        const size_t tok = ((size_t)n * T + t) * H + h;     // token (n, t) of head h
-        if (t + 1 < T) {
-            const size_t tn = tok + H;                      // token (n, t + 1)
-            const float* gb = g + tn * DK;
-            const TI *kb = k + tn * DK, *qb = q + tn * DK;
-#pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const int r = rs + RS * i;
-                ng_[i] = gb[r];
-                nk[i] = kb[r];
-                nq[i] = qb[r];
+        for (int f = 0; f < LOADS; ++f) {
+            const int blk = f * NW + wave;                // this wavefront's 1 KB of LDS
+            const int c = blk * 64 + ln;                  // piece
+            if (c < tg * PIECES) {
+                const int tk = c / PIECES, b = (c % PIECES) * 16;
+                const size_t tok = ((size_t)n * T + t0 + tk) * H + h;
+                const void* src =
+                    b < OK   ? (const void*)(g + tok * DK + b / 4)
+                    : b < OQ ? (const void*)(k + tok * DK + (b - OK) / SZ)
+                    : b < OV ? (const void*)(q + tok * DK + (b - OQ) / SZ)
+                             : (const void*)(v + tok * DV + (b - OV) / SZ);
+                lds_load16(src, sIn + blk * 1024);
             }
-            nv.load(v + tn * DV + 4 * cg);
-            nb = beta[tn];
         }
-        asm volatile("" ::: "memory");                      // keep those loads issued here
-        const int b = t & 1;
-        float kr[RPT];
-        float4 vh = make_float4(0.f, 0.f, 0.f, 0.f), rq = vh;
-        float kq = 0.f;
+        if (tid < tg) sBeta[tid] = to_f(beta[((size_t)n * T + t0 + tid) * H + h]);
+    };
+
+    float* S = pool + ((size_t)slot * H + h) * DK * DV;
+    fill(0, T < TG ? T : TG);
+    floatx4 s[RPL];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const float a = fast_exp2(cg_[i] * kLog2e);
-            const float kk = to_f(ck[i]);
-            const float qq = scale * to_f(cq[i]);
-            kr[i] = kk;
-            s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;     // forget
-            vh.x += kk * s[i].x; vh.y += kk * s[i].y;                // predict
-            vh.z += kk * s[i].z; vh.w += kk * s[i].w;
-            rq.x += qq * s[i].x; rq.y += qq * s[i].y;                // read of the decayed state
-            rq.z += qq * s[i].z; rq.w += qq * s[i].w;
-            kq += kk * qq;
+    for (int i = 0; i < RPL; ++i)
+        s[i] = *reinterpret_cast<const floatx4*>(S + (size_t)(r0 + i) * DV + c0);
+    wait_all_memory();
+    __syncthreads();
+
+#pragma unroll 1
+    for (int t0 = 0; t0 < T; t0 += TG) {
+        const int tg = T - t0 < TG ? T - t0 : TG;
+        if (t0 > 0) {
+            __syncthreads();                              // every wavefront done with the group
+            fill(t0, tg);
+            wait_all_memory();
+            __syncthreads();
         }
+#pragma unroll 1
+        for (int u = 0; u < tg; ++u) {
+            const uint8_t* in = sIn + u * TOKB;
+            const int t = t0 + u;
+            floatx4 vh = {0.f, 0.f, 0.f, 0.f}, rq = vh;
+            float kq = 0.f;
 #pragma unroll
-        for (int m = CG; m < 64; m <<= 1) {
-            vh.x += __shfl_xor(vh.x, m); vh.y += __shfl_xor(vh.y, m);
-            vh.z += __shfl_xor(vh.z, m); vh.w += __shfl_xor(vh.w, m);
-            rq.x += __shfl_xor(rq.x, m); rq.y += __shfl_xor(rq.y, m);
-            rq.z += __shfl_xor(rq.z, m); rq.w += __shfl_xor(rq.w, m);
-            kq += __shfl_xor(kq, m);
-        }
-        if (lane < CG) {
-            red_vh[b][wave][lane] = vh;
-            red_rq[b][wave][lane] = rq;
-            if (lane == 0) red_kq[b][wave] = kq;
-        }
-        // the buffer of this token's parity was last read two tokens ago, before the
-        // previous token's barrier
-        __syncthreads();
-        vh = red_vh[b][0][cg];
-        rq = red_rq[b][0][cg];
-        kq = red_kq[b][0];
+            for (int jb = 0; jb < RPL; jb += RB) {
+                float a[RB], kk[RB], qq[RB];
+                lds_vals<float>(a, in + 4 * (r0 + jb));
+                lds_vals<TI>(kk, in + OK + SZ * (r0 + jb));
+                lds_vals<TI>(qq, in + OQ + SZ * (r0 + jb));
 #pragma unroll
-        for (int w = 1; w < NW; ++w) {
-            const float4 x = red_vh[b][w][cg], y = red_rq[b][w][cg];
-            vh.x += x.x; vh.y += x.y; vh.z += x.z; vh.w += x.w;
-            rq.x += y.x; rq.y += y.y; rq.z += y.z; rq.w += y.w;
-            kq += red_kq[b][w];
-        }
-        const float bt = to_f(cb);
-        const float4 vv = cv.get();
-        float4 e;                                                    // correct
-        e.x = bt * (vv.x - vh.x); e.y = bt * (vv.y - vh.y);
-        e.z = bt * (vv.z - vh.z); e.w = bt * (vv.w - vh.w);
-        floatx4* snap = snapshots ? reinterpret_cast<floatx4*>(
-                                        snapshots + (((size_t)n * T + t) * H + h) * DK * DV)
-                                  : nullptr;
+                for (int e = 0; e < RB; ++e) {
+                    floatx4& x = s[jb + e];
+                    const float qs = scale * qq[e];
+                    x *= fast_exp2(a[e] * kLog2e);                    // forget
+                    vh += kk[e] * x;                                  // predict
+                    rq += qs * x;                                     // read of S~
+                    kq += kk[e] * qs;
+                }
+                __builtin_amdgcn_sched_barrier(0);            // keep the row blocks in turn
+            }
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {                              // write
-            const int r = rs + RS * i;
-            s[i].x += kr[i] * e.x; s[i].y += kr[i] * e.y;
-            s[i].z += kr[i] * e.z; s[i].w += kr[i] * e.w;
-            if (snap)
-                __builtin_nontemporal_store(floatx4{s[i].x, s[i].y, s[i].z, s[i].w},
-                                            snap + (r * (DV / 4) + cg));
-        }
-        if (rs == 0)                                                 // read after the write
-            store4(o + tok * DV + 4 * cg, rq.x + kq * e.x, rq.y + kq * e.y, rq.z + kq * e.z,
-                   rq.w + kq * e.w);
+            for (int c = 0; c < 4; ++c) {
+                vh[c] = rowgroup_sum<CQ>(vh[c]);
+                rq[c] = rowgroup_sum<CQ>(rq[c]);
+            }
+            kq = rowgroup_sum<CQ>(kq);
+            float vv[4];
+            lds_vals<TI>(vv, in + OV + SZ * c0);
+            const float bt = sBeta[u];
+            const floatx4 e = bt * (floatx4{vv[0], vv[1], vv[2], vv[3]} - vh);   // correct
+            const size_t tok = ((size_t)n * T + t) * H + h;
+            float* snap = snapshots ? snapshots + tok * DK * DV : nullptr;
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            cg_[i] = ng_[i];
-            ck[i] = nk[i];
-            cq[i] = nq[i];
+            for (int jb = 0; jb < RPL; jb += RB) {                    // write
+                float kk[RB];
+                lds_vals<TI>(kk, in + OK + SZ * (r0 + jb));
+#pragma unroll
+                for (int i = 0; i < RB; ++i) {
+                    s[jb + i] += kk[i] * e;
+                    if (snap)
+                        __builtin_nontemporal_store(
+                            s[jb + i],
+                            reinterpret_cast<floatx4*>(snap + (size_t)(r0 + jb + i) * DV + c0));
+                }
+            }
+            if (rg == 0)                                              // read after the write
+                store4(o + tok * DV + c0, rq[0] + kq * e[0], rq[1] + kq * e[1],
+                       rq[2] + kq * e[2], rq[3] + kq * e[3]);
         }
-        cv = nv;
-        cb = nb;
     }
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-        __builtin_nontemporal_store(floatx4{s[i].x, s[i].y, s[i].z, s[i].w},
-                                    reinterpret_cast<floatx4*>(S + (size_t)(rs + RS * i) * DV) + cg);
+    for (int i = 0; i < RPL; ++i)
+        __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + (size_t)(r0 + i) * DV + c0));
 }
 
 // dst state dst_slots[i] <- src state src_slots[i]; a state is `words` float4 long
@@ -220,7 +237,7 @@ static hipError_t launch_multi_t(const void* q, const void* k, const void* v, co
                                  const int32_t* slots, int num_slots, float* snapshots, void* o,
                                  int N, int T, int H, hipStream_t s) {
     hipLaunchKernelGGL((decode_multi_kernel<TI, TO, DK, DV>),
-                       dim3((unsigned)((long long)N * H)), dim3(MultiShape<DK, DV>::NT), 0, s,
+                       dim3((unsigned)((long long)N * H)), dim3(MultiShape<TI, DK, DV>::NT), 0, s,
                        (const TI*)q, (const TI*)k, (const TI*)v, g, (const TI*)beta, scale,
                        pool, slots, num_slots, snapshots, (TO*)o, T, H, next_decode_order());
     return hipGetLastError();

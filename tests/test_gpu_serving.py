@@ -45,12 +45,15 @@ def _oracle_steps(q, k, v, g, beta, S0, scale=1.0, keep_all=True):
     return np.stack(outs, axis=1), np.stack(snaps, axis=1)
 
 
-@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, "bf16"), (64, 32, "f32"), (16, 128, "bf16"),
-                                         (128, 16, "f32")])
-def test_decode_multi_slots_and_snapshots(dk, dv, dtype):
+@pytest.mark.parametrize("dk,dv,dtype,T", [(128, 128, "bf16", 4), (64, 32, "f32", 4),
+                                           (16, 128, "bf16", 4), (128, 16, "f32", 4),
+                                           (128, 128, "bf16", 11), (32, 64, "f32", 17),
+                                           (16, 16, "bf16", 9)])
+def test_decode_multi_slots_and_snapshots(dk, dv, dtype, T):
+    """Token counts past one staged group of 8 (11, 17) and a ragged last group."""
     w = dataclasses.replace(I.WORKLOADS[3], Dk=dk, Dv=dv, dtype=dtype, H=3)
-    N, T, P = 5, 4, 9
-    print(f"[serving] decode_multi dk={dk} dv={dv} {dtype}", flush=True)
+    N, P = 5, 9
+    print(f"[serving] decode_multi dk={dk} dv={dv} {dtype} T={T}", flush=True)
     q, k, v, g, beta = _tokens(w, N, T)
     pool = _pool(w, P, 3, 11)
     slots = torch.tensor([7, 2, 0, 5, 3], dtype=torch.int32)
