@@ -35,6 +35,11 @@
 // each stored operand. A diagonal block whose decay exceeds 2^120 in some channel (ibd
 // beyond 2^120) takes the same fallbacks as the general kernel: the block's 8th row as
 // reference, else exact pairwise exponentials.
+//
+// Gated DeltaNet-2 ("From Fast Weight Programmers to KDA", section "Gated DeltaNet-2") runs
+// through the same kernel: an erase gate b per key channel replaces beta on the reading
+// side (the row operand of A_kk is b k fr and W's operand b k exp(G)), a write gate w per
+// value channel scales v (U = T (w v)), and T' = T.
 #include "kda_prefill_shared.h"
 
 namespace kda {
@@ -97,17 +102,20 @@ template <> struct GateBuf<true> {
 // The next task's k and q are staged in LDS during the W phase (direct-to-LDS loads) and its
 // g is loaded into registers while W and U run.
 //
-// RAW: the inputs are the raw projections of the input-preparation entry point (q and k not
-// normalised, gate logits a in place of g, write-strength logits b in place of beta), and
-// the normalisation q^ = scale q / |q|, k^ = k / |k| (norm over the 128 channels of the
-// row, which the four lanes of a row hold between them), g = log sigmoid(a) and
-// beta = sigmoid(b) are applied as the inputs are read.
-template <bool RAW>
+// MODE kPrepRaw: the inputs are the raw projections of the input-preparation entry point (q
+// and k not normalised, gate logits a in place of g, write-strength logits b in place of
+// beta), and the normalisation q^ = scale q / |q|, k^ = k / |k| (norm over the 128 channels
+// of the row, which the four lanes of a row hold between them), g = log sigmoid(a) and
+// beta = sigmoid(b) are applied as the inputs are read. MODE kPrepGates: Gated DeltaNet-2,
+// with the erase gates eb [tokens, H, 128] and write gates ew [tokens, H, 128] in place of
+// beta.
+template <int MODE>
 __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const void* __restrict__ gate, const bf16* __restrict__ beta, float scale,
-    const int4* __restrict__ tab, int T, int nslots, uint8_t* __restrict__ ws, int H,
-    long long beta_elems) {
+    const void* __restrict__ gate, const bf16* __restrict__ beta, const bf16* __restrict__ eb,
+    const bf16* __restrict__ ew, float scale, const int4* __restrict__ tab, int T, int nslots,
+    uint8_t* __restrict__ ws, int H, long long beta_elems) {
+    constexpr bool RAW = MODE == kPrepRaw, EW = MODE == kPrepGates;
     using Ly = FLy;
     // ---- LDS: one 64 KB region used in turn by the staged q, k (previous task), the A
     //      phase (A_kk, A_qk, factor table, column operands), T, and the W operand ----
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
             lds_load16(k + off, sR + kStgK + (wave * 4 + st) * 1024);
             lds_load16(q + off, sR + kStgQ + (wave * 4 + st) * 1024);
         }
-        if (st == 0 && wave == 0 && lane < L) {
+        if (!EW && st == 0 && wave == 0 && lane < L) {
             const size_t e = (size_t)(t0 + lane) * H + h;
             if ((e & 1) == 0 && (long long)e + 1 >= beta_elems)
                 sBetaRaw[lane] = reinterpret_cast<const unsigned short*>(beta)[e];
@@ -223,9 +231,20 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
         }
         if (tid < 64) {
             const size_t e = (size_t)(t0 + tid) * H + h;
-            const unsigned w = sBetaRaw[tid];
+            const unsigned w = EW ? 0u : sBetaRaw[tid];
             const float bv = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-            sBeta[tid] = tid < L ? (RAW ? sigmoid(bv) : bv) : 0.f;
+            sBeta[tid] = tid < L ? (EW ? 1.f : RAW ? sigmoid(bv) : bv) : 0.f;
+        }
+        // erase gates of this lane's row and channels (Gated DeltaNet-2)
+        In32<bf16> Eb;
+        if constexpr (EW) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                if (row < L)
+                    Eb.load(st, eb + (size_t)(t0 + row) * rowq + (size_t)h * FD + 32 * st + 8 * grp);
+                else
+                    Eb.zero(st);
+            }
         }
         // row scales: k^ = rk k, scale q^ = rq q (raw mode: the norms over the row's 128
         // channels, held by the four lanes m, m + 16, m + 32, m + 48; a zero row stays zero)
@@ -361,12 +380,19 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
                     kc[e] = kf[e] * fast_exp2(row_bcast<15>(x) - x);
                 }
             }
+            float br[8];                                        // beta, or the erase gates
+            if constexpr (EW) {
+                Eb.get8(st, br);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) br[e] = bi;
+            }
             FFrag KR, QR, KD;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float f = fast_exp2(G[8 * st + e]);
                 const float sq = qf[e] * f;
-                KR.set(e, bi * kf[e] * f);
+                KR.set(e, br[e] * kf[e] * f);
                 QR.set(e, sq);
                 qd[e] = sq * pr[e];
                 KD.set(e, kc[e] * ib[e]);
@@ -416,16 +442,21 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
                 }
                 row_scan8(x);
             };
-            auto kq8 = [&](int st, float (&kf)[8], float (&qf)[8]) {
+            // k, q, and the reading-side key br k (beta k, or the erase gates times k)
+            auto kq8 = [&](int st, float (&kf)[8], float (&qf)[8], float (&kb)[8]) {
                 if (rv) {
                     load8f(kf, k + off + 32 * st);
                     load8f(qf, q + off + 32 * st);
+                    if constexpr (EW) load8f(kb, eb + off + 32 * st);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         kf[e] *= rk;
                         qf[e] *= rq;
+                        kb[e] = (EW ? kb[e] : bi) * kf[e];
                     }
                 } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kb[e] = 0.f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) { kf[e] = 0.f; qf[e] = 0.f; }
                 }
@@ -441,15 +472,15 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
             if (!__any(bad)) {
 #pragma unroll 1
                 for (int st = 0; st < 4; ++st) {
-                    float x[8], kf[8], qf[8];
+                    float x[8], kf[8], qf[8], kb[8];
                     gl8(st, x);
-                    kq8(st, kf, qf);
+                    kq8(st, kf, qf, kb);
                     FFrag KE, QE, KX;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float d = x[e] - row_bcast<7>(x[e]);
                         const float e1 = fast_exp2(d), e2 = fast_exp2(-d);
-                        KE.set(e, bi * kf[e] * e1);
+                        KE.set(e, kb[e] * e1);
                         QE.set(e, qf[e] * e1);
                         KX.set(e, kf[e] * e2);
                     }
@@ -464,15 +495,15 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
                     const int src = (lane & 48) | jj;
 #pragma unroll 1
                     for (int st = 0; st < 4; ++st) {
-                        float x[8], kf[8], qf[8];
+                        float x[8], kf[8], qf[8], kb[8];
                         gl8(st, x);
-                        kq8(st, kf, qf);
+                        kq8(st, kf, qf, kb);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const float Gj = __shfl(x[e], src);
                             const float kj = __shfl(kf[e], src);
                             const float d = jj <= m ? fast_exp2(x[e] - Gj) : 0.f;
-                            skk += kf[e] * kj * d;
+                            skk += kb[e] * kj * d;
                             sqk += qf[e] * kj * d;
                         }
                     }
@@ -483,7 +514,7 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
                     if ((jj >> 2) == grp) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            if (r == (jj & 3)) { dkk[r] = bi * skk; dqk[r] = sqk; }
+                            if (r == (jj & 3)) { dkk[r] = skk; dqk[r] = sqk; }
                     }
                 }
             }
@@ -509,13 +540,16 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
 
         // ---- value slice of this wave (for U), loaded now so it lands during the inverse ----
         const int vc0 = 32 * wave + 8 * grp;
-        In32<bf16> V;
+        In32<bf16> V, Wg;                                       // v, and the write gates
 #pragma unroll
         for (int I2 = 0; I2 < 4; ++I2) {
-            if (16 * I2 + m < L)
+            if (16 * I2 + m < L) {
                 V.load(I2, v + (size_t)(t0 + 16 * I2 + m) * rowq + (size_t)h * FD + vc0);
-            else
+                if constexpr (EW) Wg.load(I2, ew + (size_t)(t0 + 16 * I2 + m) * rowq + (size_t)h * FD + vc0);
+            } else {
                 V.zero(I2);
+                if constexpr (EW) Wg.zero(I2);
+            }
         }
         // A_qk fragment tiles of token tile tw = wave (upper blocks zero)
 #pragma unroll
@@ -596,6 +630,12 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
             FFrag xg;
 #pragma unroll
             for (int e = 0; e < 8; ++e) kf[e] *= rk;
+            if constexpr (EW) {
+                float ebv[8];
+                Eb.get8(st, ebv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kf[e] *= ebv[e];
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) xg.set(e, kf[e] * fast_exp2(G[8 * st + e]) * pr[e]);
 #pragma unroll
@@ -659,12 +699,28 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
                 FFrag vb;
-                V.frag(J, vb);
                 floatx4 t = {0.f, 0.f, 0.f, 0.f};
-                FPol::mma_copy(t, vb, Eid[hh]);
+                if constexpr (EW) {
+                    // w v is not exact in one bfloat16: the transpose and the product take
+                    // both parts
+                    float vv[8], wv[8];
+                    V.get8(J, vv);
+                    Wg.get8(J, wv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vb.set(e, vv[e] * wv[e]);
+                    FPol::mma_exact(t, vb, Eid[hh]);
+                } else {
+                    V.frag(J, vb);
+                    FPol::mma_copy(t, vb, Eid[hh]);
+                }
                 const FFrag4 b = frag4_of<FPol>(t);
 #pragma unroll
-                for (int I2 = J; I2 < 4; ++I2) FPol::mma16_exact(accU[I2], sTp[tri_tile(I2, J)][lane], b);
+                for (int I2 = J; I2 < 4; ++I2) {
+                    if constexpr (EW)
+                        FPol::mma16(accU[I2], sTp[tri_tile(I2, J)][lane], b);
+                    else
+                        FPol::mma16_exact(accU[I2], sTp[tri_tile(I2, J)][lane], b);
+                }
             }
 #pragma unroll
             for (int I2 = 0; I2 < 4; ++I2)
@@ -676,24 +732,27 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
 }
 
 // Launches the prep kernel above over nslots x H tasks (the workspace blocks start at
-// `blocks`); two workgroups per CU. raw: gate holds the logits a (bf16) and beta the logits
-// b, and q, k are normalised in the kernel; otherwise gate is g (float32).
-hipError_t launch_prep_fast(bool raw, const void* q, const void* k, const void* v,
-                            const void* gate, const void* beta, float scale, const void* tab,
-                            int T, int nslots, uint8_t* blocks, int H, long long beta_elems,
-                            int cu_count, hipStream_t s) {
+// `blocks`); two workgroups per CU. kPrepRaw: gate holds the logits a (bf16) and beta the
+// logits b, and q, k are normalised in the kernel; otherwise gate is g (float32).
+// kPrepGates: eb and ew hold the erase and write gates, beta is unused.
+hipError_t launch_prep_fast(int mode, const void* q, const void* k, const void* v,
+                            const void* gate, const void* beta, const void* eb, const void* ew,
+                            float scale, const void* tab, int T, int nslots, uint8_t* blocks,
+                            int H, long long beta_elems, int cu_count, hipStream_t s) {
     const long long ntasks = (long long)nslots * H;
     const long long grid = ntasks < 2LL * cu_count ? ntasks : 2LL * cu_count;
-    if (raw)
-        hipLaunchKernelGGL(prep_fast_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s,
-                           (const bf16*)q, (const bf16*)k, (const bf16*)v, gate,
-                           (const bf16*)beta, scale, (const int4*)tab, T, nslots, blocks, H,
-                           beta_elems);
+#define KDA_PREP_FAST(M)                                                                     \
+    hipLaunchKernelGGL(prep_fast_kernel<M>, dim3((unsigned)grid), dim3(256), 0, s,            \
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, gate, (const bf16*)beta, \
+                       (const bf16*)eb, (const bf16*)ew, scale, (const int4*)tab, T, nslots, \
+                       blocks, H, beta_elems)
+    if (mode == kPrepRaw)
+        KDA_PREP_FAST(kPrepRaw);
+    else if (mode == kPrepGates)
+        KDA_PREP_FAST(kPrepGates);
     else
-        hipLaunchKernelGGL(prep_fast_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s,
-                           (const bf16*)q, (const bf16*)k, (const bf16*)v, gate,
-                           (const bf16*)beta, scale, (const int4*)tab, T, nslots, blocks, H,
-                           beta_elems);
+        KDA_PREP_FAST(kPrepPlain);
+#undef KDA_PREP_FAST
     return hipGetLastError();
 }
 

@@ -1142,10 +1142,10 @@ hipError_t launch_chunk_map(const int32_t* cu, int N, int T, int max_slots, void
     return hipGetLastError();
 }
 
-hipError_t launch_prep_fast(bool raw, const void* q, const void* k, const void* v,
-                            const void* gate, const void* beta, float scale, const void* tab,
-                            int T, int nslots, uint8_t* blocks, int H, long long beta_elems,
-                            int cu_count, hipStream_t s);
+hipError_t launch_prep_fast(int mode, const void* q, const void* k, const void* v,
+                            const void* gate, const void* beta, const void* eb, const void* ew,
+                            float scale, const void* tab, int T, int nslots, uint8_t* blocks,
+                            int H, long long beta_elems, int cu_count, hipStream_t s);
 
 // compute units of the current device (the prep kernel keeps two workgroups on each)
 static hipError_t current_cu_count(int& n) {
@@ -1179,9 +1179,9 @@ static hipError_t launch_prefill_t(bool sg, const void* q, const void* k, const 
     const TI *tq = (const TI*)q, *tk = (const TI*)k, *tv = (const TI*)v, *tb = (const TI*)beta;
     const long long beta_elems = (cu ? (long long)T : (long long)N * T) * H;   // [tokens, H]
     constexpr bool kFastPrep = std::is_same<TI, bf16>::value && DK == 128 && DV == 128;
-    if (kFastPrep && !eb && !sg)
-        ec = launch_prep_fast(false, q, k, v, g, beta, scale, tab, T, max_slots, blocks, H,
-                              beta_elems, cu_count, s);
+    if (kFastPrep && !sg)
+        ec = launch_prep_fast(eb ? kPrepGates : kPrepPlain, q, k, v, g, beta, eb, ew, scale, tab,
+                              T, max_slots, blocks, H, beta_elems, cu_count, s);
     else if (eb)
         hipLaunchKernelGGL((prep_kernel<TI, DK, DV, false, true>), dim3((unsigned)grid), dim3(256),
                            0, s, tq, tk, tv, g, tb, (const TI*)eb, (const TI*)ew, scale,
@@ -1218,8 +1218,8 @@ hipError_t launch_prefill_raw(bool bf16_out, const void* q, const void* k, const
     hipError_t e = current_cu_count(cu_count);
     if (e != hipSuccess) return e;
     const long long beta_elems = (cu ? (long long)T : (long long)N * T) * H;
-    e = launch_prep_fast(true, q, k, v, a, b, scale, tab, T, max_slots, blocks, H, beta_elems,
-                         cu_count, s);
+    e = launch_prep_fast(kPrepRaw, q, k, v, a, b, nullptr, nullptr, scale, tab, T, max_slots,
+                         blocks, H, beta_elems, cu_count, s);
     if (e != hipSuccess) return e;
     const long long nblk = ((N * (long long)H + 7) / 8) * 8 * 4;
     if (bf16_out)

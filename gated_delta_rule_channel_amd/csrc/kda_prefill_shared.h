@@ -59,6 +59,10 @@ using WsLayoutOf = WsLayout<Pol::kPairBytes, Pol::kUTileBytes, Pol::kPairNBytes,
 
 __host__ __device__ constexpr int tri_tile(int I, int J) { return I * (I + 1) / 2 + J; }
 
+// input variants of the bf16, d = 128 prep kernel: prepared inputs (KDA), raw projections
+// (normalised and gated in the kernel), and Gated DeltaNet-2's erase and write gates
+enum PrepMode : int { kPrepPlain = 0, kPrepRaw = 1, kPrepGates = 2 };
+
 // Keeps the compiler from sinking prefetch loads to their first use: loads issued before
 // this point stay before it, so they are in flight while the following code runs.
 __device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }

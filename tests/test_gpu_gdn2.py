@@ -54,30 +54,32 @@ def test_gdn2_main_size_full():
     _compare(*I.gdn2_prefill_inputs(w_), w_.dtype)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_gdn2_varlen_edges(dtype):
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_gdn2_varlen_edges(dtype, d):
     """Packed sequences with empty, one-token, exact-chunk and ragged lengths, with h0."""
-    w_ = dataclasses.replace(I.WORKLOADS[4], H=3, Dk=64, Dv=32, dtype=dtype, h0=True)
+    w_ = dataclasses.replace(I.WORKLOADS[4], H=3, Dk=d, Dv=d // 2 if d == 64 else d,
+                             dtype=dtype, h0=True)
     x, b, w = I.gdn2_prefill_inputs(w_, lengths=[0, 1, 64, 130, 0, 63, 200])
-    print(f"[gdn2] varlen edges {dtype}", flush=True)
+    print(f"[gdn2] varlen edges {dtype} d{d}", flush=True)
     _, ht = _compare(x, b, w, dtype, scale=0.8)
     np.testing.assert_array_equal(ht[0], x.h0[0].numpy())
     np.testing.assert_array_equal(ht[4], x.h0[4].numpy())
 
 
 @pytest.mark.parametrize("B,T,H,Dk,Dv,dtype", [(2, 77, 2, 16, 128, "f32"), (1, 250, 3, 128, 16, "bf16"),
-                                               (3, 129, 1, 32, 64, "bf16"), (1, 1, 2, 64, 64, "f32")])
+                                               (3, 129, 1, 32, 64, "bf16"), (1, 1, 2, 64, 64, "f32"),
+                                               (2, 100, 3, 128, 128, "bf16")])
 def test_gdn2_ragged_shapes(B, T, H, Dk, Dv, dtype):
     w_ = dataclasses.replace(I.WORKLOADS[1], B=B, T=T, H=H, Dk=Dk, Dv=Dv, dtype=dtype)
     print(f"[gdn2] B{B} T{T} H{H} {Dk}x{Dv} {dtype}", flush=True)
     _compare(*I.gdn2_prefill_inputs(w_), dtype)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_gdn2_steep_decay_pairwise_path(dtype):
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_gdn2_steep_decay_pairwise_path(dtype, d):
     """Log-decays of -30 .. -80 in some channels send blocks through the pairwise path,
     where the erase gate enters the exact pair sums."""
-    w_ = dataclasses.replace(I.WORKLOADS[1], B=1, T=192, H=2, Dk=64, Dv=64, dtype=dtype)
+    w_ = dataclasses.replace(I.WORKLOADS[1], B=1, T=192, H=2, Dk=d, Dv=d, dtype=dtype)
     x, b, w = I.gdn2_prefill_inputs(w_)
     g = x.g.clone()
     rng = np.random.default_rng(2468)
