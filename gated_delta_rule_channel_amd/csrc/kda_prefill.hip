@@ -898,6 +898,7 @@ __global__ __launch_bounds__(768) void state_kernel(
         // empty sequence: the state passes through
     } else if (role == 0) {
         // ---- E role: E = U - W S (phase A); loads and decodes W and U (phase B) ----
+        __builtin_amdgcn_s_setprio(2);             // on the serial chain: issue before the O role
         struct Raw {
             typename Pol::PairN w[NP];
             typename Pol::URaw u[NVT];
@@ -960,6 +961,7 @@ __global__ __launch_bounds__(768) void state_kernel(
         }
         if (c < c_end) chunk(c, R0, R1);
     } else if (role == 1) {
+        __builtin_amdgcn_s_setprio(2);             // on the serial chain: issue before the O role
         // ---- S role: S' = Diag(exp G_end) S + Kd^T E. exp(G_end) (Dk floats) is fetched by
         //      the first S-role wave alone and shared through LDS ----
         struct Raw {
