@@ -126,9 +126,12 @@ def _pmc_per_kernel(path, counter):
 def _short(name):
     """Kernel of the KDA path a counter row belongs to; the Gated DeltaNet and Gated
     DeltaNet-2 instantiations (a true gate flag among the template arguments, "Lb1E" in a
-    mangled name) are not counted."""
+    mangled name) and the raw-input and gated modes of the bf16 prep kernel (mode 1, 2) are
+    not counted."""
     if re.search(r"\btrue\b|Lb1E", name):
         return None
+    if "prep_fast_kernel" in name:
+        return "prep_kernel" if re.search(r"prep_fast_kernel<0>|prep_fast_kernelILi0E", name) else None
     for key in ("prep_kernel", "state_kernel", "chunk_map_kernel", "decode_kernel"):
         if key in name:
             return key

@@ -80,7 +80,13 @@ def test_traffic_summary_calibration(tmp_path):
               {"Dispatch_Id": 6, "Kernel_Name": "_ZN3kda11prep_kernelIDF16bLi128ELi128ELb0ELb1EEEvPKT_",
                "Counter_Name": "FETCH_SIZE", "Counter_Value": 5.0e6},
               {"Dispatch_Id": 7, "Kernel_Name": "void kda::decode_kernel<__bf16, float, 128, 128, false, true>(...)",
-               "Counter_Name": "FETCH_SIZE", "Counter_Value": 3.0e6}]
+               "Counter_Name": "FETCH_SIZE", "Counter_Value": 3.0e6},
+              # the raw-input and gated modes of the bf16 prep kernel
+              {"Dispatch_Id": 8, "Kernel_Name": "void kda::prep_fast_kernel<1>(...)",
+               "Counter_Name": "FETCH_SIZE", "Counter_Value": 2.0e6},
+              {"Dispatch_Id": 9, "Kernel_Name": "void kda::prep_fast_kernel<2>(...)",
+               "Counter_Name": "FETCH_SIZE", "Counter_Value": 2.0e6}]
+
     _write_csv(tmp_path / "f.csv", fetch)
     _write_csv(tmp_path / "w.csv", write)
     out_file = str(tmp_path / "traffic.json")
@@ -108,3 +114,14 @@ def test_traffic_summary_calibration(tmp_path):
 
 def test_code_hash_ignores_python_comments():
     assert bench._code_only("x = 1  # one\n# two\n", python=True) == bench._code_only("x = 1", python=True)
+
+
+def test_kernel_names_of_the_kda_figures():
+    """The bf16 prep kernel's KDA mode counts as the prep kernel (demangled or mangled); its
+    raw-input and gated modes and the gate variants of the other kernels do not."""
+    assert bench._short("void kda::prep_fast_kernel<0>(bf16 const*, ...)") == "prep_kernel"
+    assert bench._short("_ZN3kda16prep_fast_kernelILi0EEEvPKDF16b") == "prep_kernel"
+    assert bench._short("void kda::prep_fast_kernel<1>(bf16 const*, ...)") is None
+    assert bench._short("_ZN3kda16prep_fast_kernelILi2EEEvPKDF16b") is None
+    assert bench._short("void kda::state_kernel<bf16, float, 128, 128, 32>(...)") == "state_kernel"
+    assert bench._short("void kda::decode_kernel<bf16, float, 128, 128, true, false>(...)") is None
