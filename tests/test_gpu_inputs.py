@@ -136,3 +136,16 @@ def test_raw_prefill_packed_with_initial_state():
     check("ht", ht.cpu().numpy(), ht_ref, "bf16")
     np.testing.assert_array_equal(ht.cpu().numpy()[1], h0.numpy()[1])
 
+
+
+def test_raw_prefill_zero_scale_reads_nothing():
+    """scale = 0 zeroes every query after normalisation: o is exactly 0, while the state
+    (which never sees q) still matches the oracle."""
+    B, T, H, D = 1, 150, 2, 128
+    print("[inputs] raw prefill scale 0", flush=True)
+    q, k, v, a, b = _raw_v(B, T, H, D, 51)
+    o, ht = kda.fwd_chunked_raw(*(t.to(DEV) for t in (q, k, v, a, b)), scale=0.0)
+    torch.cuda.synchronize()
+    _, ht_ref = _raw_ref(q, k, v, a, b, 1.0)
+    assert torch.all(o == 0)
+    check("ht", ht.cpu().numpy(), ht_ref, "bf16")

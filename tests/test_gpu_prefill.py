@@ -265,3 +265,21 @@ def test_nan_in_one_head_stays_in_that_head(dtype):
     check("ht (other heads)", ht[:, keep], ht_ref[:, keep], dtype)
     assert not np.all(np.isfinite(o[:, 100:, bad])), "the NaN head shows no corruption"
     assert not np.all(np.isfinite(ht[:, bad]))
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_out_of_range_cu_seqlens_are_clamped(dtype, d):
+    """A cu_seqlens that breaks its documented precondition (a negative start, an end past
+    the tokens) is clamped to [0, T] on the device: the call stays inside its buffers and
+    gives exactly the result of the clamped offsets."""
+    w = dataclasses.replace(I.WORKLOADS[4], dtype=dtype, Dk=d, Dv=d, h0=True)
+    x = I.prefill_inputs(w, heads=[0, 1], lengths=[50, 70])             # 120 tokens
+    dev = torch.device("cuda:0")
+    args = [t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta)]
+    print(f"[prefill] clamped cu_seqlens {dtype} d{d}", flush=True)
+    good = torch.tensor([0, 50, 120], dtype=torch.int32, device=dev)
+    bad = torch.tensor([-5, 50, 200], dtype=torch.int32, device=dev)
+    o1, h1 = kda.fwd_chunked(*args, initial_state=x.h0.to(dev), cu_seqlens=good)
+    o2, h2 = kda.fwd_chunked(*args, initial_state=x.h0.to(dev), cu_seqlens=bad)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
