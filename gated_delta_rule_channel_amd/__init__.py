@@ -22,7 +22,11 @@ dst_slots, src, src_slots) copies whole states (fork, rollback).
 
 Input preparation: prepare_inputs(q, k, a, b, scale) -> (q^, k^, g, beta) turns raw
 projections into the inputs above (normalised q and k, g = log sigmoid(a),
-beta = sigmoid(b)) in one pass.
+beta = sigmoid(b)) in one pass; fwd_chunked_raw(q, k, v, a, b, scale, ...) does the same
+inside the prefill (bf16, d = 128), so the prepared inputs never reach memory.
+
+fwd_chunked_noalloc(...) is fwd_chunked on the library's built-in per-device scratch
+array (no workspace argument, up to NOALLOC_SCRATCH_BYTES of workspace).
 """
 from __future__ import annotations
 
