@@ -461,33 +461,30 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
                     for (int e = 0; e < 8; ++e) { kf[e] = 0.f; qf[e] = 0.f; }
                 }
             };
+            // the 8th-row reference, formed while testing that no channel decays by more than
+            // 2^120 over half a block; if one does, its (possibly overflowed) sums are dropped
             bool bad = false;
 #pragma unroll 1
             for (int st = 0; st < 4; ++st) {
-                float x[8];
+                float x[8], kf[8], qf[8], kb[8];
                 gl8(st, x);
+                kq8(st, kf, qf, kb);
+                FFrag KE, QE, KX;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) bad |= fabsf(x[e] - row_bcast<7>(x[e])) > 120.f;
-            }
-            if (!__any(bad)) {
-#pragma unroll 1
-                for (int st = 0; st < 4; ++st) {
-                    float x[8], kf[8], qf[8], kb[8];
-                    gl8(st, x);
-                    kq8(st, kf, qf, kb);
-                    FFrag KE, QE, KX;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float d = x[e] - row_bcast<7>(x[e]);
-                        const float e1 = fast_exp2(d), e2 = fast_exp2(-d);
-                        KE.set(e, kb[e] * e1);
-                        QE.set(e, qf[e] * e1);
-                        KX.set(e, kf[e] * e2);
-                    }
-                    FPol::mma(dkk, KX, KE);
-                    FPol::mma(dqk, KX, QE);
+                for (int e = 0; e < 8; ++e) {
+                    const float d = x[e] - row_bcast<7>(x[e]);
+                    bad |= fabsf(d) > 120.f;
+                    const float e1 = fast_exp2(d), e2 = fast_exp2(-d);
+                    KE.set(e, kb[e] * e1);
+                    QE.set(e, qf[e] * e1);
+                    KX.set(e, kf[e] * e2);
                 }
-            } else {
+                FPol::mma(dkk, KX, KE);
+                FPol::mma(dqk, KX, QE);
+            }
+            if (__any(bad)) {
+                dkk = floatx4{0.f, 0.f, 0.f, 0.f};
+                dqk = floatx4{0.f, 0.f, 0.f, 0.f};
                 // entry (i = m, j = jj): sums over the channel steps, then over the quarter-rows
 #pragma unroll 1
                 for (int jj = 0; jj < 16; ++jj) {
