@@ -462,13 +462,50 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
                 }
             };
             // the 8th-row reference, formed while testing that no channel decays by more than
-            // 2^120 over half a block; if one does, its (possibly overflowed) sums are dropped
+            // 2^120 over half a block; if one does, its (possibly overflowed) sums are dropped.
+            // The next channel step's inputs are loaded (raw) while a step is formed.
+            auto far_load = [&](int st, GateBuf<RAW>& gr, u32x4& kr, u32x4& qr, u32x4& er) {
+                if (rv) {
+                    gr.load(gate, off + 32 * st, 0);
+                    kr = *reinterpret_cast<const u32x4*>(k + off + 32 * st);
+                    qr = *reinterpret_cast<const u32x4*>(q + off + 32 * st);
+                    if constexpr (EW) er = *reinterpret_cast<const u32x4*>(eb + off + 32 * st);
+                } else {
+                    gr.zero(0);                             // g = 0 on rows past the end
+                    kr = u32x4{0u, 0u, 0u, 0u};
+                    qr = kr;
+                    er = kr;
+                }
+            };
+            auto widen8 = [](const u32x4& w, float (&f)[8]) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    f[2 * p] = __uint_as_float(w[p] << 16);
+                    f[2 * p + 1] = __uint_as_float(w[p] & 0xffff0000u);
+                }
+            };
             bool bad = false;
+            GateBuf<RAW> gn;
+            u32x4 kn, qn, en;
+            far_load(0, gn, kn, qn, en);
 #pragma unroll 1
             for (int st = 0; st < 4; ++st) {
+                const GateBuf<RAW> gc = gn;
+                const u32x4 kc4 = kn, qc4 = qn, ec4 = en;
+                if (st < 3) far_load(st + 1, gn, kn, qn, en);
                 float x[8], kf[8], qf[8], kb[8];
-                gl8(st, x);
-                kq8(st, kf, qf, kb);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = gc.log_decay(e) * kLog2e;
+                row_scan8(x);
+                widen8(kc4, kf);
+                widen8(qc4, qf);
+                if constexpr (EW) widen8(ec4, kb);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    kf[e] *= rk;
+                    qf[e] *= rq;
+                    kb[e] = (EW ? kb[e] : bi) * kf[e];
+                }
                 FFrag KE, QE, KX;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
