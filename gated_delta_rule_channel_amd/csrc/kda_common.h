@@ -218,6 +218,10 @@ struct PolF32 {
         tile_load_raw(r.f[0], t, lane);
         tile_load_raw(r.f[1], reinterpret_cast<const uint8_t*>(t) + 2048, lane);
     }
+    // fragment a alone (b is not read afterwards)
+    __device__ static __forceinline__ void pair_load_a(Pair& r, const void* t, int lane) {
+        tile_load_raw(r.f[0], t, lane);
+    }
     template <int W>
     __device__ static __forceinline__ void pair_decode(Frag& f, const Pair& r) { f = r.f[W]; }
     // narrower pairs of the bf16 path: full fp32 here
@@ -387,6 +391,14 @@ struct PolSplit {
         r.hi[0] = p[lane];
         r.hi[1] = p[64 + lane];
         r.ext = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(t) + 2048)[lane];
+    }
+    // fragment a alone (b is not read afterwards): its hi values and its 8 extension bytes
+    __device__ static __forceinline__ void pair_load_a(Pair& r, const void* t, int lane) {
+        const bf16x8* p = reinterpret_cast<const bf16x8*>(t);
+        r.hi[0] = p[lane];
+        const u32x2 e = reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(t) + 2048)[2 * lane];
+        r.ext[0] = e[0];
+        r.ext[1] = e[1];
     }
     template <int W>
     __device__ static __forceinline__ void pair_decode(Frag& f, const Pair& r) {

@@ -585,9 +585,11 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
                 if constexpr (EW) Wg.zero(I2);
             }
         }
-        // A_qk fragment tiles of token tile tw = wave (upper blocks zero)
+        // A_qk fragment tiles of token tile tw = wave (upper blocks zero; the columns 32..63
+        // of token tiles 0 and 1, all zero, are not stored: the state pass does not read them)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
+            if (s2 == 1 && wave < 2) continue;                // wave-uniform
             const int J = 2 * s2 + (grp >> 1), jl = 8 * (grp & 1);
             float a[8];
             if (J <= wave) {

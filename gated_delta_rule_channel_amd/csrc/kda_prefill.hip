@@ -619,9 +619,11 @@ __global__ __launch_bounds__(256, EW ? 1 : 2) void prep_kernel(
                 if constexpr (EW) Wr.zero(I);
             }
         }
-        // A_qk fragment tiles of token tile tw = wave (upper blocks zero)
+        // A_qk fragment tiles of token tile tw = wave (upper blocks zero; the columns 32..63
+        // of token tiles 0 and 1, all zero, are not stored: the state pass does not read them)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
+            if (s == 1 && wave < 2) continue;                 // wave-uniform
             const int J = 2 * s + (grp >> 1), jl = 8 * (grp & 1);
             float a[8];
             if (J <= wave) {
@@ -1056,7 +1058,10 @@ __global__ __launch_bounds__(768) void state_kernel(
             issue_fence();
         };
         auto issue_a = [&](Raw& r, int c) {
-            Pol::pair_load(r.a, block(c) + Ly::AQ + tw * Ly::PT, lane);
+            // token tiles 0 and 1 have no nonzero columns past 31: their second fragment is
+            // neither stored nor read
+            if (tw < 2) Pol::pair_load_a(r.a, block(c) + Ly::AQ + tw * Ly::PT, lane);
+            else Pol::pair_load(r.a, block(c) + Ly::AQ + tw * Ly::PT, lane);
             issue_fence();
         };
         auto decode = [&](const Raw& r) {
