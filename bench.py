@@ -15,6 +15,7 @@ packed long-context prefill (8 sequences, 105,872 tokens, drawn on the device),
 and the input preparation pass at the main prefill's shape.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                  [--no-extras | --extras b2b,gdn,gdn2,serving,varlen,inputs]
   python bench.py --copy-calibration          # 1 GiB device copy (counter calibration)
   python bench.py --traffic-summary F W CF CW # rocprofv3 --pmc CSVs -> profiles/ json
 
@@ -253,6 +254,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the step (prefill + decode); for counter passes")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--extras", default="all",
+                    help="comma-separated sections after the step: b2b, gdn, gdn2, serving, "
+                         "varlen, inputs (default all)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"))
     args = ap.parse_args()
@@ -336,93 +340,15 @@ def main():
     mfma_alg = pf_flops / (BF16_PEAK_TFLOPS * 1e12) / tp_mean
     traffic_pf, traffic_dc = load_traffic()
 
+    sel = set(args.extras.split(","))
+
+    def want(name):
+        return "all" in sel or name in sel
+
     def run_extras():
         """The figures beyond the step: back-to-back decode, Gated DeltaNet, Gated DeltaNet-2,
-        serving state, the packed long-context prefill and input preparation."""
-        # the same decode step repeated with nothing between the calls: the Infinity Cache holds
-        # the tail of each step's state writes, which then reach HBM inside the next step rather
-        # than under the following prefill, so this is the sustained decode rate
-        eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        eb0.record(stream)
-        for _ in range(args.steps):
-            decode()
-        eb1.record(stream)
-        torch.cuda.synchronize()
-        td_b2b = eb0.elapsed_time(eb1) * 1e-3 / args.steps
-        dc_gbs_b2b = dc_bytes / td_b2b / 1e9
-
-        # Gated DeltaNet (scalar gate per token and head) on the same q, k, v, beta and state
-        # shapes, timed the same way (one prefill + one decode step per step)
-        gs = I.scalar_gate(wp, list(range(H)), B * T).view(B, T, H).to(dev)
-        gds = I.scalar_gate(wd, list(range(wd.H)), wd.N).to(dev)
-
-        def gdn_prefill():
-            kda.gdn_fwd_chunked(q, k, v, gs, b, scale=1.0, workspace=ws, out=o, final_state=ht)
-
-        def gdn_decode():
-            kda.gdn_decode_step(dq, dk, dv, gds, db, state, scale=1.0, out=od)
-
-        for _ in range(args.warmup):
-            gdn_prefill()
-            gdn_decode()
-        torch.cuda.synchronize()
-        for e0, e1, e2 in ev:
-            e0.record(stream)
-            gdn_prefill()
-            e1.record(stream)
-            gdn_decode()
-            e2.record(stream)
-        torch.cuda.synchronize()
-        tgp = np.array([a.elapsed_time(bb) for a, bb, _ in ev]) * 1e-3
-        tgd = np.array([bb.elapsed_time(c) for _, bb, c in ev]) * 1e-3
-        gdn_pf_bytes = pf_bytes - B * T * H * Dk * 4 + B * T * H * 4       # g is one float per token-head
-        gdn_dc_bytes = dc_bytes - wd.N * wd.H * wd.Dk * 4 + wd.N * wd.H * 4
-
-        # Gated DeltaNet-2 (erase gate per key channel, write gate per value channel, bf16, in
-        # place of beta) on the same q, k, v, g and state, timed the same way
-        eb2, ew2 = (t.view(B, T, H, -1).to(dev) for t in I.erase_write_gates(wp, list(range(H)), B * T))
-        ebd, ewd = (t.to(dev) for t in I.erase_write_gates(wd, list(range(wd.H)), wd.N))
-
-        def gdn2_prefill():
-            kda.gdn2_fwd_chunked(q, k, v, g, eb2, ew2, scale=1.0, workspace=ws, out=o, final_state=ht)
-
-        def gdn2_decode():
-            kda.gdn2_decode_step(dq, dk, dv, dg, ebd, ewd, state, scale=1.0, out=od)
-
-        for _ in range(args.warmup):
-            gdn2_prefill()
-            gdn2_decode()
-        torch.cuda.synchronize()
-        for e0, e1, e2 in ev:
-            e0.record(stream)
-            gdn2_prefill()
-            e1.record(stream)
-            gdn2_decode()
-            e2.record(stream)
-        torch.cuda.synchronize()
-        t2p = np.array([a.elapsed_time(bb) for a, bb, _ in ev]) * 1e-3
-        t2d = np.array([bb.elapsed_time(c) for _, bb, c in ev]) * 1e-3
-        del eb2, ew2
-        gdn2_pf_bytes = pf_bytes - B * T * H * 2 + B * T * H * (Dk + Dv) * 2   # b, w instead of beta
-        gdn2_dc_bytes = dc_bytes - wd.N * wd.H * 2 + wd.N * wd.H * (wd.Dk + wd.Dv) * 2
-
-        # serving state: 4 drafted tokens per request verified against a pool of 512 slots (the
-        # 256 requests at permuted slots), without and with per-token snapshots, and a fork of
-        # 256 states to free slots
-        TV, PS = 4, 2 * wd.N
-        xs = I.decode_inputs(wd, N=wd.N * TV, with_state=False)
-        mv = [t.view(wd.N, TV, *t.shape[1:]).to(dev) for t in (xs.q, xs.k, xs.v, xs.g, xs.beta)]
-        del xs
-        spool = torch.empty((PS, wd.H, wd.Dk, wd.Dv), dtype=torch.float32, device=dev)
-        spool[:wd.N].copy_(state)
-        spool[wd.N:].copy_(state)
-        perm = np.random.default_rng(5).permutation(PS).astype(np.int32)
-        sslots = torch.from_numpy(perm[:wd.N]).to(dev)
-        fork_src = torch.from_numpy(perm[:wd.N]).to(dev)
-        fork_dst = torch.from_numpy(perm[wd.N:]).to(dev)
-        snaps = torch.empty((wd.N, TV, wd.H, wd.Dk, wd.Dv), dtype=torch.float32, device=dev)
-        omv = torch.empty((wd.N, TV, wd.H, wd.Dv), dtype=torch.bfloat16, device=dev)
-
+        serving state, the packed long-context prefill and input preparation (the sections
+        named by --extras)."""
         def timed(fn, n):
             for _ in range(3):
                 fn()
@@ -435,118 +361,217 @@ def main():
             return a0.elapsed_time(a1) * 1e-3 / n
 
         n_serv = max(5, args.steps // 2)
-        t_mv = timed(lambda: kda.decode_multi(*mv, spool, slots=sslots, scale=1.0, out=omv), n_serv)
-        t_mvs = timed(lambda: kda.decode_multi(*mv, spool, slots=sslots, snapshots=snaps, scale=1.0,
-                                               out=omv), n_serv)
-        t_fork = timed(lambda: kda.state_copy(spool, fork_dst, spool, fork_src), n_serv)
-        st_bytes = wd.N * wd.H * wd.Dk * wd.Dv * 4
-        tok_bytes = TV * (decode_bytes(wd.N, wd.H, wd.Dk, wd.Dv, 2, 2) - 2 * st_bytes)
-        mv_bytes = 2 * st_bytes + tok_bytes
-        mvs_bytes = mv_bytes + TV * st_bytes
-        del spool, snaps, mv, omv
+        res = {}
 
-        # the packed long-context workload: 8 sequences of the seeded lengths (105,872 tokens),
-        # H64 d128 bf16, drawn on the device with the generators' distributions (unit q, k with q
-        # scaled by d^-1/2, v ~ N(0, 1), beta = sigmoid(N(0, 1)), g = -softplus(N(0, 1)) U(0.5, 2)
-        # with 13 fast channels at -U(5, 10) and 13 slow ones at -U(0, 1e-4) per head)
-        wv = I.WORKLOADS[4]
-        lens = I.varlen_lengths(wv)
-        cu_v = torch.from_numpy(I.cu_seqlens_from_lengths(lens)).to(dev)
-        TV_ = int(lens.sum())
-        gv = torch.Generator(device=dev).manual_seed(4)
-        rn = lambda *shape: torch.randn(shape, generator=gv, device=dev)
-        unit = lambda x: x / x.norm(dim=-1, keepdim=True)
-        vq = (unit(rn(1, TV_, H, Dk)) * Dk ** -0.5).to(torch.bfloat16)
-        vk = unit(rn(1, TV_, H, Dk)).to(torch.bfloat16)
-        vv = rn(1, TV_, H, Dv).to(torch.bfloat16)
-        vb = torch.sigmoid(rn(1, TV_, H)).to(torch.bfloat16)
-        vg = -torch.nn.functional.softplus(rn(1, TV_, H, Dk))
-        vg *= torch.empty_like(vg).uniform_(0.5, 2.0, generator=gv)
-        for h in range(H):
-            perm = torch.randperm(Dk, generator=gv, device=dev)
-            fast, slow = perm[:13], perm[13:26]
-            vg[0, :, h, fast] = -torch.empty((TV_, 13), device=dev).uniform_(5.0, 10.0, generator=gv)
-            vg[0, :, h, slow] = -torch.empty((TV_, 13), device=dev).uniform_(0.0, 1e-4, generator=gv)
-        nbv = kda.workspace_size(1, TV_, H, Dk, Dv, len(lens), True, kda.KDA_DTYPE_BF16)
-        wsv = torch.empty(nbv, dtype=torch.uint8, device=dev)
-        ov = torch.empty((1, TV_, H, Dv), dtype=torch.bfloat16, device=dev)
-        htv = torch.empty((len(lens), H, Dk, Dv), dtype=torch.float32, device=dev)
-        t_var = timed(lambda: kda.fwd_chunked(vq, vk, vv, vg, vb, cu_seqlens=cu_v, workspace=wsv,
-                                              out=ov, final_state=htv), max(3, n_serv // 5))
-        # algorithmic bytes per token as for the main prefill (bf16 o): 98,432 at H64 d128
-        var_bytes = TV_ * H * (3 * Dk * 2 + Dk * 4 + 2 + Dv * 2) + len(lens) * H * Dk * Dv * 4
-        del vq, vk, vv, vb, vg, wsv, ov, htv
+        if want("b2b"):
+            # the same decode step repeated with nothing between the calls: the Infinity Cache holds
+            # the tail of each step's state writes, which then reach HBM inside the next step rather
+            # than under the following prefill, so this is the sustained decode rate
+            eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            eb0.record(stream)
+            for _ in range(args.steps):
+                decode()
+            eb1.record(stream)
+            torch.cuda.synchronize()
+            td_b2b = eb0.elapsed_time(eb1) * 1e-3 / args.steps
+            dc_gbs_b2b = dc_bytes / td_b2b / 1e9
 
-        # input preparation at the main prefill's shape: raw bf16 q, k, a [T, H, Dk] and b [T, H]
-        # to normalised q, k (bf16), g (fp32) and beta (bf16), one pass
-        rng_i = torch.Generator(device=dev).manual_seed(3)
-        raw = [torch.randn((B * T, H, Dk), generator=rng_i, device=dev).to(torch.bfloat16)
-               for _ in range(3)]
-        raw.append(torch.randn((B * T, H), generator=rng_i, device=dev).to(torch.bfloat16))
-        prep_out = (torch.empty_like(raw[0]), torch.empty_like(raw[1]),
-                    torch.empty((B * T, H, Dk), dtype=torch.float32, device=dev),
-                    torch.empty_like(raw[3]))
-        t_prep = timed(lambda: kda.prepare_inputs(*raw, scale=Dk ** -0.5, out=prep_out), n_serv)
-        prep_bytes = B * T * H * (Dk * 2 * 5 + Dk * 4 + 2 * 2)
-        # raw projections to o at the main prefill's shape: the two-pass route (the preparation
-        # above, then the prefill on its outputs) against kda_fwd_chunked_raw, which forms the
-        # prepared inputs inside the prefill's first kernel
-        rs = lambda t: t.view(B, T, *t.shape[1:])
-        p4 = [rs(t) for t in prep_out]
+        if want("gdn"):
+            # Gated DeltaNet (scalar gate per token and head) on the same q, k, v, beta and state
+            # shapes, timed the same way (one prefill + one decode step per step)
+            gs = I.scalar_gate(wp, list(range(H)), B * T).view(B, T, H).to(dev)
+            gds = I.scalar_gate(wd, list(range(wd.H)), wd.N).to(dev)
 
-        def two_pass():
-            kda.prepare_inputs(*raw, scale=Dk ** -0.5, out=prep_out)
-            kda.fwd_chunked(p4[0], p4[1], v, p4[2], p4[3], scale=1.0, workspace=ws, out=o,
-                            final_state=ht)
+            def gdn_prefill():
+                kda.gdn_fwd_chunked(q, k, v, gs, b, scale=1.0, workspace=ws, out=o, final_state=ht)
 
-        r4 = [rs(t) for t in raw]
-        # the main prefill with a float32 o instead of the input dtype (2 more bytes per output
-        # element), for comparison
-        o32 = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
-        t_o32 = timed(lambda: kda.fwd_chunked(q, k, v, g, b, scale=1.0, workspace=ws, out=o32,
-                                              final_state=ht), n_serv)
-        del o32
-        t_two = timed(two_pass, n_serv)
-        t_raw = timed(lambda: kda.fwd_chunked_raw(r4[0], r4[1], v, r4[2], r4[3], scale=Dk ** -0.5,
-                                                  workspace=ws, out=o, final_state=ht), n_serv)
-        del raw, prep_out, p4, r4
+            def gdn_decode():
+                kda.gdn_decode_step(dq, dk, dv, gds, db, state, scale=1.0, out=od)
 
-        return {
-            "decode_b2b": {"ms_back_to_back": td_b2b * 1e3, "hbm_gbs_back_to_back": dc_gbs_b2b,
-                           "frac_of_peak_back_to_back": dc_gbs_b2b / HBM_PEAK_GBS},
-            "gated_deltanet": {"prefill_ms": float(tgp.mean()) * 1e3,
-                               "prefill_tokens_per_s": tokens / float(tgp.mean()),
-                               "prefill_hbm_gbs": gdn_pf_bytes / float(tgp.mean()) / 1e9,
-                               "decode_ms": float(tgd.mean()) * 1e3,
-                               "decode_hbm_gbs": gdn_dc_bytes / float(tgd.mean()) / 1e9,
-                               "decode_frac_of_peak": gdn_dc_bytes / float(tgd.mean()) / 1e9
-                               / HBM_PEAK_GBS},
-            "gated_deltanet_2": {"prefill_ms": float(t2p.mean()) * 1e3,
-                                 "prefill_tokens_per_s": tokens / float(t2p.mean()),
-                                 "prefill_hbm_gbs": gdn2_pf_bytes / float(t2p.mean()) / 1e9,
-                                 "decode_ms": float(t2d.mean()) * 1e3,
-                                 "decode_hbm_gbs": gdn2_dc_bytes / float(t2d.mean()) / 1e9,
-                                 "decode_frac_of_peak": gdn2_dc_bytes / float(t2d.mean()) / 1e9
-                                 / HBM_PEAK_GBS},
-            "serving": {"verify_tokens": TV, "pool_slots": PS,
-                        "decode_multi_ms": t_mv * 1e3, "decode_multi_tokens_per_s": wd.N * TV / t_mv,
-                        "decode_multi_hbm_gbs": mv_bytes / t_mv / 1e9,
-                        "decode_multi_snapshots_ms": t_mvs * 1e3,
-                        "decode_multi_snapshots_hbm_gbs": mvs_bytes / t_mvs / 1e9,
-                        "state_copy_256_ms": t_fork * 1e3,
-                        "state_copy_hbm_gbs": 2 * st_bytes / t_fork / 1e9},
-            "varlen_prefill": {"workload": wv.name, "tokens": TV_, "sequences": len(lens),
-                               "ms": t_var * 1e3, "tokens_per_s": TV_ / t_var,
-                               "compulsory_bytes": var_bytes, "hbm_gbs": var_bytes / t_var / 1e9,
-                               "frac_of_peak": var_bytes / t_var / 1e9 / HBM_PEAK_GBS},
-            "input_prep": {"ms": t_prep * 1e3, "bytes": prep_bytes,
-                           "hbm_gbs": prep_bytes / t_prep / 1e9,
-                           "frac_of_peak": prep_bytes / t_prep / 1e9 / HBM_PEAK_GBS},
-            "prefill_fp32_o": {"ms": t_o32 * 1e3, "tokens_per_s": tokens / t_o32},
-            "raw_to_o": {"two_pass_ms": t_two * 1e3, "fused_ms": t_raw * 1e3,
-                         "fused_tokens_per_s": tokens / t_raw,
-                         "saved_ms": (t_two - t_raw) * 1e3},
-        }
+            for _ in range(args.warmup):
+                gdn_prefill()
+                gdn_decode()
+            torch.cuda.synchronize()
+            for e0, e1, e2 in ev:
+                e0.record(stream)
+                gdn_prefill()
+                e1.record(stream)
+                gdn_decode()
+                e2.record(stream)
+            torch.cuda.synchronize()
+            tgp = np.array([a.elapsed_time(bb) for a, bb, _ in ev]) * 1e-3
+            tgd = np.array([bb.elapsed_time(c) for _, bb, c in ev]) * 1e-3
+            gdn_pf_bytes = pf_bytes - B * T * H * Dk * 4 + B * T * H * 4       # g is one float per token-head
+            gdn_dc_bytes = dc_bytes - wd.N * wd.H * wd.Dk * 4 + wd.N * wd.H * 4
+
+        if want("gdn2"):
+            # Gated DeltaNet-2 (erase gate per key channel, write gate per value channel, bf16, in
+            # place of beta) on the same q, k, v, g and state, timed the same way
+            eb2, ew2 = (t.view(B, T, H, -1).to(dev) for t in I.erase_write_gates(wp, list(range(H)), B * T))
+            ebd, ewd = (t.to(dev) for t in I.erase_write_gates(wd, list(range(wd.H)), wd.N))
+
+            def gdn2_prefill():
+                kda.gdn2_fwd_chunked(q, k, v, g, eb2, ew2, scale=1.0, workspace=ws, out=o, final_state=ht)
+
+            def gdn2_decode():
+                kda.gdn2_decode_step(dq, dk, dv, dg, ebd, ewd, state, scale=1.0, out=od)
+
+            for _ in range(args.warmup):
+                gdn2_prefill()
+                gdn2_decode()
+            torch.cuda.synchronize()
+            for e0, e1, e2 in ev:
+                e0.record(stream)
+                gdn2_prefill()
+                e1.record(stream)
+                gdn2_decode()
+                e2.record(stream)
+            torch.cuda.synchronize()
+            t2p = np.array([a.elapsed_time(bb) for a, bb, _ in ev]) * 1e-3
+            t2d = np.array([bb.elapsed_time(c) for _, bb, c in ev]) * 1e-3
+            del eb2, ew2
+            gdn2_pf_bytes = pf_bytes - B * T * H * 2 + B * T * H * (Dk + Dv) * 2   # b, w instead of beta
+            gdn2_dc_bytes = dc_bytes - wd.N * wd.H * 2 + wd.N * wd.H * (wd.Dk + wd.Dv) * 2
+
+        if want("serving"):
+            # serving state: 4 drafted tokens per request verified against a pool of 512 slots (the
+            # 256 requests at permuted slots), without and with per-token snapshots, and a fork of
+            # 256 states to free slots
+            TV, PS = 4, 2 * wd.N
+            xs = I.decode_inputs(wd, N=wd.N * TV, with_state=False)
+            mv = [t.view(wd.N, TV, *t.shape[1:]).to(dev) for t in (xs.q, xs.k, xs.v, xs.g, xs.beta)]
+            del xs
+            spool = torch.empty((PS, wd.H, wd.Dk, wd.Dv), dtype=torch.float32, device=dev)
+            spool[:wd.N].copy_(state)
+            spool[wd.N:].copy_(state)
+            perm = np.random.default_rng(5).permutation(PS).astype(np.int32)
+            sslots = torch.from_numpy(perm[:wd.N]).to(dev)
+            fork_src = torch.from_numpy(perm[:wd.N]).to(dev)
+            fork_dst = torch.from_numpy(perm[wd.N:]).to(dev)
+            snaps = torch.empty((wd.N, TV, wd.H, wd.Dk, wd.Dv), dtype=torch.float32, device=dev)
+            omv = torch.empty((wd.N, TV, wd.H, wd.Dv), dtype=torch.bfloat16, device=dev)
+
+
+            t_mv = timed(lambda: kda.decode_multi(*mv, spool, slots=sslots, scale=1.0, out=omv), n_serv)
+            t_mvs = timed(lambda: kda.decode_multi(*mv, spool, slots=sslots, snapshots=snaps, scale=1.0,
+                                                   out=omv), n_serv)
+            t_fork = timed(lambda: kda.state_copy(spool, fork_dst, spool, fork_src), n_serv)
+            st_bytes = wd.N * wd.H * wd.Dk * wd.Dv * 4
+            tok_bytes = TV * (decode_bytes(wd.N, wd.H, wd.Dk, wd.Dv, 2, 2) - 2 * st_bytes)
+            mv_bytes = 2 * st_bytes + tok_bytes
+            mvs_bytes = mv_bytes + TV * st_bytes
+            del spool, snaps, mv, omv
+
+        if want("varlen"):
+            # the packed long-context workload: 8 sequences of the seeded lengths (105,872 tokens),
+            # H64 d128 bf16, drawn on the device with the generators' distributions (unit q, k with q
+            # scaled by d^-1/2, v ~ N(0, 1), beta = sigmoid(N(0, 1)), g = -softplus(N(0, 1)) U(0.5, 2)
+            # with 13 fast channels at -U(5, 10) and 13 slow ones at -U(0, 1e-4) per head)
+            wv = I.WORKLOADS[4]
+            lens = I.varlen_lengths(wv)
+            cu_v = torch.from_numpy(I.cu_seqlens_from_lengths(lens)).to(dev)
+            TV_ = int(lens.sum())
+            gv = torch.Generator(device=dev).manual_seed(4)
+            rn = lambda *shape: torch.randn(shape, generator=gv, device=dev)
+            unit = lambda x: x / x.norm(dim=-1, keepdim=True)
+            vq = (unit(rn(1, TV_, H, Dk)) * Dk ** -0.5).to(torch.bfloat16)
+            vk = unit(rn(1, TV_, H, Dk)).to(torch.bfloat16)
+            vv = rn(1, TV_, H, Dv).to(torch.bfloat16)
+            vb = torch.sigmoid(rn(1, TV_, H)).to(torch.bfloat16)
+            vg = -torch.nn.functional.softplus(rn(1, TV_, H, Dk))
+            vg *= torch.empty_like(vg).uniform_(0.5, 2.0, generator=gv)
+            for h in range(H):
+                perm = torch.randperm(Dk, generator=gv, device=dev)
+                fast, slow = perm[:13], perm[13:26]
+                vg[0, :, h, fast] = -torch.empty((TV_, 13), device=dev).uniform_(5.0, 10.0, generator=gv)
+                vg[0, :, h, slow] = -torch.empty((TV_, 13), device=dev).uniform_(0.0, 1e-4, generator=gv)
+            nbv = kda.workspace_size(1, TV_, H, Dk, Dv, len(lens), True, kda.KDA_DTYPE_BF16)
+            wsv = torch.empty(nbv, dtype=torch.uint8, device=dev)
+            ov = torch.empty((1, TV_, H, Dv), dtype=torch.bfloat16, device=dev)
+            htv = torch.empty((len(lens), H, Dk, Dv), dtype=torch.float32, device=dev)
+            t_var = timed(lambda: kda.fwd_chunked(vq, vk, vv, vg, vb, cu_seqlens=cu_v, workspace=wsv,
+                                                  out=ov, final_state=htv), max(3, n_serv // 5))
+            # algorithmic bytes per token as for the main prefill (bf16 o): 98,432 at H64 d128
+            var_bytes = TV_ * H * (3 * Dk * 2 + Dk * 4 + 2 + Dv * 2) + len(lens) * H * Dk * Dv * 4
+            del vq, vk, vv, vb, vg, wsv, ov, htv
+
+        if want("inputs"):
+            # input preparation at the main prefill's shape: raw bf16 q, k, a [T, H, Dk] and b [T, H]
+            # to normalised q, k (bf16), g (fp32) and beta (bf16), one pass
+            rng_i = torch.Generator(device=dev).manual_seed(3)
+            raw = [torch.randn((B * T, H, Dk), generator=rng_i, device=dev).to(torch.bfloat16)
+                   for _ in range(3)]
+            raw.append(torch.randn((B * T, H), generator=rng_i, device=dev).to(torch.bfloat16))
+            prep_out = (torch.empty_like(raw[0]), torch.empty_like(raw[1]),
+                        torch.empty((B * T, H, Dk), dtype=torch.float32, device=dev),
+                        torch.empty_like(raw[3]))
+            t_prep = timed(lambda: kda.prepare_inputs(*raw, scale=Dk ** -0.5, out=prep_out), n_serv)
+            prep_bytes = B * T * H * (Dk * 2 * 5 + Dk * 4 + 2 * 2)
+            # raw projections to o at the main prefill's shape: the two-pass route (the preparation
+            # above, then the prefill on its outputs) against kda_fwd_chunked_raw, which forms the
+            # prepared inputs inside the prefill's first kernel
+            rs = lambda t: t.view(B, T, *t.shape[1:])
+            p4 = [rs(t) for t in prep_out]
+
+            def two_pass():
+                kda.prepare_inputs(*raw, scale=Dk ** -0.5, out=prep_out)
+                kda.fwd_chunked(p4[0], p4[1], v, p4[2], p4[3], scale=1.0, workspace=ws, out=o,
+                                final_state=ht)
+
+            r4 = [rs(t) for t in raw]
+            # the main prefill with a float32 o instead of the input dtype (2 more bytes per output
+            # element), for comparison
+            o32 = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+            t_o32 = timed(lambda: kda.fwd_chunked(q, k, v, g, b, scale=1.0, workspace=ws, out=o32,
+                                                  final_state=ht), n_serv)
+            del o32
+            t_two = timed(two_pass, n_serv)
+            t_raw = timed(lambda: kda.fwd_chunked_raw(r4[0], r4[1], v, r4[2], r4[3], scale=Dk ** -0.5,
+                                                      workspace=ws, out=o, final_state=ht), n_serv)
+            del raw, prep_out, p4, r4
+        if want("b2b"):
+            res["decode_b2b"] = {"ms_back_to_back": td_b2b * 1e3, "hbm_gbs_back_to_back": dc_gbs_b2b,
+                                 "frac_of_peak_back_to_back": dc_gbs_b2b / HBM_PEAK_GBS}
+        if want("gdn"):
+            res["gated_deltanet"] = {"prefill_ms": float(tgp.mean()) * 1e3,
+                                     "prefill_tokens_per_s": tokens / float(tgp.mean()),
+                                     "prefill_hbm_gbs": gdn_pf_bytes / float(tgp.mean()) / 1e9,
+                                     "decode_ms": float(tgd.mean()) * 1e3,
+                                     "decode_hbm_gbs": gdn_dc_bytes / float(tgd.mean()) / 1e9,
+                                     "decode_frac_of_peak": gdn_dc_bytes / float(tgd.mean()) / 1e9
+                                     / HBM_PEAK_GBS}
+        if want("gdn2"):
+            res["gated_deltanet_2"] = {"prefill_ms": float(t2p.mean()) * 1e3,
+                                       "prefill_tokens_per_s": tokens / float(t2p.mean()),
+                                       "prefill_hbm_gbs": gdn2_pf_bytes / float(t2p.mean()) / 1e9,
+                                       "decode_ms": float(t2d.mean()) * 1e3,
+                                       "decode_hbm_gbs": gdn2_dc_bytes / float(t2d.mean()) / 1e9,
+                                       "decode_frac_of_peak": gdn2_dc_bytes / float(t2d.mean()) / 1e9
+                                       / HBM_PEAK_GBS}
+        if want("serving"):
+            res["serving"] = {"verify_tokens": TV, "pool_slots": PS,
+                              "decode_multi_ms": t_mv * 1e3, "decode_multi_tokens_per_s": wd.N * TV / t_mv,
+                              "decode_multi_hbm_gbs": mv_bytes / t_mv / 1e9,
+                              "decode_multi_snapshots_ms": t_mvs * 1e3,
+                              "decode_multi_snapshots_hbm_gbs": mvs_bytes / t_mvs / 1e9,
+                              "state_copy_256_ms": t_fork * 1e3,
+                              "state_copy_hbm_gbs": 2 * st_bytes / t_fork / 1e9}
+        if want("varlen"):
+            res["varlen_prefill"] = {"workload": wv.name, "tokens": TV_, "sequences": len(lens),
+                                     "ms": t_var * 1e3, "tokens_per_s": TV_ / t_var,
+                                     "compulsory_bytes": var_bytes, "hbm_gbs": var_bytes / t_var / 1e9,
+                                     "frac_of_peak": var_bytes / t_var / 1e9 / HBM_PEAK_GBS}
+        if want("inputs"):
+            res["input_prep"] = {"ms": t_prep * 1e3, "bytes": prep_bytes,
+                                 "hbm_gbs": prep_bytes / t_prep / 1e9,
+                                 "frac_of_peak": prep_bytes / t_prep / 1e9 / HBM_PEAK_GBS}
+        if want("inputs"):
+            res["prefill_fp32_o"] = {"ms": t_o32 * 1e3, "tokens_per_s": tokens / t_o32}
+        if want("inputs"):
+            res["raw_to_o"] = {"two_pass_ms": t_two * 1e3, "fused_ms": t_raw * 1e3,
+                               "fused_tokens_per_s": tokens / t_raw,
+                               "saved_ms": (t_two - t_raw) * 1e3}
+        return res
 
     extra = {} if args.no_extras else run_extras()
 

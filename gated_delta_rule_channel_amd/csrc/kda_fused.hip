@@ -727,41 +727,58 @@ __global__ __launch_bounds__(256, 2) void prep_fast_kernel(
                                            accW[hh][I2][0], accW[hh][I2][1], accW[hh][I2][2], accW[hh][I2][3]);
         }
         // ---- U = T' v: lane (m = value, grp) of tile (value tile, I) holds U[16 I + 4 grp + r][value] ----
+        if constexpr (EW) {
+            // U = T (w v): w v is not exact in one bfloat16, so the transpose and the product
+            // take both parts; it is formed once per token block for both value halves
+            floatx4 accU[2][4];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            floatx4 accU[4];
+            for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int I2 = 0; I2 < 4; ++I2) accU[I2] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int I2 = 0; I2 < 4; ++I2) accU[hh][I2] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
+                float vv[8], wv[8];
+                V.get8(J, vv);
+                Wg.get8(J, wv);
                 FFrag vb;
-                floatx4 t = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (EW) {
-                    // w v is not exact in one bfloat16: the transpose and the product take
-                    // both parts
-                    float vv[8], wv[8];
-                    V.get8(J, vv);
-                    Wg.get8(J, wv);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) vb.set(e, vv[e] * wv[e]);
+                for (int e = 0; e < 8; ++e) vb.set(e, vv[e] * wv[e]);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    floatx4 t = {0.f, 0.f, 0.f, 0.f};
                     FPol::mma_exact(t, vb, Eid[hh]);
-                } else {
-                    V.frag(J, vb);
-                    FPol::mma_copy(t, vb, Eid[hh]);
-                }
-                const FFrag4 b = frag4_of<FPol>(t);
+                    const FFrag4 b = frag4_of<FPol>(t);
 #pragma unroll
-                for (int I2 = J; I2 < 4; ++I2) {
-                    if constexpr (EW)
-                        FPol::mma16(accU[I2], sTp[tri_tile(I2, J)][lane], b);
-                    else
-                        FPol::mma16_exact(accU[I2], sTp[tri_tile(I2, J)][lane], b);
+                    for (int I2 = J; I2 < 4; ++I2) FPol::mma16(accU[hh][I2], sTp[tri_tile(I2, J)][lane], b);
                 }
             }
 #pragma unroll
-            for (int I2 = 0; I2 < 4; ++I2)
-                FPol::utile_store(blk + Ly::U + ((2 * wave + hh) * 4 + I2) * Ly::QT, lane,
-                                  accU[I2][0], accU[I2][1], accU[I2][2], accU[I2][3]);
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int I2 = 0; I2 < 4; ++I2)
+                    FPol::utile_store(blk + Ly::U + ((2 * wave + hh) * 4 + I2) * Ly::QT, lane,
+                                      accU[hh][I2][0], accU[hh][I2][1], accU[hh][I2][2], accU[hh][I2][3]);
+        } else {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                floatx4 accU[4];
+#pragma unroll
+                for (int I2 = 0; I2 < 4; ++I2) accU[I2] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    FFrag vb;
+                    floatx4 t = {0.f, 0.f, 0.f, 0.f};
+                    V.frag(J, vb);
+                    FPol::mma_copy(t, vb, Eid[hh]);         // v is exact in one bfloat16
+                    const FFrag4 b = frag4_of<FPol>(t);
+#pragma unroll
+                    for (int I2 = J; I2 < 4; ++I2) FPol::mma16_exact(accU[I2], sTp[tri_tile(I2, J)][lane], b);
+                }
+#pragma unroll
+                for (int I2 = 0; I2 < 4; ++I2)
+                    FPol::utile_store(blk + Ly::U + ((2 * wave + hh) * 4 + I2) * Ly::QT, lane,
+                                      accU[I2][0], accU[I2][1], accU[I2][2], accU[I2][3]);
+            }
         }
         if (staged) wait_all_memory();
     }
