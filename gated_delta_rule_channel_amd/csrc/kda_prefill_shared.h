@@ -23,7 +23,8 @@ namespace kda {
 //  Kd^T   20-bit pairs [channel tile ct][token halves (0, 1)]: channel 16 ct + m, tokens
 //         32 ks + 8 grp + e;
 //  U      tiles [value tile vt][token tile tw]: tokens 16 tw + 4 grp + r, value 16 vt + m;
-//  A_qk   pairs [token tile tw][column halves (0, 1)]: row 16 tw + m, columns 32 s + 8 grp + e;
+//  A_qk   pairs [token tile tw][column halves (0, 1)]: row 16 tw + m, columns 32 s + 8 grp + e
+//         (token tiles 0 and 1: the second half, all zero, is neither written nor read);
 //  exp(G_end) float [Dk].
 __host__ __device__ constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
